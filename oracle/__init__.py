@@ -1,0 +1,283 @@
+"""CPU oracle for MX microscaling quantisation and block-scaled GEMMs.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the package smoke check
+and by the benchmark's CPU-baseline leg, never by the product path.  The
+arithmetic lives in ``mxq_oracle.c`` (plain C, fp64), compiled with gcc into
+``liboracle.so`` next to this file; this module only marshals numpy arrays.
+
+bf16 tensors are passed as ``uint16`` bit patterns (numpy has no bf16).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mxq_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+BLOCK = 32
+
+
+def build(src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+           "-fno-fast-math", "-ffp-contract=off", src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _declare(lib):
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I32 = ctypes.c_int32
+    sig = {
+        "oracle_num_threads": ([], ctypes.c_int),
+        "oracle_e4m3_decode": ([ctypes.c_uint8], ctypes.c_double),
+        "oracle_e4m3_encode": ([ctypes.c_double], ctypes.c_uint8),
+        "oracle_e4m3_encode_n": ([P, I64, P], None),
+        "oracle_e8m0_decode": ([ctypes.c_uint8], ctypes.c_double),
+        "oracle_mxfp8_quant_row": ([P, I64, I64, I64, P, P], ctypes.c_int),
+        "oracle_mxfp8_quant_colT": ([P, I64, I64, I64, P, P], ctypes.c_int),
+        "oracle_mxfp8_quant_grouped_colT": ([P, I64, I64, I64, P, I32, I64, P, P], ctypes.c_int),
+        "oracle_mxfp8_dequant": ([P, P, I64, I64, P], None),
+        "oracle_mxfp4_qdq": ([P, P, I64, I64, P, P], ctypes.c_int),
+        "oracle_gemm": ([P, P, P, P, I64, I64, I64, P, P], ctypes.c_int),
+        "oracle_gemm_sampled": ([P, P, P, P, I64, I64, I64, P, P, I64, P, P], ctypes.c_int),
+        "oracle_grouped_gemm_ragged_m": ([P, P, P, P, I64, I64, I64, P, I32, P, P], ctypes.c_int),
+        "oracle_grouped_gemm_ragged_m_sampled":
+            ([P, P, P, P, I64, I64, I64, P, I32, P, P, I64, P, P], ctypes.c_int),
+        "oracle_grouped_gemm_ragged_k": ([P, P, P, P, I64, I64, I64, P, I32, P, P], ctypes.c_int),
+        "oracle_grouped_gemm_ragged_k_sampled":
+            ([P, P, P, P, I64, I64, I64, P, I32, P, P, P, I64, P, P], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+def lib(path: str | None = None):
+    """Load the oracle library, compiling it first if it is not built."""
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        _lib = _declare(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+class using:
+    """Context manager that routes this module's calls to another build of the
+    oracle (the mutation tests use it to run the pins against planted bugs)."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.saved = _lib
+        _lib = _declare(ctypes.CDLL(self.path))
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
+def _p(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its input (status {rc})")
+
+
+def ceil32(v: int) -> int:
+    return (v + BLOCK - 1) // BLOCK * BLOCK
+
+
+def grouped_cols(group_end) -> int:
+    """Columns used by a grouped token-axis copy: sum of ceil32(group sizes)."""
+    prev, tot = 0, 0
+    for e in np.asarray(group_end, dtype=np.int64).tolist():
+        tot += ceil32(e - prev)
+        prev = e
+    return tot
+
+
+# ---------------------------------------------------------------- elements
+def e4m3_decode(code: int) -> float:
+    return lib().oracle_e4m3_decode(int(code))
+
+
+def e4m3_encode(v: float) -> int:
+    return lib().oracle_e4m3_encode(float(v))
+
+
+def e4m3_encode_array(v) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.zeros(v.shape, np.uint8)
+    lib().oracle_e4m3_encode_n(_p(v), v.size, _p(out))
+    return out
+
+
+def e8m0_decode(byte: int) -> float:
+    return lib().oracle_e8m0_decode(int(byte))
+
+
+# ---------------------------------------------------------------- MXFP8
+def mxfp8_quant_row(x_bits: np.ndarray):
+    """bf16 bits [R][C] -> (codes uint8 [R][Cp], scales uint8 [R][Cp/32])."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    R, C = x.shape
+    Cp = ceil32(C)
+    q = np.zeros((R, Cp), np.uint8)
+    s = np.zeros((R, Cp // BLOCK), np.uint8)
+    _check(lib().oracle_mxfp8_quant_row(_p(x), R, C, C, _p(q), _p(s)), "quant_row")
+    return q, s
+
+
+def mxfp8_quant_colT(x_bits: np.ndarray):
+    """bf16 bits [R][C] -> (codes [C][Rp], scales [C][Rp/32]) of the transpose."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    R, C = x.shape
+    Rp = ceil32(R)
+    q = np.zeros((C, Rp), np.uint8)
+    s = np.zeros((C, Rp // BLOCK), np.uint8)
+    _check(lib().oracle_mxfp8_quant_colT(_p(x), R, C, C, _p(q), _p(s)), "quant_colT")
+    return q, s
+
+
+def mxfp8_quant_grouped_colT(x_bits: np.ndarray, group_end, ldq: int | None = None):
+    """bf16 bits [T][C] + cumulative group ends -> (codes [C][ldq], scales [C][ldq/32]).
+
+    Columns at and beyond sum_g ceil32(m_g) are returned as zeros.
+    """
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    T, C = x.shape
+    ge = np.ascontiguousarray(group_end, dtype=np.int32)
+    if ldq is None:
+        ldq = max(grouped_cols(ge), BLOCK)
+    q = np.zeros((C, ldq), np.uint8)
+    s = np.zeros((C, ldq // BLOCK), np.uint8)
+    _check(lib().oracle_mxfp8_quant_grouped_colT(_p(x), T, C, C, _p(ge), len(ge), ldq,
+                                                 _p(q), _p(s)), "quant_grouped_colT")
+    return q, s
+
+
+def mxfp8_dequant(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.uint8)
+    R, K = q.shape
+    assert s.shape == (R, K // BLOCK)
+    out = np.zeros((R, K), np.float64)
+    lib().oracle_mxfp8_dequant(_p(q), _p(s), R, K, _p(out))
+    return out
+
+
+# ---------------------------------------------------------------- MXFP4
+def mxfp4_qdq(x: np.ndarray, want_codes: bool = False):
+    """fp32 array of any shape -> fp32 QDQ of the same shape (blocks of 32 on
+    the last dim, each row padded on its own).  With ``want_codes`` also
+    returns (codes [rows][Lp/2], scales [rows][Lp/32])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    shape = x.shape
+    L = shape[-1] if x.ndim else 1
+    rows = int(np.prod(shape[:-1])) if x.ndim > 1 else 1
+    y = np.zeros(shape, np.float32)
+    Lp = ceil32(L)
+    codes = np.zeros((rows, Lp // 2), np.uint8) if want_codes else None
+    scales = np.zeros((rows, Lp // BLOCK), np.uint8) if want_codes else None
+    _check(lib().oracle_mxfp4_qdq(_p(x), _p(y), rows, L, _p(codes), _p(scales)), "mxfp4_qdq")
+    return (y, codes, scales) if want_codes else y
+
+
+# ---------------------------------------------------------------- GEMMs
+def gemm(A, sA, B, sB):
+    """C[m][n] = sum_k deq(A)[m][k]*deq(B)[n][k]; returns (C, sum|products|) in fp64."""
+    M, K = A.shape
+    N = B.shape[0]
+    C = np.zeros((M, N), np.float64)
+    Cabs = np.zeros((M, N), np.float64)
+    _check(lib().oracle_gemm(_p(A), _p(sA), _p(B), _p(sB), M, N, K, _p(C), _p(Cabs)), "gemm")
+    return C, Cabs
+
+
+def gemm_sampled(A, sA, B, sB, mi, ni):
+    M, K = A.shape
+    N = B.shape[0]
+    mi = np.ascontiguousarray(mi, dtype=np.int64)
+    ni = np.ascontiguousarray(ni, dtype=np.int64)
+    C = np.zeros(len(mi), np.float64)
+    Cabs = np.zeros(len(mi), np.float64)
+    _check(lib().oracle_gemm_sampled(_p(A), _p(sA), _p(B), _p(sB), M, N, K, _p(mi), _p(ni),
+                                     len(mi), _p(C), _p(Cabs)), "gemm_sampled")
+    return C, Cabs
+
+
+def grouped_gemm_ragged_m(A, sA, B, sB, group_end):
+    """A [T][K], B [G][N][K] -> C [T][N] (rows outside every group stay 0)."""
+    T, K = A.shape
+    G, N, _ = B.shape
+    ge = np.ascontiguousarray(group_end, dtype=np.int32)
+    C = np.zeros((T, N), np.float64)
+    Cabs = np.zeros((T, N), np.float64)
+    _check(lib().oracle_grouped_gemm_ragged_m(_p(A), _p(sA), _p(B), _p(sB), T, N, K, _p(ge), G,
+                                              _p(C), _p(Cabs)), "grouped_gemm_ragged_m")
+    return C, Cabs
+
+
+def grouped_gemm_ragged_m_sampled(A, sA, B, sB, group_end, mi, ni):
+    T, K = A.shape
+    G, N, _ = B.shape
+    ge = np.ascontiguousarray(group_end, dtype=np.int32)
+    mi = np.ascontiguousarray(mi, dtype=np.int64)
+    ni = np.ascontiguousarray(ni, dtype=np.int64)
+    C = np.zeros(len(mi), np.float64)
+    Cabs = np.zeros(len(mi), np.float64)
+    _check(lib().oracle_grouped_gemm_ragged_m_sampled(
+        _p(A), _p(sA), _p(B), _p(sB), T, N, K, _p(ge), G, _p(mi), _p(ni), len(mi),
+        _p(C), _p(Cabs)), "grouped_gemm_ragged_m_sampled")
+    return C, Cabs
+
+
+def grouped_gemm_ragged_k(A, sA, B, sB, group_end):
+    """A [M][ldk], B [N][ldk] grouped token-axis copies -> C [G][M][N]."""
+    M, ldk = A.shape
+    N = B.shape[0]
+    ge = np.ascontiguousarray(group_end, dtype=np.int32)
+    G = len(ge)
+    C = np.zeros((G, M, N), np.float64)
+    Cabs = np.zeros((G, M, N), np.float64)
+    _check(lib().oracle_grouped_gemm_ragged_k(_p(A), _p(sA), _p(B), _p(sB), M, N, ldk, _p(ge), G,
+                                              _p(C), _p(Cabs)), "grouped_gemm_ragged_k")
+    return C, Cabs
+
+
+def grouped_gemm_ragged_k_sampled(A, sA, B, sB, group_end, gi, mi, ni):
+    M, ldk = A.shape
+    N = B.shape[0]
+    ge = np.ascontiguousarray(group_end, dtype=np.int32)
+    gi = np.ascontiguousarray(gi, dtype=np.int32)
+    mi = np.ascontiguousarray(mi, dtype=np.int64)
+    ni = np.ascontiguousarray(ni, dtype=np.int64)
+    C = np.zeros(len(mi), np.float64)
+    Cabs = np.zeros(len(mi), np.float64)
+    _check(lib().oracle_grouped_gemm_ragged_k_sampled(
+        _p(A), _p(sA), _p(B), _p(sB), M, N, ldk, _p(ge), len(ge), _p(gi), _p(mi), _p(ni),
+        len(mi), _p(C), _p(Cabs)), "grouped_gemm_ragged_k_sampled")
+    return C, Cabs
