@@ -1,0 +1,192 @@
+/*
+ * mxq.h -- C ABI of libmxq: MX microscaling quantisation and block-scaled
+ * GEMMs for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow these web pages:
+ *  - torchtitan-npu feature guide "低精度训练特性（MXFP8 / HiFloat8）",
+ *    sections "线性层低精度" (MXFP8 linear: per-block quantisation with 32
+ *    elements sharing one scale, forward, input-gradient and weight-gradient
+ *    GEMMs in FP8, output returned at higher precision) and "MoE 专家层低精度"
+ *    (grouped expert GEMMs; grouped per-block quantisation of the
+ *    weight-gradient operands).
+ *  - MindSpeed pull request 3852 (--fp8-quant-fb-split), "主要改动": expert
+ *    weights quantised on both axes at once in the forward pass, or on the
+ *    forward reduction axis only with the backward axis re-quantised later.
+ *  - "AMCT FakeQuant 模拟伪量化工具包：MXFP4 推理精度验证与 QAT 训练实践",
+ *    section 2 "MXFP4 数值模型" and section 3.3 (MXFP4 quant-dequant).
+ * The pages leave the MXFP8 shared-exponent rule open; the library uses the
+ * OCP MX v1.0 rule (shared = floor(log2(amax)) - 8, elements rounded to
+ * nearest-even and saturated at +-448, all-zero block -> scale byte 0).
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are row-major and live in device memory of the current HIP
+ *    device; host pointers are never accepted for tensor arguments.
+ *  - Ownership: the caller allocates and frees every buffer.  The library
+ *    never allocates or frees device memory, never synchronises, never copies
+ *    group sizes back to the host and keeps no per-call state; it only caches
+ *    the per-device architecture check and a thread-local error message.
+ *  - Work is enqueued on the caller's stream `st` (0 = the null stream).
+ *    Outputs must not alias inputs.  Tensor pointers must be 16-byte aligned.
+ *  - A quantised MXFP8 operand is `codes[rows][Kp]` (one E4M3 byte per
+ *    element, the reduction axis K contiguous, Kp = ceil32(K), padding codes
+ *    0x00) plus `scales[rows][Kp/32]` (one E8M0 byte per block of 32,
+ *    value 2^(byte-127)).
+ *  - "row" copy: blocks along the contiguous dim of the input.  "colT" copy:
+ *    the quantised transpose, blocks running down the columns of the input.
+ *  - Errors: every entry point validates its host-visible arguments first
+ *    and returns a status (never aborts); on failure `mxq_last_error()`
+ *    describes it.  Faults inside kernels surface at the caller's next
+ *    synchronisation of the stream.  Group ends live on the device and are a
+ *    precondition (non-decreasing, last <= rows); kernels clamp them so that a
+ *    malformed array never makes them access memory out of bounds, and
+ *    `mxq_validate_group_end` checks them on the device.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXQ_ABI_VERSION 1
+#define MXQ_BLOCK 32          /* elements per MX block; fixed */
+#define MXQ_MAX_GROUPS 1024   /* largest G the grouped entry points accept */
+
+typedef enum {
+    MXQ_OK = 0,
+    MXQ_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misaligned pointer, bad enum */
+    MXQ_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement */
+    MXQ_ERR_DEVICE = 3,           /* no HIP device, or the current device is not gfx950 */
+    MXQ_ERR_LAUNCH = 4            /* the HIP runtime rejected a kernel launch */
+} mxq_status;
+
+/* axis bitmask for the quantisers; ROW|COLT is the dual-axis quantisation
+ * (both copies from one read of the input). */
+enum { MXQ_AXIS_ROW = 1, MXQ_AXIS_COLT = 2 };
+
+/* element format of a GEMM operand */
+typedef enum { MXQ_FMT_E4M3 = 0 } mxq_fmt;
+
+/* grouped GEMM modes */
+typedef enum {
+    MXQ_GG_RAGGED_M = 0, /* expert forward / input gradient: rows split into groups */
+    MXQ_GG_RAGGED_K = 1  /* expert weight gradient: reduction axis split into groups */
+} mxq_gg_mode;
+
+/* Version of this ABI (MXQ_ABI_VERSION of the built library). */
+int mxq_abi_version(void);
+
+/* Message for the last failed call on this thread ("" if none). Owned by the
+ * library; valid until the next call on the same thread. */
+const char* mxq_last_error(void);
+
+/* MXQ_OK iff HIP device `device` exists and is gfx950. */
+mxq_status mxq_device_check(int device);
+
+/* Columns a grouped token-axis copy of T rows in G groups may need: an upper
+ * bound of sum_g ceil32(m_g), rounded up to 32.  Pure host arithmetic. */
+int64_t mxq_grouped_cols_max(int64_t T, int32_t G);
+
+/*
+ * MXFP8 quantisation of a bf16 matrix x [R][ldx] (R x C used), the per-block
+ * quantisation of activations and weights of the torchtitan-npu guide
+ * ("线性层低精度"), with the axis choice of MindSpeed PR 3852 ("主要改动").
+ *   axis_mask & MXQ_AXIS_ROW : q_row [R][Cp], s_row [R][Cp/32], Cp = ceil32(C)
+ *   axis_mask & MXQ_AXIS_COLT: q_colT [C][Rp], s_colT [C][Rp/32], Rp = ceil32(R)
+ * Pointers for an axis not requested may be NULL.  Both axes together read
+ * x once (dual-axis quantisation).  R, C >= 1; ldx >= C.
+ */
+mxq_status mxq_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int axis_mask,
+                        uint8_t* q_row, uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT,
+                        hipStream_t st);
+
+/*
+ * Grouped token-axis MXFP8 quantisation for the expert weight gradient
+ * (torchtitan-npu guide, "MoE 专家层低精度").  x bf16 [T][ldx] (T x C used);
+ * group g owns rows [end_{g-1}, end_g) with end_g = group_end[g] (device
+ * int32 [G], cumulative, end_{-1} = 0).
+ *   MXQ_AXIS_COLT: q_colT [C][ldq], s_colT [C][ldq/32].  Blocks restart at
+ *     each group start; group g occupies columns [P_g, P_g + ceil32(m_g)),
+ *     P_g = sum_{j<g} ceil32(m_j), its tail zero-padded.  Columns at and past
+ *     P_G are not written.  ldq % 32 == 0; ldq >= sum_g ceil32(m_g) is a
+ *     precondition (mxq_grouped_cols_max(T, G) always suffices); blocks that
+ *     would fall past ldq are dropped.
+ *   MXQ_AXIS_ROW: q_row [T][Cp], s_row [T][Cp/32], identical to
+ *     mxq_quantize's row copy; with COLT the input is read once.
+ * 1 <= G <= MXQ_MAX_GROUPS; T, C >= 1.
+ */
+mxq_status mxq_quantize_grouped(const uint16_t* x, int64_t T, int64_t C, int64_t ldx,
+                                const int32_t* group_end, int32_t G, int64_t ldq, int axis_mask,
+                                uint8_t* q_row, uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT,
+                                hipStream_t st);
+
+/*
+ * MXFP4 quantise-dequantise of the AMCT FakeQuant article (section 2 and
+ * section 3.3).  x, y fp32 [rows][L], L = last dim of the caller's tensor.
+ * Each row is zero-padded to Lp = ceil32(L) on its own, so rows never share a
+ * block.  Per block: scale = 2^round(log2(max|x|/6)) with the raw scale
+ * max|x|/6 clamped at 2^-30 (round taken exactly); each element becomes the
+ * E2M1 codebook value {0,0.5,1,1.5,2,3,4,6} nearest to |x|/scale, ties to the
+ * larger magnitude, everything from 5 up saturating to 6; y = sign(x) * code
+ * * scale (the sign of x is kept also when the code is 0).
+ * Optional outputs (NULL to skip): codes [rows][Lp/2] E2M1 nibbles, element
+ * 2j in the low nibble of byte j, nibble = sign<<3 | codebook index (the OCP
+ * E2M1 bit pattern); scales [rows][Lp/32] E8M0 bytes.  NaN/Inf inputs are
+ * outside the contract.  rows, L >= 1.
+ */
+mxq_status mxq_qdq_fp4(const float* x, float* y, int64_t rows, int64_t L,
+                       uint8_t* codes, uint8_t* scales, hipStream_t st);
+
+/*
+ * Block-scaled GEMM C[m][n] = sum_k deq(A)[m][k] * deq(B)[n][k] (the FP8
+ * linear GEMMs of the torchtitan-npu guide, "线性层低精度"), fp32
+ * accumulation and fp32 output.  A codes [M][K] + scales [M][K/32];
+ * B codes [N][K] + scales [N][K/32]; C fp32 [M][ldc].
+ * Forward Y = X W: A = row copy of X, B = colT copy of W [K][N].
+ * Input gradient dX = dY W^T: A = row copy of dY, B = row copy of W.
+ * Weight gradient dW = X^T dY: A = colT copy of X, B = colT copy of dY.
+ * M, N >= 1; K >= 32, K % 32 == 0; ldc >= N.
+ */
+mxq_status mxq_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
+                    float* C, int64_t M, int64_t N, int64_t K, int64_t ldc, mxq_fmt fmt,
+                    hipStream_t st);
+
+/*
+ * Grouped block-scaled GEMM over ragged expert groups (torchtitan-npu guide,
+ * "MoE 专家层低精度"); group_end device int32 [G] as for mxq_quantize_grouped.
+ *   MXQ_GG_RAGGED_M: A [M][K] (+[M][K/32]); B [G][N][K] (+[G][N][K/32]);
+ *     C fp32 [M][N].  Rows of group g use expert B[g]; rows at or past
+ *     group_end[G-1] are not written.  K >= 32, K % 32 == 0.
+ *     Expert forward: A = row copy of X, B[g] = colT copy of W[g] [K][N].
+ *     Expert input gradient: A = row copy of dY, B[g] = row copy of W[g].
+ *   MXQ_GG_RAGGED_K: A [M][K] and B [N][K] are grouped token-axis copies
+ *     (K = their ldq); C fp32 [G][M][N] with
+ *     C[g] = sum over group g's padded columns of deq(A) deq(B);
+ *     an empty group gets exact zeros.  Expert weight gradient:
+ *     A = grouped copy of X (M = hidden), B = grouped copy of dY (N = ffn).
+ * M, N >= 1; 1 <= G <= MXQ_MAX_GROUPS.
+ */
+mxq_status mxq_grouped_gemm(mxq_gg_mode mode, const uint8_t* A, const uint8_t* sA,
+                            const uint8_t* B, const uint8_t* sB, float* C,
+                            int64_t M, int64_t N, int64_t K,
+                            const int32_t* group_end, int32_t G, mxq_fmt fmt, hipStream_t st);
+
+/*
+ * Device-side check of a group_end array: writes 0 to *flag (device int32)
+ * if group_end is non-decreasing, starts >= 0 and ends <= T, else 1 + the
+ * index of the first offending entry.  Enqueued on `st`; read *flag after
+ * synchronising.  1 <= G <= MXQ_MAX_GROUPS.
+ */
+mxq_status mxq_validate_group_end(const int32_t* group_end, int32_t G, int64_t T,
+                                  int32_t* flag, hipStream_t st);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H */

@@ -1,0 +1,108 @@
+// Device-side helpers shared by the libmxq kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+constexpr int kBlock = 32;  // elements per MX block
+
+typedef short v2i16 __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- lane exchange
+// DPP quad permutations: lane i reads lane i^1 / i^2 of its quad; row half
+// mirror: lane i of each 8-lane group reads lane 7-i (the other quad).
+__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t dpp_half_mirror(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);
+}
+// max over the 4 lanes of a quad (unsigned)
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
+  v = max(v, dpp_xor1(v));
+  v = max(v, dpp_xor2(v));
+  return v;
+}
+
+// ---------------------------------------------------------------- bf16 helpers
+// max of the two bf16 magnitudes held in a dword, as an unsigned 16-bit value
+__device__ __forceinline__ uint32_t absmax_bf16x2(uint32_t a, uint32_t b) {
+  v2u16 x = __builtin_bit_cast(v2u16, a & 0x7FFF7FFFu);
+  v2u16 y = __builtin_bit_cast(v2u16, b & 0x7FFF7FFFu);
+  v2u16 m = __builtin_elementwise_max(x, y);
+  return __builtin_bit_cast(uint32_t, m);
+}
+// per-half maximum of two packed unsigned 16-bit pairs (a plain 32-bit max would
+// compare the high halves first and could drop a larger low half)
+__device__ __forceinline__ uint32_t pkmax_u16(uint32_t a, uint32_t b) {
+  v2u16 m = __builtin_elementwise_max(__builtin_bit_cast(v2u16, a), __builtin_bit_cast(v2u16, b));
+  return __builtin_bit_cast(uint32_t, m);
+}
+__device__ __forceinline__ uint32_t hmax_u16x2(uint32_t v) { return max(v & 0xFFFFu, v >> 16); }
+
+// ---------------------------------------------------------------- MXFP8 (E4M3)
+// E8M0 scale byte of a block from its largest bf16 magnitude (sign cleared):
+// shared = floor(log2 amax) - 8 clamped at -127, i.e. byte = max(Efield - 8, 0);
+// zero and subnormal maxima give byte 0.
+__device__ __forceinline__ uint32_t mxfp8_scale_byte(uint32_t amax16) {
+  uint32_t e = amax16 >> 7;
+  return e > 8u ? e - 8u : 0u;
+}
+
+// The scaled conversion divides by the power of two held in the exponent field of
+// its fp32 scale operand (only that field is used), then rounds to nearest-even;
+// it does not saturate, so magnitudes from 464*scale up come out as the NaN code.
+// Four packed codes: turn S.1111.111 into S.1111.110 (448), the saturated value.
+__device__ __forceinline__ uint32_t e4m3_saturate4(uint32_t c) {
+  uint32_t m = ((c & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+  return c - (m >> 7);
+}
+
+// Four bf16 values (two dwords, element order lo..hi) -> four E4M3 codes.
+__device__ __forceinline__ uint32_t e4m3_encode4(uint32_t lo, uint32_t hi, float scale) {
+  v2i16 r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(v2bf16, lo), scale, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(v2bf16, hi), scale, true);
+  return e4m3_saturate4(__builtin_bit_cast(uint32_t, r));
+}
+
+__device__ __forceinline__ float e8m0_as_scale(uint32_t byte) { return __uint_as_float(byte << 23); }
+
+// ---------------------------------------------------------------- MXFP4 (E2M1)
+// Exact round(log2(amax/6)) clamped at -30 from the fp32 bits of amax: with
+// amax = m * 2^E (m in [1,2)), log2(amax/6) rounds up to E-2 iff m >= 3/(2*sqrt 2),
+// i.e. iff the mantissa field is >= 0x7C3B7, else to E-3.  Subnormal or zero
+// maxima lie far below 6*2^-30.5, so they take the clamp.
+__device__ __forceinline__ int mxfp4_scale_exp(uint32_t amax_bits) {
+  int ef = (int)(amax_bits >> 23);
+  if (ef == 0) return -30;
+  int e = ef - 127 - 3 + ((amax_bits & 0x7FFFFFu) >= 0x7C3B7u ? 1 : 0);
+  return e < -30 ? -30 : e;
+}
+
+// codebook index (0..7 for 0,0.5,1,1.5,2,3,4,6) of |x| / 2^e: count the midpoints
+// |x| reaches (ties go up).  yabs = |x| * 2^-e is exact.
+__device__ __forceinline__ uint32_t mxfp4_index(float yabs) {
+  return (uint32_t)(yabs >= 0.25f) + (uint32_t)(yabs >= 0.75f) + (uint32_t)(yabs >= 1.25f) +
+         (uint32_t)(yabs >= 1.75f) + (uint32_t)(yabs >= 2.5f) + (uint32_t)(yabs >= 3.5f) +
+         (uint32_t)(yabs >= 5.0f);
+}
+
+// fp32 bits of codebook[idx] * 2^e with the sign bit `sign` (0 or 0x80000000).
+// codebook[idx] for idx >= 2 has exponent field 126 + idx/2 and top mantissa bit
+// idx&1, so its bits are (126 << 23) + (idx << 22); 0.5 is 126 << 23.  Adding
+// e << 23 multiplies by 2^e exactly (results stay normal: e >= -30, value >= 0.5).
+__device__ __forceinline__ uint32_t mxfp4_value_bits(uint32_t idx, int e, uint32_t sign) {
+  uint32_t b = idx >= 2u ? (126u << 23) + (idx << 22) : (idx ? (126u << 23) : 0u);
+  if (idx) b += (uint32_t)e << 23;
+  return b | sign;
+}
+
+}  // namespace mxq

@@ -1,0 +1,78 @@
+// Per-workgroup table of ragged groups, built on the device from cumulative
+// group ends (used by the grouped quantiser and the grouped GEMM schedulers).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+constexpr int kMaxGroups = 1024;
+
+// start row and size of every group, and the exclusive prefix of
+// ceil(size / unit) (bstart[G] = total units).  Group ends are clamped into
+// [0, R], so a malformed array never sends an access out of bounds; a valid
+// (non-decreasing, <= R) array is used unchanged.
+struct GroupTable {
+  int32_t start[kMaxGroups];
+  int32_t size[kMaxGroups];
+  int32_t bstart[kMaxGroups + 1];
+};
+
+// All THREADS threads of the workgroup must call this; G <= 4 * THREADS.
+template <int THREADS>
+__device__ void build_group_table(const int32_t* __restrict__ group_end, int32_t G, int64_t R,
+                                  int32_t unit, GroupTable& gt, int32_t* scan_tmp /* [THREADS] */) {
+  static_assert(4 * THREADS >= kMaxGroups, "each thread owns at most four groups");
+  const int t = threadIdx.x;
+  int local = 0;
+  int nb[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int g = t * 4 + j;
+    nb[j] = 0;
+    if (g < G) {
+      int64_t e = group_end[g];
+      int64_t b = g ? (int64_t)group_end[g - 1] : 0;
+      e = e < 0 ? 0 : (e > R ? R : e);
+      b = b < 0 ? 0 : (b > R ? R : b);
+      const int32_t m = e > b ? (int32_t)(e - b) : 0;
+      gt.start[g] = (int32_t)b;
+      gt.size[g] = m;
+      nb[j] = (m + unit - 1) / unit;
+      local += nb[j];
+    }
+  }
+  // exclusive scan of `local` over the workgroup (Hillis-Steele in LDS)
+  scan_tmp[t] = local;
+  __syncthreads();
+  for (int off = 1; off < THREADS; off <<= 1) {
+    const int v = t >= off ? scan_tmp[t - off] : 0;
+    __syncthreads();
+    scan_tmp[t] += v;
+    __syncthreads();
+  }
+  int run = scan_tmp[t] - local;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int g = t * 4 + j;
+    if (g < G) {
+      gt.bstart[g] = run;
+      run += nb[j];
+    }
+  }
+  if (t == THREADS - 1) gt.bstart[G] = scan_tmp[t];
+  __syncthreads();
+}
+
+// largest g with bstart[g] <= u (u < bstart[G] assumed)
+__device__ __forceinline__ int find_group(const GroupTable& gt, int G, int32_t u) {
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (gt.bstart[mid] <= u) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace mxq

@@ -1,0 +1,35 @@
+// Host-side launchers of the libmxq kernels (arguments already validated).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+// number of compute units of the current device (cached per device)
+int device_cu_count();
+
+// MXFP8 row copy: x bf16 [R][ldx] -> q [R][Cp], s [R][Cp/32]
+hipError_t launch_quant_row(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                            uint8_t* q, uint8_t* s, hipStream_t st);
+
+// MXFP8 column copy (and optionally the row copy from the same read).
+// grouped: group_end != nullptr; colT width ldq (multiple of 32).
+hipError_t launch_quant_tile(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                             const int32_t* group_end, int32_t G, int64_t ldq,
+                             uint8_t* q_row, uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT,
+                             hipStream_t st);
+
+// MXFP4 quant-dequant
+hipError_t launch_qdq_fp4(const float* x, float* y, int64_t rows, int64_t L,
+                          uint8_t* codes, uint8_t* scales, hipStream_t st);
+
+// Block-scaled GEMMs.  mode 0: dense (G = 1, no group_end); 1: ragged M; 2: ragged K.
+hipError_t launch_gemm(int mode, const uint8_t* A, const uint8_t* sA, const uint8_t* B,
+                       const uint8_t* sB, float* C, int64_t M, int64_t N, int64_t K, int64_t ldc,
+                       const int32_t* group_end, int32_t G, hipStream_t st);
+
+hipError_t launch_validate_group_end(const int32_t* group_end, int32_t G, int64_t T, int32_t* flag,
+                                     hipStream_t st);
+
+}  // namespace mxq

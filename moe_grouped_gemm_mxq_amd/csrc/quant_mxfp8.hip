@@ -1,0 +1,243 @@
+// MXFP8 quantisers for gfx950: row copy, column copy (quantised transpose),
+// dual-axis (both from one read) and grouped token-axis column copy.
+//
+// Per block of 32 values along the quantised axis (torchtitan-npu guide,
+// "线性层低精度" / "MoE 专家层低精度"): scale byte = max(exponent field of the
+// largest bf16 magnitude - 8, 0) (OCP MX shared exponent floor(log2 amax) - 8),
+// element = E4M3 round-to-nearest-even of v / 2^(byte-127), saturated at 448.
+// The element conversion is the hardware scaled conversion plus a saturation
+// fix-up (see mxq_device.h); it was checked exhaustively over every bf16 value
+// and every scale byte against the CPU oracle.
+#include "mxq_device.h"
+#include "mxq_groups.h"
+#include "mxq_internal.h"
+
+namespace mxq {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// ------------------------------------------------------------------ row copy
+// A row is Cp/8 chunks of 8 bf16 (16 bytes); four consecutive lanes hold one
+// block.  `tpr` (threads per row, a power of two >= 4) lanes share a row and
+// 256/tpr rows are processed per step, so no division is needed.
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void quant_row_kernel(const uint16_t* __restrict__ x, int64_t R,
+                                                            int64_t C, int64_t ldx, int tpr_log2,
+                                                            uint8_t* __restrict__ q,
+                                                            uint8_t* __restrict__ s) {
+  const int64_t Cp = (C + 31) / 32 * 32;
+  const int cpr = (int)(Cp / 8);  // chunks per row
+  const int tpr = 1 << tpr_log2;
+  const int rps = kThreads >> tpr_log2;  // rows per step
+  const int t = threadIdx.x;
+  for (int64_t row0 = (int64_t)blockIdx.x * rps; row0 < R; row0 += (int64_t)gridDim.x * rps) {
+    const int64_t row = row0 + (t >> tpr_log2);
+    const bool row_ok = row < R;  // uniform per quad
+    const uint16_t* xr = x + (row_ok ? row : 0) * ldx;
+    for (int c8 = t & (tpr - 1); c8 < cpr; c8 += tpr) {
+      const int64_t col = (int64_t)c8 * 8;
+      uint32_t w[4];
+      if (VEC && col + 8 <= C) {
+        uint4 v = *reinterpret_cast<const uint4*>(xr + col);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          uint32_t lo = col + 2 * j < C ? xr[col + 2 * j] : 0u;
+          uint32_t hi = col + 2 * j + 1 < C ? xr[col + 2 * j + 1] : 0u;
+          w[j] = lo | (hi << 16);
+        }
+      }
+      uint32_t m = hmax_u16x2(pkmax_u16(absmax_bf16x2(w[0], w[1]), absmax_bf16x2(w[2], w[3])));
+      m = quad_max_u32(m);
+      const uint32_t byte = mxfp8_scale_byte(m);
+      const float sc = e8m0_as_scale(byte);
+      uint2 codes;
+      codes.x = e4m3_encode4(w[0], w[1], sc);
+      codes.y = e4m3_encode4(w[2], w[3], sc);
+      if (row_ok) {
+        *reinterpret_cast<uint2*>(q + row * Cp + col) = codes;
+        if ((c8 & 3) == 0) s[row * (Cp / 32) + c8 / 4] = (uint8_t)byte;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ tile kernel
+// A 128 x 128 bf16 tile (128 rows of padded position space = 4 blocks, 128
+// columns) is read once with coalesced 16-byte loads, optionally quantised
+// along its rows (four lanes per block), staged in LDS, and quantised down its
+// columns: each thread takes a column pair and one block of 32 rows.
+constexpr int kTR = 128, kTC = 128, kLdsStride = kTC * 2 + 16;
+
+template <bool ROW, bool GROUPED, bool VEC>
+__global__ __launch_bounds__(kThreads) void quant_tile_kernel(
+    const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx,
+    const int32_t* __restrict__ group_end, int32_t G, int64_t ldq, int n_col_tiles,
+    uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row, uint8_t* __restrict__ q_colT,
+    uint8_t* __restrict__ s_colT) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kTR * kLdsStride];
+  __shared__ int64_t rb_src[kTR / 32];   // first source row of each block of the tile
+  __shared__ int32_t rb_valid[kTR / 32]; // valid rows in that block (0: no output block)
+  const int t = threadIdx.x;
+  const int rt = blockIdx.x / n_col_tiles;
+  const int ct = blockIdx.x - rt * n_col_tiles;
+  const int64_t p0 = (int64_t)rt * kTR;  // first padded position of the tile
+  const int64_t c0 = (int64_t)ct * kTC;
+
+  if constexpr (GROUPED) {
+    __shared__ GroupTable gt;
+    __shared__ int32_t scan_tmp[kThreads];
+    build_group_table<kThreads>(group_end, G, R, 32, gt, scan_tmp);
+    if (t < kTR / 32) {
+      const int64_t pb = p0 / 32 + t;
+      int64_t src = 0;
+      int32_t valid = 0;
+      if (pb < gt.bstart[G] && (pb + 1) * 32 <= ldq) {
+        const int g = find_group(gt, G, (int32_t)pb);
+        const int32_t off = ((int32_t)pb - gt.bstart[g]) * 32;
+        src = (int64_t)gt.start[g] + off;
+        valid = min(32, gt.size[g] - off);
+        if (valid <= 0) valid = -1;  // cannot happen for consistent tables
+      }
+      rb_src[t] = src;
+      rb_valid[t] = valid;
+    }
+  } else {
+    if (t < kTR / 32) {
+      const int64_t r0 = p0 + 32 * t;
+      rb_src[t] = r0;
+      rb_valid[t] = r0 < R ? (int32_t)min<int64_t>(32, R - r0) : 0;
+    }
+  }
+  __syncthreads();
+  if (rb_valid[0] <= 0) return;  // tile lies past the last block (uniform)
+
+  const int64_t Cp = (C + 31) / 32 * 32;
+  // ---- phase 1: load (+ row copy), stage in LDS
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int lr = (t >> 4) + 16 * i;  // tile row
+    const int c16 = t & 15;
+    const int rb = lr >> 5;
+    const int32_t valid = rb_valid[rb];
+    const bool row_ok = (lr & 31) < valid;
+    const int64_t src = rb_src[rb] + (lr & 31);
+    const int64_t col = c0 + c16 * 8;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (row_ok) {
+      const uint16_t* xr = x + src * ldx;
+      if (VEC && col + 8 <= C) {
+        uint4 v = *reinterpret_cast<const uint4*>(xr + col);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          uint32_t lo = col + 2 * j < C ? xr[col + 2 * j] : 0u;
+          uint32_t hi = col + 2 * j + 1 < C ? xr[col + 2 * j + 1] : 0u;
+          w[j] = lo | (hi << 16);
+        }
+      }
+    }
+    if constexpr (ROW) {
+      uint32_t m = hmax_u16x2(pkmax_u16(absmax_bf16x2(w[0], w[1]), absmax_bf16x2(w[2], w[3])));
+      m = quad_max_u32(m);
+      const uint32_t byte = mxfp8_scale_byte(m);
+      const float sc = e8m0_as_scale(byte);
+      uint2 codes;
+      codes.x = e4m3_encode4(w[0], w[1], sc);
+      codes.y = e4m3_encode4(w[2], w[3], sc);
+      if (row_ok && col < Cp) {
+        *reinterpret_cast<uint2*>(q_row + src * Cp + col) = codes;
+        if ((c16 & 3) == 0) s_row[src * (Cp / 32) + col / 32] = (uint8_t)byte;
+      }
+    }
+    *reinterpret_cast<uint4*>(tile + lr * kLdsStride + c16 * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  __syncthreads();
+
+  // ---- phase 2: column copy
+  const int pr = t & 63;  // column pair
+  const int rb = t >> 6;  // block of 32 tile rows
+  const int64_t col = c0 + 2 * pr;
+  if (rb_valid[rb] <= 0 || col >= C) return;
+  const int64_t pb = p0 / 32 + rb;  // padded block = output block column
+  uint32_t d[32];
+#pragma unroll
+  for (int i = 0; i < 32; i++)
+    d[i] = *reinterpret_cast<const uint32_t*>(tile + (rb * 32 + i) * kLdsStride + 4 * pr);
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 32; i += 2) m = pkmax_u16(m, absmax_bf16x2(d[i], d[i + 1]));
+  // absmax_bf16x2 keeps per-half maxima: low half = column col, high half = col + 1
+  const uint32_t byte_lo = mxfp8_scale_byte(m & 0xFFFFu);
+  const uint32_t byte_hi = mxfp8_scale_byte(m >> 16);
+  const float sc_lo = e8m0_as_scale(byte_lo), sc_hi = e8m0_as_scale(byte_hi);
+  uint32_t clo[8], chi[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const uint32_t a0 = __builtin_amdgcn_perm(d[4 * i + 1], d[4 * i], 0x05040100u);
+    const uint32_t a1 = __builtin_amdgcn_perm(d[4 * i + 3], d[4 * i + 2], 0x05040100u);
+    const uint32_t b0 = __builtin_amdgcn_perm(d[4 * i + 1], d[4 * i], 0x07060302u);
+    const uint32_t b1 = __builtin_amdgcn_perm(d[4 * i + 3], d[4 * i + 2], 0x07060302u);
+    clo[i] = e4m3_encode4(a0, a1, sc_lo);
+    chi[i] = e4m3_encode4(b0, b1, sc_hi);
+  }
+  const int64_t nsb = ldq / 32;
+  uint8_t* dst = q_colT + col * ldq + pb * 32;
+  reinterpret_cast<uint4*>(dst)[0] = make_uint4(clo[0], clo[1], clo[2], clo[3]);
+  reinterpret_cast<uint4*>(dst)[1] = make_uint4(clo[4], clo[5], clo[6], clo[7]);
+  s_colT[col * nsb + pb] = (uint8_t)byte_lo;
+  if (col + 1 < C) {
+    dst += ldq;
+    reinterpret_cast<uint4*>(dst)[0] = make_uint4(chi[0], chi[1], chi[2], chi[3]);
+    reinterpret_cast<uint4*>(dst)[1] = make_uint4(chi[4], chi[5], chi[6], chi[7]);
+    s_colT[(col + 1) * nsb + pb] = (uint8_t)byte_hi;
+  }
+}
+
+int grid_cap() { return device_cu_count() * 8; }
+
+}  // namespace
+
+hipError_t launch_quant_row(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q,
+                            uint8_t* s, hipStream_t st) {
+  const int64_t cpr = (C + 31) / 32 * 4;
+  int tpr_log2 = 2;
+  while ((1 << tpr_log2) < cpr && tpr_log2 < 8) tpr_log2++;
+  const int64_t rps = kThreads >> tpr_log2;
+  const int64_t want = (R + rps - 1) / rps;
+  const int grid = (int)(want < grid_cap() ? want : grid_cap());
+  const bool vec = (ldx % 8 == 0) && ((uintptr_t)x % 16 == 0);
+  if (vec)
+    quant_row_kernel<true><<<grid, kThreads, 0, st>>>(x, R, C, ldx, tpr_log2, q, s);
+  else
+    quant_row_kernel<false><<<grid, kThreads, 0, st>>>(x, R, C, ldx, tpr_log2, q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_tile(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
+                             const int32_t* group_end, int32_t G, int64_t ldq, uint8_t* q_row,
+                             uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT, hipStream_t st) {
+  const bool grouped = group_end != nullptr;
+  const bool row = q_row != nullptr;
+  const bool vec = (ldx % 8 == 0) && ((uintptr_t)x % 16 == 0);
+  const int64_t padded = grouped ? (R + 31 * (int64_t)G) : R;
+  const int64_t n_row_tiles = (padded + kTR - 1) / kTR;
+  const int n_col_tiles = (int)((C + kTC - 1) / kTC);
+  const int64_t grid = n_row_tiles * n_col_tiles;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+#define MXQ_TILE_LAUNCH(ROWv, GRPv, VECv)                                                     \
+  quant_tile_kernel<ROWv, GRPv, VECv><<<(unsigned)grid, kThreads, 0, st>>>(                 \
+      x, R, C, ldx, group_end, G, ldq, n_col_tiles, q_row, s_row, q_colT, s_colT)
+  if (row && grouped) { if (vec) MXQ_TILE_LAUNCH(true, true, true); else MXQ_TILE_LAUNCH(true, true, false); }
+  else if (row) { if (vec) MXQ_TILE_LAUNCH(true, false, true); else MXQ_TILE_LAUNCH(true, false, false); }
+  else if (grouped) { if (vec) MXQ_TILE_LAUNCH(false, true, true); else MXQ_TILE_LAUNCH(false, true, false); }
+  else { if (vec) MXQ_TILE_LAUNCH(false, false, true); else MXQ_TILE_LAUNCH(false, false, false); }
+#undef MXQ_TILE_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace mxq

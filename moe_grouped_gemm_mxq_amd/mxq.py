@@ -1,0 +1,265 @@
+"""ctypes binding of libmxq (include/mxq.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libmxq.so``; PyTorch supplies device memory and streams.  Importing
+this module fails loudly (RuntimeError) when the library is not built -- there
+is no fallback.
+
+Functions named like the C entry points take every buffer from the caller;
+the lower-case helpers (``quantize``, ``gemm`` ...) allocate the outputs with
+``torch.empty`` and call them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("MXQ_LIB_PATH") or os.path.join(HERE, "libmxq.so")
+
+MXQ_OK = 0
+MXQ_ERR_INVALID_ARGUMENT = 1
+MXQ_ERR_UNSUPPORTED = 2
+MXQ_ERR_DEVICE = 3
+MXQ_ERR_LAUNCH = 4
+STATUS_NAMES = {0: "MXQ_OK", 1: "MXQ_ERR_INVALID_ARGUMENT", 2: "MXQ_ERR_UNSUPPORTED",
+                3: "MXQ_ERR_DEVICE", 4: "MXQ_ERR_LAUNCH"}
+
+MXQ_AXIS_ROW = 1
+MXQ_AXIS_COLT = 2
+MXQ_FMT_E4M3 = 0
+MXQ_GG_RAGGED_M = 0
+MXQ_GG_RAGGED_K = 1
+BLOCK = 32
+MAX_GROUPS = 1024
+
+EXPORTED = [
+    "mxq_abi_version", "mxq_last_error", "mxq_device_check", "mxq_grouped_cols_max",
+    "mxq_quantize", "mxq_quantize_grouped", "mxq_qdq_fp4", "mxq_gemm", "mxq_grouped_gemm",
+    "mxq_validate_group_end",
+]
+
+
+def _load(path: str = LIB_PATH):
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"libmxq.so not found at {path}. Build it with "
+            "`python -m moe_grouped_gemm_mxq_amd.build` (hipcc, gfx950) or point MXQ_LIB_PATH at a build.")
+    lib = ctypes.CDLL(path)
+    P, I64, I32, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+    sig = {
+        "mxq_abi_version": ([], I),
+        "mxq_last_error": ([], ctypes.c_char_p),
+        "mxq_device_check": ([I], I),
+        "mxq_grouped_cols_max": ([I64, I32], I64),
+        "mxq_quantize": ([P, I64, I64, I64, I, P, P, P, P, P], I),
+        "mxq_quantize_grouped": ([P, I64, I64, I64, P, I32, I64, I, P, P, P, P, P], I),
+        "mxq_qdq_fp4": ([P, P, I64, I64, P, P, P], I),
+        "mxq_gemm": ([P, P, P, P, P, I64, I64, I64, I64, I, P], I),
+        "mxq_grouped_gemm": ([I, P, P, P, P, P, I64, I64, I64, P, I32, I, P], I),
+        "mxq_validate_group_end": ([P, I32, I64, P, P], I),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+
+
+class MxqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.mxq_last_error().decode()
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {msg}")
+
+
+def _check(status: int, where: str):
+    if status != MXQ_OK:
+        raise MxqError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _need(t, dtype, name, dim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims, got {t.dim()}")
+
+
+def ceil32(v: int) -> int:
+    return (v + BLOCK - 1) // BLOCK * BLOCK
+
+
+# ------------------------------------------------------------------ C entry points
+def mxq_abi_version() -> int:
+    return _lib.mxq_abi_version()
+
+
+def mxq_last_error() -> str:
+    return _lib.mxq_last_error().decode()
+
+
+def mxq_device_check(device: int = 0) -> int:
+    return _lib.mxq_device_check(device)
+
+
+def mxq_grouped_cols_max(T: int, G: int) -> int:
+    return _lib.mxq_grouped_cols_max(T, G)
+
+
+def mxq_quantize(x, axis_mask, q_row=None, s_row=None, q_colT=None, s_colT=None, stream=None):
+    """x bf16 [R][C] (unit column stride, any row stride)."""
+    _need(x, torch.bfloat16, "x", 2)
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit stride along its last dim")
+    R, C = x.shape
+    _check(_lib.mxq_quantize(_ptr(x), R, C, x.stride(0), axis_mask, _ptr(q_row), _ptr(s_row),
+                             _ptr(q_colT), _ptr(s_colT), _stream(stream, x.device)), "mxq_quantize")
+
+
+def mxq_quantize_grouped(x, group_end, ldq, axis_mask, q_row=None, s_row=None, q_colT=None,
+                         s_colT=None, stream=None):
+    _need(x, torch.bfloat16, "x", 2)
+    _need(group_end, torch.int32, "group_end", 1)
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit stride along its last dim")
+    T, C = x.shape
+    _check(_lib.mxq_quantize_grouped(_ptr(x), T, C, x.stride(0), _ptr(group_end), group_end.numel(),
+                                     ldq, axis_mask, _ptr(q_row), _ptr(s_row), _ptr(q_colT),
+                                     _ptr(s_colT), _stream(stream, x.device)), "mxq_quantize_grouped")
+
+
+def mxq_qdq_fp4(x, y, codes=None, scales=None, stream=None):
+    """x, y fp32 contiguous, same shape; blocks along the last dim."""
+    _need(x, torch.float32, "x")
+    _need(y, torch.float32, "y")
+    if not (x.is_contiguous() and y.is_contiguous()) or x.shape != y.shape:
+        raise ValueError("x and y must be contiguous and of the same shape")
+    L = x.shape[-1] if x.dim() else 1
+    rows = x.numel() // L if L else 0
+    _check(_lib.mxq_qdq_fp4(_ptr(x), _ptr(y), rows, L, _ptr(codes), _ptr(scales),
+                            _stream(stream, x.device)), "mxq_qdq_fp4")
+
+
+def mxq_gemm(A, sA, B, sB, C, stream=None):
+    """A uint8 [M][K], sA [M][K/32], B [N][K], sB [N][K/32] -> C fp32 [M][ldc >= N]."""
+    for t, n in ((A, "A"), (sA, "sA"), (B, "B"), (sB, "sB")):
+        _need(t, torch.uint8, n, 2)
+    _need(C, torch.float32, "C", 2)
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or sA.shape != (M, K // BLOCK) or sB.shape != (N, K // BLOCK):
+        raise ValueError("operand shapes disagree")
+    if C.shape[0] != M or C.shape[1] < N or C.stride(1) != 1:
+        raise ValueError("C must be [M][>=N] with unit column stride")
+    _check(_lib.mxq_gemm(_ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(C), M, N, K, C.stride(0),
+                         MXQ_FMT_E4M3, _stream(stream, A.device)), "mxq_gemm")
+
+
+def mxq_grouped_gemm(mode, A, sA, B, sB, C, group_end, stream=None):
+    """RAGGED_M: A [M][K], B [G][N][K], C [M][N].  RAGGED_K: A [M][K], B [N][K], C [G][M][N]."""
+    for t, n in ((A, "A"), (sA, "sA"), (B, "B"), (sB, "sB")):
+        _need(t, torch.uint8, n)
+    _need(C, torch.float32, "C")
+    _need(group_end, torch.int32, "group_end", 1)
+    G = group_end.numel()
+    M, K = A.shape
+    N = B.shape[-2]
+    if mode == MXQ_GG_RAGGED_M:
+        ok = B.shape == (G, N, K) and sB.shape == (G, N, K // BLOCK) and C.shape == (M, N)
+    else:
+        N = B.shape[0]
+        ok = B.shape == (N, K) and sB.shape == (N, K // BLOCK) and C.shape == (G, M, N)
+    if not ok or sA.shape != (M, K // BLOCK) or not C.is_contiguous():
+        raise ValueError("grouped GEMM operand shapes disagree")
+    _check(_lib.mxq_grouped_gemm(mode, _ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(C), M, N, K,
+                                 _ptr(group_end), G, MXQ_FMT_E4M3, _stream(stream, A.device)),
+           "mxq_grouped_gemm")
+
+
+def mxq_validate_group_end(group_end, T, flag, stream=None):
+    _need(group_end, torch.int32, "group_end", 1)
+    _need(flag, torch.int32, "flag")
+    _check(_lib.mxq_validate_group_end(_ptr(group_end), group_end.numel(), T, _ptr(flag),
+                                       _stream(stream, group_end.device)), "mxq_validate_group_end")
+
+
+# ------------------------------------------------------------------ allocate-and-call helpers
+def _u8(shape, device):
+    return torch.empty(shape, dtype=torch.uint8, device=device)
+
+
+def quantize(x, axis_mask=MXQ_AXIS_ROW | MXQ_AXIS_COLT, stream=None):
+    """Returns a dict with 'q_row', 's_row' and/or 'q_colT', 's_colT'."""
+    R, C = x.shape
+    out = {}
+    if axis_mask & MXQ_AXIS_ROW:
+        out["q_row"] = _u8((R, ceil32(C)), x.device)
+        out["s_row"] = _u8((R, ceil32(C) // BLOCK), x.device)
+    if axis_mask & MXQ_AXIS_COLT:
+        out["q_colT"] = _u8((C, ceil32(R)), x.device)
+        out["s_colT"] = _u8((C, ceil32(R) // BLOCK), x.device)
+    mxq_quantize(x, axis_mask, out.get("q_row"), out.get("s_row"), out.get("q_colT"),
+                 out.get("s_colT"), stream)
+    return out
+
+
+def quantize_grouped(x, group_end, axis_mask=MXQ_AXIS_COLT, ldq=None, stream=None):
+    T, C = x.shape
+    if ldq is None:
+        ldq = mxq_grouped_cols_max(T, group_end.numel())
+    out = {"ldq": ldq}
+    if axis_mask & MXQ_AXIS_ROW:
+        out["q_row"] = _u8((T, ceil32(C)), x.device)
+        out["s_row"] = _u8((T, ceil32(C) // BLOCK), x.device)
+    if axis_mask & MXQ_AXIS_COLT:
+        out["q_colT"] = _u8((C, ldq), x.device)
+        out["s_colT"] = _u8((C, ldq // BLOCK), x.device)
+    mxq_quantize_grouped(x, group_end, ldq, axis_mask, out.get("q_row"), out.get("s_row"),
+                         out.get("q_colT"), out.get("s_colT"), stream)
+    return out
+
+
+def qdq_fp4(x, want_codes=False, stream=None):
+    y = torch.empty_like(x)
+    codes = scales = None
+    if want_codes:
+        L = x.shape[-1]
+        rows = x.numel() // L
+        codes = _u8((rows, ceil32(L) // 2), x.device)
+        scales = _u8((rows, ceil32(L) // BLOCK), x.device)
+    mxq_qdq_fp4(x, y, codes, scales, stream)
+    return (y, codes, scales) if want_codes else y
+
+
+def gemm(A, sA, B, sB, stream=None):
+    C = torch.empty((A.shape[0], B.shape[0]), dtype=torch.float32, device=A.device)
+    mxq_gemm(A, sA, B, sB, C, stream)
+    return C
+
+
+def grouped_gemm(mode, A, sA, B, sB, group_end, stream=None):
+    if mode == MXQ_GG_RAGGED_M:
+        C = torch.empty((A.shape[0], B.shape[1]), dtype=torch.float32, device=A.device)
+    else:
+        C = torch.empty((group_end.numel(), A.shape[0], B.shape[0]), dtype=torch.float32, device=A.device)
+    mxq_grouped_gemm(mode, A, sA, B, sB, C, group_end, stream)
+    return C

@@ -1,0 +1,127 @@
+"""Helpers shared by the GPU parity tests (imported only by tests marked gpu)."""
+import numpy as np
+import torch
+
+import oracle
+from moe_grouped_gemm_mxq_amd.workloads import bf16_bits
+
+GEMM_TOL = 1e-5   # |err| <= GEMM_TOL * sum_k |a_k b_k| per element (fp32 accumulation)
+
+
+def mxq():
+    from moe_grouped_gemm_mxq_amd import mxq as m
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return m
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def bits(x: torch.Tensor) -> np.ndarray:
+    """bf16 tensor (any device) -> uint16 bit patterns on the host."""
+    return bf16_bits(x)
+
+
+def scaled_randn(shape, seed, lo=-20, hi=20, zero_rows=0, axis=0):
+    """N(0,1) bf16 times a random power of two per row (axis=0) or per column
+    (axis=1), plus some all-zero rows.  Scaling whole reduction vectors keeps
+    the within-block value distribution of the N(0,1) workloads."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(shape, generator=g)
+    if axis == 0:
+        x = x * torch.exp2(torch.randint(lo, hi, (shape[0], 1), generator=g).float())
+    else:
+        x = x * torch.exp2(torch.randint(lo, hi, (1, shape[1]), generator=g).float())
+    if zero_rows:
+        x[torch.randperm(shape[0], generator=g)[:zero_rows]] = 0.0
+    return x.to(torch.bfloat16)
+
+
+def mfma_group_bound(A, sA, B, sB, mi=None, ni=None):
+    """Error bound of the gfx950 FP8 scaled MFMA's internal summation: it adds
+    each group of 8 consecutive-K products with about 13 bits below the group's
+    largest product (measured), so per output
+    |err| <= 2^-10 * sum over groups of max |product| (on top of fp32 rounding)."""
+    a = oracle.mxfp8_dequant(A, sA)
+    b = oracle.mxfp8_dequant(B, sB)
+    if mi is not None:
+        a = a[mi]
+    if ni is not None:
+        b = b[ni]
+    M, K = a.shape
+    N = b.shape[0]
+    ga = np.abs(a).reshape(M, K // 8, 8)
+    gb = np.abs(b).reshape(N, K // 8, 8)
+    out = np.zeros((M, N))
+    for j in range(K // 8):
+        out += np.max(ga[:, j, None, :] * gb[None, :, j, :], axis=2)
+    return 2.0 ** -10 * out
+
+
+def assert_gemm_close(got: np.ndarray, ref: np.ndarray, refabs: np.ndarray, what: str,
+                      hw_bound: np.ndarray | None = None):
+    """|got - ref| <= 1e-5 * sum|ab| per element, plus `hw_bound` (the FP8 MFMA
+    group-truncation term of mfma_group_bound) where the reduction is short.
+    Returns max err / sum|ab| (the strict ratio)."""
+    got = np.asarray(got, np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
+    err = np.abs(got - ref)
+    bound = GEMM_TOL * refabs + (0.0 if hw_bound is None else hw_bound)
+    bad = err > bound
+    ratio = float(np.max(err / np.where(refabs > 0, refabs, 1.0)))
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} outputs outside the bound "
+                           f"({'strict' if hw_bound is None else 'with MFMA group term'}); "
+                           f"max err/sum|ab| = {ratio:.3e}")
+    return ratio
+
+
+def boundary_indices(n: int, tile: int, rng, extra: int) -> np.ndarray:
+    """Tile-boundary indices (first/last of every few tiles) plus random ones."""
+    idx = {0, n - 1}
+    for t0 in range(0, n, tile):
+        idx.update({t0, min(t0 + tile - 1, n - 1)})
+    idx = sorted(i for i in idx if 0 <= i < n)
+    if len(idx) > extra:
+        idx = list(rng.choice(idx, extra, replace=False))
+    idx += list(rng.integers(0, n, extra))
+    return np.unique(np.asarray(idx, np.int64))
+
+
+def assert_bytes_equal(got: np.ndarray, ref: np.ndarray, what: str):
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
+    bad = np.argwhere(got != ref)
+    if len(bad):
+        ex = [(tuple(int(i) for i in b), int(got[tuple(b)]), int(ref[tuple(b)])) for b in bad[:8]]
+        raise AssertionError(f"{what}: {len(bad)} of {got.size} bytes differ; first (index, got, want): {ex}")
+
+
+def ragged_m_bound(A, sA, Bq, Bs, ge):
+    """mfma_group_bound for a ragged-M grouped GEMM (rows of group g x B[g])."""
+    out = np.zeros((A.shape[0], Bq.shape[1]))
+    start = 0
+    for g, e in enumerate(np.asarray(ge).tolist()):
+        if e > start:
+            out[start:e] = mfma_group_bound(np.ascontiguousarray(A[start:e]), np.ascontiguousarray(sA[start:e]),
+                                            Bq[g], Bs[g])
+        start = e
+    return out
+
+
+def ragged_k_bound(A, sA, B, sB, ge):
+    """mfma_group_bound for a ragged-K grouped GEMM over each group's padded columns."""
+    G = len(ge)
+    out = np.zeros((G, A.shape[0], B.shape[0]))
+    P, start = 0, 0
+    for g, e in enumerate(np.asarray(ge).tolist()):
+        w = (e - start + 31) // 32 * 32
+        if w:
+            sl = slice(P, P + w)
+            ss = slice(P // 32, (P + w) // 32)
+            out[g] = mfma_group_bound(np.ascontiguousarray(A[:, sl]), np.ascontiguousarray(sA[:, ss]),
+                                      np.ascontiguousarray(B[:, sl]), np.ascontiguousarray(sB[:, ss]))
+        P += w
+        start = e
+    return out

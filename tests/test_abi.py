@@ -1,0 +1,124 @@
+"""Host-side checks of the C ABI (no GPU needed): libmxq.so loads, exports
+every entry point include/mxq.h declares, validates arguments before touching
+a device, and the Python binding fails loudly when the library is missing."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxq.h")
+LIB = os.path.join(ROOT, "moe_grouped_gemm_mxq_amd", "libmxq.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from moe_grouped_gemm_mxq_amd.build import build
+        build()
+    return ctypes.CDLL(LIB)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["mxq_quantize", "mxq_quantize_grouped", "mxq_qdq_fp4", "mxq_gemm",
+              "mxq_grouped_gemm", "mxq_validate_group_end", "mxq_last_error", "mxq_device_check"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"libmxq.so does not export {n}"
+    from moe_grouped_gemm_mxq_amd import mxq
+    assert sorted(mxq.EXPORTED) == declared_functions()
+
+
+def test_build_targets_gfx950_only():
+    from moe_grouped_gemm_mxq_amd import build
+    arch = [f for f in build.FLAGS if f.startswith("--offload-arch")]
+    assert arch == ["--offload-arch=gfx950"]
+    assert "-packed-fp32-ops" in build.FLAGS
+
+
+def test_abi_version_and_pure_host_helpers(lib):
+    lib.mxq_abi_version.restype = ctypes.c_int
+    assert lib.mxq_abi_version() == 1
+    f = lib.mxq_grouped_cols_max
+    f.restype = ctypes.c_int64
+    f.argtypes = [ctypes.c_int64, ctypes.c_int32]
+    assert f(131072, 32) == 131072 + 992
+    assert f(1, 1) == 32
+    assert f(70, 6) % 32 == 0 and f(70, 6) >= 70 + 31 * 6
+
+
+def call(lib, name, *args):
+    fn = getattr(lib, name)
+    fn.restype = ctypes.c_int
+    return fn(*args)
+
+
+def err(lib):
+    lib.mxq_last_error.restype = ctypes.c_char_p
+    return lib.mxq_last_error().decode()
+
+
+P = ctypes.c_void_p
+I64 = ctypes.c_int64
+FAKE = P(0x1000)       # never dereferenced: validation fails before any device work
+
+
+def test_invalid_arguments_are_rejected_on_the_host(lib):
+    # NULL input
+    assert call(lib, "mxq_quantize", P(0), I64(4), I64(32), I64(32), 1, FAKE, FAKE, P(0), P(0), P(0)) == 1
+    assert "NULL" in err(lib)
+    # bad sizes / axis / ldx
+    assert call(lib, "mxq_quantize", FAKE, I64(0), I64(32), I64(32), 1, FAKE, FAKE, P(0), P(0), P(0)) == 1
+    assert call(lib, "mxq_quantize", FAKE, I64(4), I64(32), I64(16), 1, FAKE, FAKE, P(0), P(0), P(0)) == 1
+    assert call(lib, "mxq_quantize", FAKE, I64(4), I64(32), I64(32), 4, FAKE, FAKE, FAKE, FAKE, P(0)) == 1
+    # misaligned code output
+    assert call(lib, "mxq_quantize", FAKE, I64(4), I64(32), I64(32), 1, P(0x1001), FAKE, P(0), P(0), P(0)) == 1
+    # GEMM: K not a multiple of 32, ldc < N, bad format
+    assert call(lib, "mxq_gemm", FAKE, FAKE, FAKE, FAKE, FAKE, I64(4), I64(4), I64(48), I64(4), 0, P(0)) == 1
+    assert "multiple of 32" in err(lib)
+    assert call(lib, "mxq_gemm", FAKE, FAKE, FAKE, FAKE, FAKE, I64(4), I64(8), I64(64), I64(4), 0, P(0)) == 1
+    assert call(lib, "mxq_gemm", FAKE, FAKE, FAKE, FAKE, FAKE, I64(4), I64(4), I64(64), I64(4), 7, P(0)) == 2
+    # grouped: G out of range, bad mode, ldq not a multiple of 32
+    assert call(lib, "mxq_grouped_gemm", 0, FAKE, FAKE, FAKE, FAKE, FAKE, I64(4), I64(4), I64(64), FAKE,
+                ctypes.c_int32(0), 0, P(0)) == 1
+    assert call(lib, "mxq_grouped_gemm", 5, FAKE, FAKE, FAKE, FAKE, FAKE, I64(4), I64(4), I64(64), FAKE,
+                ctypes.c_int32(2), 0, P(0)) == 1
+    assert call(lib, "mxq_quantize_grouped", FAKE, I64(64), I64(32), I64(32), FAKE, ctypes.c_int32(2),
+                I64(40), 2, P(0), P(0), FAKE, FAKE, P(0)) == 1
+    assert call(lib, "mxq_qdq_fp4", FAKE, P(0), I64(2), I64(33), P(0), P(0), P(0)) == 1
+    assert call(lib, "mxq_validate_group_end", FAKE, ctypes.c_int32(2000), I64(5), FAKE, P(0)) == 1
+
+
+def _gpu_present():
+    r = subprocess.run([sys.executable, "-c", "import torch; print(torch.cuda.device_count())"],
+                       capture_output=True, text=True)
+    return r.stdout.strip() not in ("", "0")
+
+
+def test_valid_call_without_gfx950_reports_device_error(lib):
+    if _gpu_present():
+        pytest.skip("a GPU is present; this checks the no-device path")
+    assert call(lib, "mxq_device_check", 0) == 3
+    assert call(lib, "mxq_quantize", FAKE, I64(4), I64(32), I64(32), 1, FAKE, FAKE, P(0), P(0), P(0)) == 3
+    assert err(lib)
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    env = dict(os.environ, MXQ_LIB_PATH=str(tmp_path / "missing.so"))
+    r = subprocess.run([sys.executable, "-c", "import moe_grouped_gemm_mxq_amd.mxq"], cwd=ROOT,
+                       env=env, capture_output=True, text=True)
+    assert r.returncode != 0
+    assert "RuntimeError" in r.stderr and "libmxq.so not found" in r.stderr

@@ -1,0 +1,175 @@
+"""GPU parity of the quantisers (MXFP4 QDQ, MXFP8 row / column / dual /
+grouped) against the CPU oracle: codes, scales and dequantised values must be
+bit-exact.  The oracle always quantises the seeded bf16/fp32 inputs itself."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import assert_bytes_equal, bits, host, mxq, scaled_randn
+from moe_grouped_gemm_mxq_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ MXFP4 QDQ
+def check_qdq(x: torch.Tensor, what: str):
+    m = mxq()
+    y, codes, scales = m.qdq_fp4(x.cuda(), want_codes=True)
+    torch.cuda.synchronize()
+    yr, cr, sr = oracle.mxfp4_qdq(x.numpy(), want_codes=True)
+    assert np.array_equal(host(y).view(np.uint32), yr.view(np.uint32)), f"{what}: values differ"
+    assert np.array_equal(host(codes), cr), f"{what}: nibbles differ"
+    assert np.array_equal(host(scales), sr), f"{what}: scales differ"
+
+
+def test_qdq_page_test_shapes():
+    for x in workloads.qdq_small():
+        check_qdq(x, f"qdq {tuple(x.shape)}")
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (5, 32), (7, 64), (3, 100), (9, 31), (2, 4097)])
+def test_qdq_ragged_and_aligned_shapes(shape):
+    g = torch.Generator().manual_seed(sum(shape))
+    x = torch.randn(shape, generator=g) * torch.exp2(torch.randint(-40, 40, (shape[0], 1), generator=g).float())
+    check_qdq(x, f"qdq {shape}")
+
+
+def test_qdq_crafted_thresholds_ties_and_extremes():
+    rows = []
+    for E in range(-100, 127, 3):     # the round-half threshold pair in many binades
+        for mant in (0x7C3B6, 0x7C3B7):
+            a = np.array([(E + 127) << 23 | mant], np.uint32).view(np.float32)[0]
+            rows.append([a] + [a * f for f in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.041)] + [0.0] * 23)
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    for k in (-30, -10, 0, 20, 100):
+        s = 2.0 ** k
+        rows.append([6 * s] + [m * s for m in mids] + [-m * s for m in mids] + [-0.0, 0.0] * 8 + [1e-45])
+    fmax = float(np.finfo(np.float32).max)
+    rows.append([fmax, -fmax] + [1.0] * 30)
+    rows.append([1e-40, -1e-38] + [0.0] * 30)
+    check_qdq(torch.tensor(rows, dtype=torch.float32), "crafted")
+
+
+def test_qdq_full_size_8192x8192_one_percent_rows_scaled():
+    x = workloads.qdq_large()
+    check_qdq(x, "qdq 8192x8192")
+
+
+# ------------------------------------------------------------------ MXFP8
+SHAPES = [(1, 1), (1, 32), (2, 33), (33, 2), (3, 17), (65, 65), (128, 128), (127, 129),
+          (300, 257), (256, 1000), (1000, 264), (4097, 40)]
+
+
+def quant_ref(xb: np.ndarray, axis_mask: int):
+    out = {}
+    if axis_mask & 1:
+        out["q_row"], out["s_row"] = oracle.mxfp8_quant_row(xb)
+    if axis_mask & 2:
+        out["q_colT"], out["s_colT"] = oracle.mxfp8_quant_colT(xb)
+    return out
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("axis", [1, 2, 3])
+def test_quantize_bitexact(shape, axis):
+    m = mxq()
+    x = scaled_randn(shape, seed=shape[0] * 7 + shape[1], zero_rows=min(2, shape[0] // 8))
+    got = m.quantize(x.cuda(), axis)
+    torch.cuda.synchronize()
+    ref = quant_ref(bits(x), axis)
+    for k, v in ref.items():
+        assert_bytes_equal(host(got[k]), v, f"{k} {shape}")
+
+
+@pytest.mark.parametrize("C,pad", [(200, 8), (203, 3)])
+def test_quantize_strided_input(C, pad):
+    """x is a column slice of a wider matrix (row stride C+pad)."""
+    m = mxq()
+    big = scaled_randn((150, C + pad), seed=C)
+    x = big.cuda()[:, :C]
+    got = m.quantize(x, 3)
+    torch.cuda.synchronize()
+    ref = quant_ref(bits(big[:, :C].contiguous()), 3)
+    for k, v in ref.items():
+        assert np.array_equal(host(got[k]), v), k
+
+
+def test_quantize_extreme_values():
+    rows = [[0.0] * 64, [-0.0, 0.0] * 32, [2.0 ** -133] + [0.0] * 63,
+            [3.0e38, -3.0e38] + [1.0] * 62, [2.0 ** -120, 2.0 ** -126, 2.0 ** -130] + [0.0] * 61,
+            [464.0, 448.0, 480.0, 1.0, 1.0625, 1.1875, -500.0] + [0.0] * 57]
+    x = torch.tensor(rows, dtype=torch.float32).to(torch.bfloat16)
+    got = mxq().quantize(x.cuda(), 3)
+    torch.cuda.synchronize()
+    for k, v in quant_ref(bits(x), 3).items():
+        assert np.array_equal(host(got[k]), v), k
+
+
+def exhaustive_blocks():
+    """Every (bf16 value, scale byte) pair the quantiser can meet: for each
+    scale byte b a pilot of exponent field b+8 fixes the block scale, and the
+    other 31 slots of the blocks run through every bf16 pattern (both signs)
+    with exponent field <= b+8."""
+    blocks = []
+    for b in range(0, 247):
+        ef = b + 8
+        pilot = (ef << 7) | 0x7F
+        mags = np.arange(0, (ef + 1) << 7, dtype=np.uint32)     # all patterns with Efield <= ef
+        vals = np.concatenate([mags, mags | 0x8000]).astype(np.uint16)
+        n = -(-len(vals) // 31)
+        vals = np.concatenate([vals, np.zeros(n * 31 - len(vals), np.uint16)]).reshape(n, 31)
+        blk = np.concatenate([np.full((n, 1), pilot, np.uint16), vals], axis=1)
+        blocks.append(blk)
+    return np.concatenate(blocks)
+
+
+def test_quantize_every_element_and_scale_pair():
+    xb = exhaustive_blocks()                              # [n][32] bf16 bits, one block per row
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16)
+    m = mxq()
+    got = m.quantize(x.cuda(), 1)
+    torch.cuda.synchronize()
+    q, s = oracle.mxfp8_quant_row(xb)
+    assert np.array_equal(host(got["s_row"]), s)
+    assert np.array_equal(host(got["q_row"]), q)
+    # the same blocks through the column path (blocks running down columns)
+    xt = np.ascontiguousarray(xb[:4096].T)                # [32][4096]
+    got = m.quantize(torch.from_numpy(xt.view(np.int16)).view(torch.bfloat16).cuda(), 2)
+    torch.cuda.synchronize()
+    qt, st = oracle.mxfp8_quant_colT(xt)
+    assert np.array_equal(host(got["q_colT"]), qt) and np.array_equal(host(got["s_colT"]), st)
+
+
+GROUPS = [[70], [0, 1, 31, 32, 33, 0], [0, 0, 5], [64, 0], [17, 40, 1, 0, 96],
+          [0, 0, 0, 200, 0, 0], [129, 1, 255, 0, 2, 64, 33]]
+
+
+@pytest.mark.parametrize("sizes", GROUPS)
+@pytest.mark.parametrize("C", [40, 129])
+@pytest.mark.parametrize("axis", [2, 3])
+def test_grouped_quantize_bitexact(sizes, C, axis):
+    m = mxq()
+    T = sum(sizes)
+    x = scaled_randn((T, C), seed=T + C)
+    ge = np.cumsum(sizes).astype(np.int32)
+    got = m.quantize_grouped(x.cuda(), torch.from_numpy(ge).cuda(), axis)
+    torch.cuda.synchronize()
+    P = oracle.grouped_cols(ge)
+    q, s = oracle.mxfp8_quant_grouped_colT(bits(x), ge, got["ldq"])
+    assert np.array_equal(host(got["q_colT"])[:, :P], q[:, :P])
+    assert np.array_equal(host(got["s_colT"])[:, :P // 32], s[:, :P // 32])
+    if axis & 1:
+        qr, sr = oracle.mxfp8_quant_row(bits(x))
+        assert np.array_equal(host(got["q_row"]), qr) and np.array_equal(host(got["s_row"]), sr)
+
+
+def test_validate_group_end():
+    m = mxq()
+    flag = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    cases = [([0, 3, 3, 10], 10, 0), ([0, 3, 2, 10], 10, 3), ([5, 11], 10, 2), ([-1, 4], 10, 1),
+             ([10] * 32, 10, 0)]
+    for ge, T, want in cases:
+        m.mxq_validate_group_end(torch.tensor(ge, dtype=torch.int32, device="cuda"), T, flag)
+        torch.cuda.synchronize()
+        assert int(flag.item()) == want, (ge, T)
