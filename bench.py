@@ -1,0 +1,332 @@
+"""Benchmark of the MX quantise + block-scaled GEMM hot path on one MI355X.
+
+One step = one pass of the whole path over resident synthetic inputs:
+  * MXFP4 quant-dequant of an 8192x8192 fp32 tensor (1% of rows scaled by 2^U(-20,20));
+  * MXFP8 dense linear M=8192, K=7168, N=18432: dual-axis quantisation of X, W
+    and dY, then the forward, input-gradient and weight-gradient GEMMs;
+  * MoE expert layer, one GPU's 32 experts, 7168 -> 4096, 16384 tokens routed
+    top-8 over Zipf(1.1) weights (131072 rows): forward (X by rows, W[g] on both
+    axes, ragged-M GEMM) and backward (dY by rows and grouped by tokens, X
+    grouped by tokens, ragged-M input gradient, ragged-K weight gradient),
+    dual-axis schedule.
+The forward/backward-split schedule of the MoE layer (W[g] quantised on its
+reduction axis only in the forward, re-quantised along N in the backward) is
+timed beside the step, with the device memory each schedule holds from
+forward to backward.
+
+Prints one JSON line.  `value` = GEMM FLOPs of the step / step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MXFP8 GEMM & grouped-GEMM TFLOP/s (+quantize GB/s), % of MI355X roofline"
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle CPU leg")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle leg")
+    return ap.parse_args()
+
+
+class Timeline:
+    """HIP events around each component on the launch stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.marks = []
+
+    def __call__(self, name):
+        ev = self.torch.cuda.Event(enable_timing=True)
+        ev.record(self.torch.cuda.current_stream())
+        self.marks.append((name, ev))
+
+    def durations(self):
+        out = {}
+        for (name, a), (_, b) in zip(self.marks, self.marks[1:]):
+            if name is not None:
+                out.setdefault(name, []).append(a.elapsed_time(b))
+        return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the MX quantise/GEMM hot path on exactly one MI355X; runs on "
+              "several GPUs are not part of this benchmark. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from moe_grouped_gemm_mxq_amd import mxq, workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if mxq.mxq_device_check(0) != mxq.MXQ_OK:
+        raise RuntimeError(f"device 0 is not usable: {mxq.mxq_last_error()}")
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)
+    f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
+    c32 = lambda v: (v + 31) // 32 * 32
+
+    # ---------------------------------------------------------------- inputs (resident)
+    x4 = workloads.qdq_large().to(dev)
+    y4 = torch.empty_like(x4)
+    M, K, N = 8192, 7168, 18432
+    X, W, dY = workloads.dense_linear(M, K, N, device=dev)
+    Xm, Wm, dYm, ge = workloads.moe_layer(device=dev)
+    ge = ge.to(dev)
+    G, H, F = Wm.shape          # 32 experts, hidden 7168, ffn 4096
+    T = Xm.shape[0]
+    sizes = workloads.moe_group_sizes()
+
+    # ---------------------------------------------------------------- outputs (allocated once)
+    qx = dict(q_row=u8(M, K), s_row=u8(M, K // 32), q_colT=u8(K, M), s_colT=u8(K, M // 32))
+    qw = dict(q_row=u8(K, N), s_row=u8(K, N // 32), q_colT=u8(N, K), s_colT=u8(N, K // 32))
+    qy = dict(q_row=u8(M, N), s_row=u8(M, N // 32), q_colT=u8(N, M), s_colT=u8(N, M // 32))
+    Y, dX, dW = f32(M, N), f32(M, K), f32(K, N)
+    ldq = mxq.mxq_grouped_cols_max(T, G)
+    mx = dict(q_row=u8(T, H), s_row=u8(T, H // 32))
+    mw = dict(q_row=u8(G * H, F), s_row=u8(G * H, F // 32), q_colT=u8(G, F, H), s_colT=u8(G, F, H // 32))
+    mdy = dict(q_row=u8(T, F), s_row=u8(T, F // 32), q_colT=u8(F, ldq), s_colT=u8(F, ldq // 32))
+    mxt = dict(q_colT=u8(H, ldq), s_colT=u8(H, ldq // 32))
+    mY, mdX, mdW = f32(T, F), f32(T, H), f32(G, H, F)
+    R, C = mxq.MXQ_AXIS_ROW, mxq.MXQ_AXIS_COLT
+
+    def quant_w_experts(mask):
+        for g in range(G):
+            mxq.mxq_quantize(Wm[g], mask,
+                             mw["q_row"][g * H:(g + 1) * H] if mask & R else None,
+                             mw["s_row"][g * H:(g + 1) * H] if mask & R else None,
+                             mw["q_colT"][g] if mask & C else None, mw["s_colT"][g] if mask & C else None)
+
+    def moe_fwd(tl, schedule):
+        tl("moe_quant_x_row")
+        mxq.mxq_quantize(Xm, R, mx["q_row"], mx["s_row"])
+        tl("moe_quant_w_dual" if schedule == "dual" else "moe_quant_w_colT")
+        quant_w_experts(R | C if schedule == "dual" else C)
+        tl("moe_gemm_fwd_raggedM")
+        mxq.mxq_grouped_gemm(mxq.MXQ_GG_RAGGED_M, mx["q_row"], mx["s_row"], mw["q_colT"], mw["s_colT"], mY, ge)
+
+    def moe_bwd(tl, schedule):
+        tl("moe_quant_dy_row_grouped")
+        mxq.mxq_quantize_grouped(dYm, ge, ldq, R | C, mdy["q_row"], mdy["s_row"], mdy["q_colT"], mdy["s_colT"])
+        tl("moe_quant_x_grouped")
+        mxq.mxq_quantize_grouped(Xm, ge, ldq, C, None, None, mxt["q_colT"], mxt["s_colT"])
+        if schedule == "fb_split":
+            tl("moe_requant_w_row")
+            quant_w_experts(R)
+        tl("moe_gemm_dgrad_raggedM")
+        mxq.mxq_grouped_gemm(mxq.MXQ_GG_RAGGED_M, mdy["q_row"], mdy["s_row"], mw["q_row"].view(G, H, F),
+                             mw["s_row"].view(G, H, F // 32), mdX, ge)
+        tl("moe_gemm_wgrad_raggedK")
+        mxq.mxq_grouped_gemm(mxq.MXQ_GG_RAGGED_K, mxt["q_colT"], mxt["s_colT"], mdy["q_colT"], mdy["s_colT"], mdW, ge)
+
+    def step(tl):
+        tl("qdq_fp4")
+        mxq.mxq_qdq_fp4(x4, y4)
+        tl("dense_quant_dual")
+        mxq.mxq_quantize(X, R | C, qx["q_row"], qx["s_row"], qx["q_colT"], qx["s_colT"])
+        mxq.mxq_quantize(W, R | C, qw["q_row"], qw["s_row"], qw["q_colT"], qw["s_colT"])
+        mxq.mxq_quantize(dY, R | C, qy["q_row"], qy["s_row"], qy["q_colT"], qy["s_colT"])
+        tl("dense_gemm_fwd")
+        mxq.mxq_gemm(qx["q_row"], qx["s_row"], qw["q_colT"], qw["s_colT"], Y)
+        tl("dense_gemm_dgrad")
+        mxq.mxq_gemm(qy["q_row"], qy["s_row"], qw["q_row"], qw["s_row"], dX)
+        tl("dense_gemm_wgrad")
+        mxq.mxq_gemm(qx["q_colT"], qx["s_colT"], qy["q_colT"], qy["s_colT"], dW)
+        moe_fwd(tl, "dual")
+        moe_bwd(tl, "dual")
+        tl(None)
+
+    # ---------------------------------------------------------------- algorithmic work
+    routed = sum(sizes)
+    flops = {
+        "dense_gemm_fwd": 2.0 * M * N * K, "dense_gemm_dgrad": 2.0 * M * N * K, "dense_gemm_wgrad": 2.0 * M * N * K,
+        "moe_gemm_fwd_raggedM": 2.0 * routed * H * F, "moe_gemm_dgrad_raggedM": 2.0 * routed * H * F,
+        "moe_gemm_wgrad_raggedK": 2.0 * routed * H * F,
+    }
+    qb = lambda r, c, n_axes: r * c * (2 + n_axes * (1 + 1 / 32))     # bf16 read once, codes+scales per axis
+    padded = sum(c32(s) for s in sizes)
+    bytes_ = {
+        "qdq_fp4": 8.0 * x4.numel(),
+        "dense_quant_dual": qb(M, K, 2) + qb(K, N, 2) + qb(M, N, 2),
+        "moe_quant_x_row": qb(T, H, 1),
+        "moe_quant_w_dual": qb(G * H, F, 2),
+        "moe_quant_w_colT": qb(G * H, F, 1),
+        "moe_requant_w_row": qb(G * H, F, 1),
+        "moe_quant_dy_row_grouped": T * F * 2 + T * F * (1 + 1 / 32) + padded * F * (1 + 1 / 32),
+        "moe_quant_x_grouped": T * H * 2 + padded * H * (1 + 1 / 32),
+    }
+    step_flops = sum(flops.values())
+
+    # ---------------------------------------------------------------- warmup + timed steps
+    for _ in range(args.warmup):
+        step(Timeline(torch))
+    torch.cuda.synchronize()
+    tls = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        tl = Timeline(torch)
+        step(tl)
+        tls.append(tl)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    per = {}
+    for tl in tls:
+        for k, v in tl.durations().items():
+            per.setdefault(k, []).extend(v)
+    avg = {k: sum(v) / len(v) for k, v in per.items()}
+    components = {}
+    for k, ms in avg.items():
+        d = {"ms": round(ms, 4)}
+        if k in flops:
+            tf = flops[k] / (ms * 1e-3) / 1e12
+            d.update(tflops=round(tf, 1), frac_fp8_peak=round(tf / PEAK_FP8_TFLOPS, 4))
+        if k in bytes_:
+            gbs = bytes_[k] / (ms * 1e-3) / 1e9
+            d.update(gbs=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
+        components[k] = d
+
+    # dominant kernel: the GEMM launch taking the most time per step
+    dom = max((k for k in avg if k in flops), key=lambda k: avg[k])
+    dom_tf = flops[dom] / (avg[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 1), "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                "algorithmic_flops_per_launch": flops[dom], "avg_launch_ms": round(avg[dom], 4)}
+
+    # ---------------------------------------------------------------- MoE schedules: time and memory
+    schedules = {}
+    for sched in ("dual", "fb_split"):
+        for _ in range(2):
+            tl = Timeline(torch)
+            moe_fwd(tl, sched)
+            moe_bwd(tl, sched)
+            tl(None)
+        torch.cuda.synchronize()
+        fb = []
+        for _ in range(5):
+            tl = Timeline(torch)
+            tl("fwd")
+            moe_fwd(Timeline(torch), sched)
+            tl("bwd")
+            moe_bwd(Timeline(torch), sched)
+            tl(None)
+            fb.append(tl)
+        torch.cuda.synchronize()
+        d = {}
+        for tl in fb:
+            for k, v in tl.durations().items():
+                d.setdefault(k, []).extend(v)
+        held = (mw["q_row"].numel() + mw["s_row"].numel()) if sched == "dual" else 0
+        schedules[sched] = {"fwd_ms": round(sum(d["fwd"]) / len(d["fwd"]), 3),
+                            "bwd_ms": round(sum(d["bwd"]) / len(d["bwd"]), 3),
+                            "quantised_w_held_fwd_to_bwd_bytes": held}
+    # the two schedules must produce the same input gradient bit for bit
+    ref = mdX.clone()
+    moe_fwd(Timeline(torch), "dual")
+    moe_bwd(Timeline(torch), "dual")
+    torch.cuda.synchronize()
+    schedules["bitwise_equal_dgrad"] = bool(torch.equal(ref, mdX))
+
+    # ---------------------------------------------------------------- CPU baseline (oracle)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.cpu_seconds, X, W, dY, Xm, Wm, dYm, ge, sizes)
+
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
+        "data": "synthetic (seeded N(0,1) activations and gradients, N(0,0.02^2) weights, "
+                "Zipf(1.1) top-8 routing; MXFP4 input N(0,1) with 1% rows x 2^U(-20,20))",
+        "config": {
+            "workload": "MX hot path step: MXFP4 QDQ 8192x8192 fp32 + MXFP8 dense linear M8192 K7168 N18432 "
+                        "fwd/dgrad/wgrad with dual-axis quantisation + MoE 32 experts x (7168->4096), "
+                        "131072 routed rows, fwd/bwd, dual-axis schedule",
+            "gemm_tflop_per_step": round(step_flops / 1e12, 3),
+            "parallelism": "single GPU",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "components": components,
+        "moe_schedules": schedules,
+    }
+    print(json.dumps(out))
+
+
+def cpu_baseline(target_s, X, W, dY, Xm, Wm, dYm, ge, sizes):
+    """The oracle (plain C, fp64) on a bounded sample of the same workload: for
+    each of the six GEMMs, quantise the operand rows/columns a block of sampled
+    outputs needs and compute those outputs; TFLOP/s = sampled GEMM FLOPs /
+    oracle time (quantisation included)."""
+    import numpy as np
+    import torch
+    import oracle
+    from moe_grouped_gemm_mxq_amd.workloads import bf16_bits
+
+    rows = lambda t, idx: bf16_bits(t[torch.as_tensor(idx, device=t.device)])
+    cols = lambda t, idx: np.ascontiguousarray(bf16_bits(t[:, torch.as_tensor(idx, device=t.device)].contiguous()).T)
+    ge_np = ge.cpu().numpy()
+    big = int(np.argmax(sizes))
+    start = int(ge_np[big - 1]) if big else 0
+    rng = np.random.default_rng(0)
+
+    def gather(s):
+        """(A-source rows, B-source rows, K) of the sampled block for each GEMM, s x s outputs."""
+        mi = rng.choice(X.shape[0], s, replace=False)
+        ni = rng.choice(W.shape[1], s, replace=False)
+        ki = rng.choice(W.shape[0], s, replace=False)
+        ti = start + rng.choice(sizes[big], s, replace=False)
+        fi = rng.choice(Wm.shape[2], s, replace=False)
+        hi = rng.choice(Wm.shape[1], s, replace=False)
+        return [
+            (lambda: rows(X, mi), lambda: cols(W, ni)),            # dense fwd, K = 7168
+            (lambda: rows(dY, mi), lambda: rows(W, ki)),            # dense dgrad, K = 18432
+            (lambda: cols(X, ki), lambda: cols(dY, ni)),            # dense wgrad, K = 8192
+            (lambda: rows(Xm, ti), lambda: cols(Wm[big], fi)),      # MoE fwd (largest expert), K = 7168
+            (lambda: rows(dYm, ti), lambda: rows(Wm[big], hi)),     # MoE dgrad, K = 4096
+            (lambda: cols(Xm[start:start + sizes[big]], hi),        # MoE wgrad of that expert, K = its tokens
+             lambda: cols(dYm[start:start + sizes[big]], fi)),
+        ]
+
+    def run(s):
+        work = gather(s)
+        srcs = [(fa(), fb()) for fa, fb in work]     # host copies of the bf16 inputs (not timed)
+        t0 = time.perf_counter()
+        fl = 0.0
+        for a_bits, b_bits in srcs:
+            A, sA = oracle.mxfp8_quant_row(a_bits)
+            B, sB = oracle.mxfp8_quant_row(b_bits)
+            oracle.gemm(A, sA, B, sB)
+            fl += 2.0 * A.shape[0] * B.shape[0] * A.shape[1]
+        return time.perf_counter() - t0, fl
+
+    t_probe, f_probe = run(32)
+    s = 32
+    # grow the sample until it takes about target_s of CPU time (cost ~ s^2)
+    s = int(min(2048, max(32, 32 * (target_s / max(t_probe, 1e-3)) ** 0.5)))
+    t, fl = run(s)
+    return {"value": round(fl / t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.lib().oracle_num_threads(),
+            "kind": "oracle",
+            "sample": f"{s}x{s} outputs of each of the six GEMMs (dense fwd/dgrad/wgrad; MoE fwd/dgrad/wgrad of "
+                      f"the largest expert), with the oracle quantising the operand rows they need; "
+                      f"{fl / 1e9:.1f} GFLOP in {t:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()
