@@ -39,7 +39,39 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle CPU leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle leg")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (reference for HBM counter scaling)")
     return ap.parse_args()
+
+
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+GEMM_SRC = os.path.join(ROOT, "moe_grouped_gemm_mxq_amd", "csrc", "gemm_mxfp8.hip")
+
+
+def source_digest(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_label):
+    """HBM bytes per launch of `kernel_label` from the committed counter summary,
+    or None when there is none or the GEMM source changed since it was taken."""
+    path = os.path.join(PROFILE_DIR, f"{kernel_label}__hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel source sha256[:16]") != source_digest(GEMM_SRC):
+        return None
+    try:
+        return int(float(vals["HBM bytes per launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 class Timeline:
@@ -74,6 +106,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": src.numel() * 4,
+                          "bytes_written_per_launch": dst.numel() * 4, "launches": 5}))
+        return
     if mxq.mxq_device_check(0) != mxq.MXQ_OK:
         raise RuntimeError(f"device 0 is not usable: {mxq.mxq_last_error()}")
     u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)
@@ -205,7 +246,7 @@ def main():
     dom = max((k for k in avg if k in flops), key=lambda k: avg[k])
     dom_tf = flops[dom] / (avg[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 1), "peak": PEAK_FP8_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_FP8_TFLOPS, 4), "traffic": measured_traffic(dom),
                 "algorithmic_flops_per_launch": flops[dom], "avg_launch_ms": round(avg[dom], 4)}
 
     # ---------------------------------------------------------------- MoE schedules: time and memory
@@ -316,11 +357,12 @@ def cpu_baseline(target_s, X, W, dY, Xm, Wm, dYm, ge, sizes):
             fl += 2.0 * A.shape[0] * B.shape[0] * A.shape[1]
         return time.perf_counter() - t0, fl
 
-    t_probe, f_probe = run(32)
-    s = 32
-    # grow the sample until it takes about target_s of CPU time (cost ~ s^2)
-    s = int(min(2048, max(32, 32 * (target_s / max(t_probe, 1e-3)) ** 0.5)))
+    # grow the sample (cost ~ s^2) until one run takes about target_s of CPU time
+    s = 64
     t, fl = run(s)
+    while t < 0.5 * target_s and s < 4096:
+        s = int(min(4096, s * max(1.4, min(4.0, (target_s / max(t, 1e-3)) ** 0.5))))
+        t, fl = run(s)
     return {"value": round(fl / t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.lib().oracle_num_threads(),
             "kind": "oracle",
             "sample": f"{s}x{s} outputs of each of the six GEMMs (dense fwd/dgrad/wgrad; MoE fwd/dgrad/wgrad of "

@@ -263,13 +263,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
         order[rank] = g;
       }
       __syncthreads();
-      // dispatch order (no XCD remap): consecutive workgroups spread over all
-      // XCDs, so every XCD gets a share of the large groups
+      // groups are taken largest first; inside a group's run of workgroups the
+      // XCD remap gives every XCD an equal, contiguous share of that group's
+      // tiles (balanced across XCDs, and each XCD's concurrent tiles share
+      // operand panels in its L2)
       const int per_g = tiles_m * tiles_n;
       const int gi = bid / per_g;
       const int g = order[gi];
       int mt, nt;
-      raster(bid - gi * per_g, tiles_m, tiles_n, mt, nt);
+      raster(xcd_remap(bid - gi * per_g, per_g), tiles_m, tiles_n, mt, nt);
       m0 = (int64_t)mt * BM;
       n0 = (int64_t)nt * BN;
       rows_a = (int)min<int64_t>(BM, M - m0);
