@@ -133,15 +133,17 @@ def main():
     sizes = workloads.moe_group_sizes()
 
     # ---------------------------------------------------------------- outputs (allocated once)
-    qx = dict(q_row=u8(M, K), s_row=u8(M, K // 32), q_colT=u8(K, M), s_colT=u8(K, M // 32))
-    qw = dict(q_row=u8(K, N), s_row=u8(K, N // 32), q_colT=u8(N, K), s_colT=u8(N, K // 32))
-    qy = dict(q_row=u8(M, N), s_row=u8(M, N // 32), q_colT=u8(N, M), s_colT=u8(N, M // 32))
+    sc = lambda rows, nblk: u8(*mxq.scale_shape(rows, nblk))   # interleaved scale array
+    qx = dict(q_row=u8(M, K), s_row=sc(M, K // 32), q_colT=u8(K, M), s_colT=sc(K, M // 32))
+    qw = dict(q_row=u8(K, N), s_row=sc(K, N // 32), q_colT=u8(N, K), s_colT=sc(N, K // 32))
+    qy = dict(q_row=u8(M, N), s_row=sc(M, N // 32), q_colT=u8(N, M), s_colT=sc(N, M // 32))
     Y, dX, dW = f32(M, N), f32(M, K), f32(K, N)
     ldq = mxq.mxq_grouped_cols_max(T, G)
-    mx = dict(q_row=u8(T, H), s_row=u8(T, H // 32))
-    mw = dict(q_row=u8(G * H, F), s_row=u8(G * H, F // 32), q_colT=u8(G, F, H), s_colT=u8(G, F, H // 32))
-    mdy = dict(q_row=u8(T, F), s_row=u8(T, F // 32), q_colT=u8(F, ldq), s_colT=u8(F, ldq // 32))
-    mxt = dict(q_colT=u8(H, ldq), s_colT=u8(H, ldq // 32))
+    mx = dict(q_row=u8(T, H), s_row=sc(T, H // 32))
+    mw = dict(q_row=u8(G * H, F), s_row=sc(G * H, F // 32), q_colT=u8(G, F, H),
+              s_colT=u8(G, *mxq.scale_shape(F, H // 32)))
+    mdy = dict(q_row=u8(T, F), s_row=sc(T, F // 32), q_colT=u8(F, ldq), s_colT=sc(F, ldq // 32))
+    mxt = dict(q_colT=u8(H, ldq), s_colT=sc(H, ldq // 32))
     mY, mdX, mdW = f32(T, F), f32(T, H), f32(G, H, F)
     R, C = mxq.MXQ_AXIS_ROW, mxq.MXQ_AXIS_COLT
 
@@ -149,7 +151,7 @@ def main():
         for g in range(G):
             mxq.mxq_quantize(Wm[g], mask,
                              mw["q_row"][g * H:(g + 1) * H] if mask & R else None,
-                             mw["s_row"][g * H:(g + 1) * H] if mask & R else None,
+                             mw["s_row"][g * H // 32:(g + 1) * H // 32] if mask & R else None,
                              mw["q_colT"][g] if mask & C else None, mw["s_colT"][g] if mask & C else None)
 
     def moe_fwd(tl, schedule):
@@ -170,7 +172,7 @@ def main():
             quant_w_experts(R)
         tl("moe_gemm_dgrad_raggedM")
         mxq.mxq_grouped_gemm(mxq.MXQ_GG_RAGGED_M, mdy["q_row"], mdy["s_row"], mw["q_row"].view(G, H, F),
-                             mw["s_row"].view(G, H, F // 32), mdX, ge)
+                             mw["s_row"].view(G, H // 32, F // 32, 32), mdX, ge)
         tl("moe_gemm_wgrad_raggedK")
         mxq.mxq_grouped_gemm(mxq.MXQ_GG_RAGGED_K, mxt["q_colT"], mxt["s_colT"], mdy["q_colT"], mdy["s_colT"], mdW, ge)
 

@@ -29,8 +29,14 @@
  *    Outputs must not alias inputs.  Tensor pointers must be 16-byte aligned.
  *  - A quantised MXFP8 operand is `codes[rows][Kp]` (one E4M3 byte per
  *    element, the reduction axis K contiguous, Kp = ceil32(K), padding codes
- *    0x00) plus `scales[rows][Kp/32]` (one E8M0 byte per block of 32,
- *    value 2^(byte-127)).
+ *    0x00) plus its scales: one E8M0 byte (value 2^(byte-127)) per row and
+ *    block of 32, stored 32-row interleaved -- the scale of row r, block b is
+ *    byte ((r/32) * (Kp/32) + b) * 32 + r%32 of an array of
+ *    ceil32(rows) * (Kp/32) bytes ("scales[ceil32(rows)/32][Kp/32][32]").
+ *    The scales of 32 consecutive rows for one block are adjacent, which is
+ *    how a GEMM tile fetches them.  Bytes of rows past `rows` are not
+ *    written.  A row range whose first row is a multiple of 32 is itself a
+ *    valid operand (its scale array starts at byte first_row * (Kp/32)).
  *  - "row" copy: blocks along the contiguous dim of the input.  "colT" copy:
  *    the quantised transpose, blocks running down the columns of the input.
  *  - Errors: every entry point validates its host-visible arguments first
@@ -53,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 1
+#define MXQ_ABI_VERSION 2
 #define MXQ_BLOCK 32          /* elements per MX block; fixed */
 #define MXQ_MAX_GROUPS 1024   /* largest G the grouped entry points accept */
 
@@ -96,8 +102,10 @@ int64_t mxq_grouped_cols_max(int64_t T, int32_t G);
  * MXFP8 quantisation of a bf16 matrix x [R][ldx] (R x C used), the per-block
  * quantisation of activations and weights of the torchtitan-npu guide
  * ("线性层低精度"), with the axis choice of MindSpeed PR 3852 ("主要改动").
- *   axis_mask & MXQ_AXIS_ROW : q_row [R][Cp], s_row [R][Cp/32], Cp = ceil32(C)
- *   axis_mask & MXQ_AXIS_COLT: q_colT [C][Rp], s_colT [C][Rp/32], Rp = ceil32(R)
+ *   axis_mask & MXQ_AXIS_ROW : q_row [R][Cp], s_row (R rows, Cp/32 blocks,
+ *                              interleaved), Cp = ceil32(C)
+ *   axis_mask & MXQ_AXIS_COLT: q_colT [C][Rp], s_colT (C rows, Rp/32 blocks,
+ *                              interleaved), Rp = ceil32(R)
  * Pointers for an axis not requested may be NULL.  Both axes together read
  * x once (dual-axis quantisation).  R, C >= 1; ldx >= C.
  */
@@ -110,13 +118,14 @@ mxq_status mxq_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, in
  * (torchtitan-npu guide, "MoE 专家层低精度").  x bf16 [T][ldx] (T x C used);
  * group g owns rows [end_{g-1}, end_g) with end_g = group_end[g] (device
  * int32 [G], cumulative, end_{-1} = 0).
- *   MXQ_AXIS_COLT: q_colT [C][ldq], s_colT [C][ldq/32].  Blocks restart at
+ *   MXQ_AXIS_COLT: q_colT [C][ldq], s_colT (C rows, ldq/32 blocks,
+ *     interleaved).  Blocks restart at
  *     each group start; group g occupies columns [P_g, P_g + ceil32(m_g)),
  *     P_g = sum_{j<g} ceil32(m_j), its tail zero-padded.  Columns at and past
  *     P_G are not written.  ldq % 32 == 0; ldq >= sum_g ceil32(m_g) is a
  *     precondition (mxq_grouped_cols_max(T, G) always suffices); blocks that
  *     would fall past ldq are dropped.
- *   MXQ_AXIS_ROW: q_row [T][Cp], s_row [T][Cp/32], identical to
+ *   MXQ_AXIS_ROW: q_row [T][Cp], s_row (T rows, interleaved), identical to
  *     mxq_quantize's row copy; with COLT the input is read once.
  * 1 <= G <= MXQ_MAX_GROUPS; T, C >= 1.
  */
@@ -136,8 +145,8 @@ mxq_status mxq_quantize_grouped(const uint16_t* x, int64_t T, int64_t C, int64_t
  * * scale (the sign of x is kept also when the code is 0).
  * Optional outputs (NULL to skip): codes [rows][Lp/2] E2M1 nibbles, element
  * 2j in the low nibble of byte j, nibble = sign<<3 | codebook index (the OCP
- * E2M1 bit pattern); scales [rows][Lp/32] E8M0 bytes.  NaN/Inf inputs are
- * outside the contract.  rows, L >= 1.
+ * E2M1 bit pattern); scales [rows][Lp/32] E8M0 bytes, row-major (these are
+ * not GEMM operands).  NaN/Inf inputs are outside the contract.  rows, L >= 1.
  */
 mxq_status mxq_qdq_fp4(const float* x, float* y, int64_t rows, int64_t L,
                        uint8_t* codes, uint8_t* scales, hipStream_t st);
@@ -145,8 +154,8 @@ mxq_status mxq_qdq_fp4(const float* x, float* y, int64_t rows, int64_t L,
 /*
  * Block-scaled GEMM C[m][n] = sum_k deq(A)[m][k] * deq(B)[n][k] (the FP8
  * linear GEMMs of the torchtitan-npu guide, "线性层低精度"), fp32
- * accumulation and fp32 output.  A codes [M][K] + scales [M][K/32];
- * B codes [N][K] + scales [N][K/32]; C fp32 [M][ldc].
+ * accumulation and fp32 output.  A codes [M][K] + scales (M rows);
+ * B codes [N][K] + scales (N rows), scales interleaved; C fp32 [M][ldc].
  * Forward Y = X W: A = row copy of X, B = colT copy of W [K][N].
  * Input gradient dX = dY W^T: A = row copy of dY, B = row copy of W.
  * Weight gradient dW = X^T dY: A = colT copy of X, B = colT copy of dY.
@@ -159,7 +168,8 @@ mxq_status mxq_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const
 /*
  * Grouped block-scaled GEMM over ragged expert groups (torchtitan-npu guide,
  * "MoE 专家层低精度"); group_end device int32 [G] as for mxq_quantize_grouped.
- *   MXQ_GG_RAGGED_M: A [M][K] (+[M][K/32]); B [G][N][K] (+[G][N][K/32]);
+ *   MXQ_GG_RAGGED_M: A [M][K] (+ scales of M rows); B [G][N][K] with G
+ *     scale arrays of N rows each, expert g's at byte g * ceil32(N) * (K/32);
  *     C fp32 [M][N].  Rows of group g use expert B[g]; rows at or past
  *     group_end[G-1] are not written.  K >= 32, K % 32 == 0.
  *     Expert forward: A = row copy of X, B[g] = colT copy of W[g] [K][N].

@@ -11,16 +11,26 @@
 //               (expert weight gradient over each group's padded tokens).
 //
 // Tiling: 256 x 256 output tile per workgroup of 4 waves (2 x 2), each wave a
-// 128 x 128 sub-tile of 8 x 8 MFMA blocks of 16 x 16; K advances 128 codes per
-// step.  Operand tiles go from global memory straight into LDS
-// (global_load_lds_dwordx4, no register staging), double-buffered: the loads
-// of step k+1 are in flight while step k is multiplied.
+// 128 x 128 sub-tile of 4 x 4 MFMA blocks of 32 x 32; K advances 64 codes per
+// step (one v_mfma_scale_f32_32x32x64_f8f6f4 per block and step).
 //
-// Operand layout of v_mfma_scale_f32_16x16x128_f8f6f4 for FP8 (found by
-// probing): lane l holds row l%16; its bytes 0-15 are K = 16g..16g+15 and
-// bytes 16-31 are K = 64+16g..64+16g+15 with g = l/16; its scale byte (chosen
-// by op_sel) scales row l%16 over K-block g (K = 32g..32g+31).  Accumulator
-// element i of lane l is C[4*(l/16) + i][l%16].
+// Pipeline: codes (global_load_lds_dwordx4) and scale bytes
+// (global_load_lds_ubyte) go from global memory straight into LDS, into a
+// ring of four stages; step k's loads are issued four steps ahead, into the
+// stage that step k-4 used.  Each wave keeps two register sets of MFMA
+// fragments: while the MFMAs of step k run on one, the LDS reads of step k+1
+// fill the other, so the matrix cores never wait on LDS.  One s_barrier per
+// step (raw, with explicit vmcnt / lgkmcnt waits: a full __syncthreads would
+// drain the loads in flight) publishes stage k+1 and retires stage k.  The four
+// stages are separate LDS arrays and the loop is unrolled by four, so the
+// compiler can tell the stage being read from the stages being filled and
+// never waits on the latter.
+//
+// Operand layout of v_mfma_scale_f32_32x32x64_f8f6f4 for FP8 (found by
+// probing): lane l holds row l%32; its bytes 0-15 are K = 16g..16g+15 and
+// bytes 16-31 are K = 32+16g..32+16g+15 with g = l/32; its scale byte (chosen
+// by op_sel) scales row l%32 over K-block g.  Accumulator element e of lane l
+// is C[8*(e/4) + 4*(l/32) + e%4][l%32].
 #include "mxq_device.h"
 #include "mxq_groups.h"
 #include "mxq_internal.h"
@@ -30,160 +40,144 @@ namespace mxq {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr int kThreads = 256;
-constexpr int BM = 256, BN = 256, BK = 128;  // BK in codes (bytes) per step
+constexpr int BM = 256, BN = 256, BK = 64;   // BK in codes (bytes) per step
 constexpr int WM = 128, WN = 128;             // wave tile
-constexpr int TM = WM / 16, TN = WN / 16;     // MFMA blocks per wave
-constexpr int kTileBytes = BM * BK;           // one operand tile per stage (32 KB)
-constexpr int kScaleBytes = 4 * BM;           // scale bytes of one operand tile per stage
-constexpr int kStageBytes = 2 * kTileBytes + 2 * kScaleBytes;
+constexpr int TM = WM / 32, TN = WN / 32;     // MFMA blocks per wave
+constexpr int kTileBytes = BM * BK;           // codes of one operand tile per stage (16 KB)
+constexpr int kScaleRegion = 4 * 2 * BM;      // one dword per (tile row, K-block) of one operand
+constexpr int kStageBytes = 2 * kTileBytes + 2 * kScaleRegion;  // A, B codes, A, B scales (36 KB)
+constexpr int kVmemPerStep = 12;              // per wave and step: 4 + 4 code loads, 2 + 2 scale loads
 constexpr int kXcds = 8;                      // XCDs per MI355X; workgroups are dealt round robin
 constexpr int kGroupM = 8;                    // m-tiles per raster group
 
 enum Mode { kDense = 0, kRaggedM = 1, kRaggedK = 2 };
 
-// op_sel must be an immediate: dispatch the 16 combinations (folded away once
-// the calling loops are unrolled).
-template <int OA, int OB>
-__device__ __forceinline__ v4f mfma_os(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, OA, sa, OB, sb);
-}
-__device__ __forceinline__ v4f mfma_scaled(int oa, int ob, const v8i& a, const v8i& b, const v4f& c,
-                                           int sa, int sb) {
-  switch (oa * 4 + ob) {
-    case 0: return mfma_os<0, 0>(a, b, c, sa, sb);
-    case 1: return mfma_os<0, 1>(a, b, c, sa, sb);
-    case 2: return mfma_os<0, 2>(a, b, c, sa, sb);
-    case 3: return mfma_os<0, 3>(a, b, c, sa, sb);
-    case 4: return mfma_os<1, 0>(a, b, c, sa, sb);
-    case 5: return mfma_os<1, 1>(a, b, c, sa, sb);
-    case 6: return mfma_os<1, 2>(a, b, c, sa, sb);
-    case 7: return mfma_os<1, 3>(a, b, c, sa, sb);
-    case 8: return mfma_os<2, 0>(a, b, c, sa, sb);
-    case 9: return mfma_os<2, 1>(a, b, c, sa, sb);
-    case 10: return mfma_os<2, 2>(a, b, c, sa, sb);
-    case 11: return mfma_os<2, 3>(a, b, c, sa, sb);
-    case 12: return mfma_os<3, 0>(a, b, c, sa, sb);
-    case 13: return mfma_os<3, 1>(a, b, c, sa, sb);
-    case 14: return mfma_os<3, 2>(a, b, c, sa, sb);
-    default: return mfma_os<3, 3>(a, b, c, sa, sb);
-  }
+__device__ __forceinline__ v16f mfma_scaled(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
-// LDS position of 16-byte chunk c (0..7) of tile row r: XOR swizzle so that the
-// 16 rows one MFMA fragment read touches fall in distinct bank groups.
-__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ ((r >> 1) & 7)) << 4); }
+// LDS position of 16-byte chunk c (0..3) of tile row r (64 bytes): XOR swizzle
+// so that the 16 rows a fragment read touches at once fall in distinct banks.
+__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ ((r >> 2) & 3)) << 4); }
 
-// LDS position of the scale byte of tile row r, K-block g: each lane later
-// reads the 8 bytes of its 8 MFMA row blocks (rows wave*128 + i*16 + l%16,
-// i = 0..7) with one 64-bit load; byte i%4 of dword i/4 is op_sel'ed.
-__device__ __forceinline__ int sidx(int r, int g) {
-  return ((g * 2 + (r >> 7)) * 16 + (r & 15)) * 8 + ((r & 127) >> 4);
-}
-
-// One operand of one workgroup tile: tile rows [0, rows_valid) of a matrix
-// whose row r starts at base + r*ld (codes) and sbase + r*(ld/32) (scales).
-// Rows at or past rows_valid are loaded from row rows_valid-1 (their results
-// are never stored).
+// One operand of one workgroup tile: tile rows [0, rows_valid), which are rows
+// row0 .. row0 + rows_valid - 1 of a matrix with codes at base + (r - row0)*ld
+// and scales at sbase + scale_offset(r, block, ld/32) (the 32-row interleaved
+// layout the quantisers write).  Rows at or past rows_valid are read from row
+// rows_valid-1 (their results are never stored).
 struct Operand {
-  const uint8_t* base;
-  const uint8_t* sbase;
+  const uint8_t* base;   // codes of tile row 0
+  const uint8_t* sbase;  // scale array of the whole matrix
+  int64_t row0;
   int64_t ld;
   int rows_valid;
 };
 
-// Direct loads of one operand tile: wave w issues 8 dwordx4 loads; load j
-// fills LDS bytes [(8w + j) * 1024, +1024), i.e. tile rows 8(8w+j) .. +8, lane l
-// writing 16-byte slot l%8 of row 8(8w+j) + l/8, which holds global chunk
-// slot ^ swizzle(row).  swizzle(row) = (row >> 1) & 7 = (4*(j&1) + l/16) & 7, so
-// the chunk a lane moves depends only on the parity of j.
-__device__ __forceinline__ int load_chunk(int lane, int j) { return (lane & 7) ^ ((4 * (j & 1) + (lane >> 4)) & 7); }
+// Direct loads of one operand's codes (16 KB) for the step at k: wave w issues
+// 4 dwordx4 loads; load j fills LDS bytes [(4w + j) * 1024, +1024) = tile rows
+// 16(4w+j) .. +16, lane l writing 16-byte slot l%4 of row 16(4w+j) + l/4, which
+// holds global chunk slot ^ swizzle(row) = (l%4) ^ ((l/16)%4).  Chunks past
+// the end of K (the tail step) are fetched from the last valid chunk (always
+// in bounds) and zeroed by zero_codes() once they have landed.
+__device__ __forceinline__ int dma_chunk(int lane) { return (lane & 3) ^ ((lane >> 4) & 3); }
 
-// Issue the 8 direct loads of one operand tile for the K step at k.  In the
-// tail step chunks past the last valid one (last_chunk) are fetched from the
-// last valid chunk instead (always in bounds) and zeroed by zero_tail() once
-// they have landed.  Addresses are formed on the fly (no held offsets).
-__device__ __forceinline__ void issue_loads(const Operand& op, uint8_t* lds_tile, int wave, int lane,
-                                            int64_t k, int last_chunk) {
-  int r0 = wave * 64 + (lane >> 3);
-  // opaque to the optimiser: keeps the 16 load addresses from being hoisted out
-  // of the K loop (holding them would cost 32+ registers and spill)
-  asm volatile("" : "+v"(r0));
+__device__ __forceinline__ void issue_codes(const Operand& op, uint8_t* tile, int wave, int lane, int64_t k,
+                                            int valid_chunks) {
+  int l = lane;
+  asm volatile("" : "+v"(l));  // keep the addresses from being hoisted out of the K loop
+  const int c = dma_chunk(l);
+  const int cc = c < valid_chunks ? c : valid_chunks - 1;
 #pragma unroll
-  for (int j = 0; j < 8; j++) {
-    const int c = load_chunk(lane, j);
-    const int cc = c <= last_chunk ? c : last_chunk;
-    const int r = min(r0 + 8 * j, op.rows_valid - 1);
+  for (int j = 0; j < 4; j++) {
+    const int r = min((wave * 4 + j) * 16 + (l >> 2), op.rows_valid - 1);
     __builtin_amdgcn_global_load_lds(op.base + (int64_t)r * op.ld + k + cc * 16,
-                                     (lds_ptr)(lds_tile + (wave * 8 + j) * 1024), 16, 0, 0);
+                                     (lds_ptr)(tile + (wave * 4 + j) * 1024), 16, 0, 0);
   }
 }
 
-// After the tail step's loads have landed: zero the chunks past the end of K.
-__device__ __forceinline__ void zero_tail(uint8_t* lds_tile, int wave, int lane, int last_chunk) {
+// Zero the code chunks at or past valid_chunks (0 zeroes the whole step) in
+// the bytes this wave's own loads wrote; called after those loads landed.
+__device__ __forceinline__ void zero_codes(uint8_t* tile, int wave, int lane, int valid_chunks) {
+  if (dma_chunk(lane) >= valid_chunks)
 #pragma unroll
-  for (int j = 0; j < 8; j++)
-    if (load_chunk(lane, j) > last_chunk)
-      *reinterpret_cast<uint4*>(lds_tile + (wave * 8 + j) * 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
+    for (int j = 0; j < 4; j++)
+      *reinterpret_cast<uint4*>(tile + (wave * 4 + j) * 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// Scale bytes: thread t needs the 4 bytes of tile row t for K-blocks
-// k/32 .. k/32+3 (row length ld/32 bytes, so rows need not be dword aligned).
-// Two aligned dword loads cover them: the dwords holding the first byte and
-// the last valid byte (both inside the allocation).  The raw dwords are
-// combined only after the MFMAs (combine_scales), so the loads are waited for
-// once per step, not one by one.
-struct ScaleRaw {
-  uint32_t lo, hi;
-  int shift;  // byte offset of the first byte within `lo`
+// Scale slot d (0..511) of one operand and step, one dword each (the scale in
+// its low byte): d = ((h*2 + g)*32 + r)*4 + i holds the scale of tile row
+// h*128 + i*32 + r over K-block g of the step.  A lane of wave half h reading
+// the 16 bytes at slot ((h*2 + l/32)*32 + l%32)*4 gets its four MFMA row
+// blocks' scales.  Wave w fills slots [128w, 128w+128) with two ubyte loads;
+// in the interleaved scale layout the 64 lanes of one load read 4 runs of 16
+// consecutive bytes.  A K-block past the end of K re-reads block 0 (its codes
+// are zeroed).
+__device__ __forceinline__ void issue_scales(const Operand& op, uint8_t* region, int wave, int lane, int64_t k,
+                                             int valid_blocks) {
+  int l = lane;
+  asm volatile("" : "+v"(l));
+  const int64_t nblk = op.ld / 32;
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const int d = (wave * 2 + j) * 64 + l;
+    const int i = d & 3, r = (d >> 2) & 31, g = (d >> 7) & 1, h = d >> 8;
+    const int row = min(h * 128 + i * 32 + r, op.rows_valid - 1);
+    const int gg = min(g, valid_blocks - 1);
+    __builtin_amdgcn_global_load_lds(op.sbase + scale_offset(op.row0 + row, k / 32 + gg, nblk),
+                                     (lds_ptr)(region + (wave * 2 + j) * 256), 1, 0, 0);
+  }
+}
+
+// MFMA operands of one step for one wave: 4 row blocks of A, 4 of B (32 bytes
+// per lane each), and the lane's 4 + 4 block scales.
+struct Frags {
+  v8i a[TM], b[TN];
+  uint4 sa, sb;
 };
 
-__device__ __forceinline__ ScaleRaw load_scales(const Operand& op, int64_t k, int last_block) {
-  int t = threadIdx.x;
-  asm volatile("" : "+v"(t));
-  const int r = t < op.rows_valid ? t : op.rows_valid - 1;
-  const uint8_t* p = op.sbase + (int64_t)r * (op.ld / 32) + k / 32;
-  const uintptr_t a0 = (uintptr_t)p, a1 = (uintptr_t)(p + last_block);
-  ScaleRaw s;
-  s.lo = *reinterpret_cast<const uint32_t*>(a0 & ~(uintptr_t)3);
-  s.hi = *reinterpret_cast<const uint32_t*>(a1 & ~(uintptr_t)3);
-  s.shift = (int)(a0 & 3);
-  return s;
-}
-
-// the 4 scale bytes in K order; blocks past last_block become 127 (their codes
-// are zero, any finite scale will do)
-__device__ __forceinline__ uint32_t combine_scales(const ScaleRaw& s, int last_block) {
-  // bytes lo[shift..3] followed by hi[0..]: when the 4 bytes sit in one dword, hi == lo
-  // and the shift is 0, so the funnel shift returns lo itself
-  uint32_t v = __builtin_amdgcn_alignbyte(s.hi, s.lo, (uint32_t)s.shift);
-  if (last_block < 3) {
-    const uint32_t keep = 0xFFFFFFFFu >> (8 * (3 - last_block));
-    v = (v & keep) | (0x7F7F7F7Fu & ~keep);
-  }
-  return v;
-}
-
-__device__ __forceinline__ void store_scales(uint8_t* lds_scales, uint32_t sc) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int g = 0; g < 4; g++) lds_scales[sidx(t, g)] = (uint8_t)(sc >> (8 * g));
-}
-
-// fragment of the MFMA row block starting at tile row r0 for this lane
-__device__ __forceinline__ v8i load_frag(const uint8_t* lds_codes, int r0, int lane) {
-  const int r = r0 + (lane & 15);
-  const int g = lane >> 4;
-  const uint4 lo = *reinterpret_cast<const uint4*>(lds_codes + swz(r, g));
-  const uint4 hi = *reinterpret_cast<const uint4*>(lds_codes + swz(r, 4 + g));
+__device__ __forceinline__ v8i load_frag(const uint8_t* codes, int r0, int lane) {
+  const int r = r0 + (lane & 31);
+  const int g = lane >> 5;
+  const uint4 lo = *reinterpret_cast<const uint4*>(codes + swz(r, g));
+  const uint4 hi = *reinterpret_cast<const uint4*>(codes + swz(r, 2 + g));
   v8i f;
   f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
   f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
   return f;
 }
+
+__device__ __forceinline__ void read_frags(const uint8_t* st, int wm, int wn, int lane, Frags& f) {
+  const int so = (((lane >> 5) * 32 + (lane & 31)) * 4) * 4;
+  f.sa = *reinterpret_cast<const uint4*>(st + 2 * kTileBytes + wm * 1024 + so);
+  f.sb = *reinterpret_cast<const uint4*>(st + 2 * kTileBytes + kScaleRegion + wn * 1024 + so);
+#pragma unroll
+  for (int i = 0; i < TM; i++) f.a[i] = load_frag(st, wm * WM + i * 32, lane);
+#pragma unroll
+  for (int j = 0; j < TN; j++) f.b[j] = load_frag(st + kTileBytes, wn * WN + j * 32, lane);
+}
+
+__device__ __forceinline__ int u4_get(const uint4& v, int i) {
+  return (int)(i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w);
+}
+
+__device__ __forceinline__ void mfma_step(v16f (&acc)[TM][TN], const Frags& f) {
+#pragma unroll
+  for (int i = 0; i < TM; i++)
+#pragma unroll
+    for (int j = 0; j < TN; j++) acc[i][j] = mfma_scaled(f.a[i], f.b[j], acc[i][j], u4_get(f.sa, i), u4_get(f.sb, j));
+}
+
+// s_waitcnt with vmcnt(n) only (expcnt / lgkmcnt left at their maximum), gfx9 encoding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (0x7 << 4)); }
 
 // Logical tile order: workgroups are dealt to the XCDs round robin, so remap
 // blockIdx so that each XCD walks a contiguous run of the logical order (tiles
@@ -207,12 +201,24 @@ __device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int& mt,
   nt = r / gm;
 }
 
+// group bookkeeping of the grouped modes, placed in the last stage (used
+// only before that stage's first load is issued)
+struct GroupScratch {
+  GroupTable gt;
+  int32_t scan_tmp[kThreads];
+  int32_t order[kMaxGroups];
+};
+static_assert(sizeof(GroupScratch) <= kStageBytes, "group scratch must fit in one stage");
+
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ sB, float* __restrict__ C, int64_t M, int64_t N, int64_t K,
     int64_t ldc, const int32_t* __restrict__ group_end, int32_t G, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage3[kStageBytes];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -232,8 +238,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
     n0 = (int64_t)nt * BN;
     rows_a = (int)min<int64_t>(BM, M - m0);
   } else {
-    __shared__ GroupTable gt;
-    __shared__ int32_t scan_tmp[kThreads];
+    GroupScratch& gs = *reinterpret_cast<GroupScratch*>(stage3);
+    GroupTable& gt = gs.gt;
+    int32_t* const scan_tmp = gs.scan_tmp;
     if constexpr (MODE == kRaggedM) {
       build_group_table<kThreads>(group_end, G, M, BM, gt, scan_tmp);
       // the grid covers an upper bound of m-tiles; the real ones are bstart[G]
@@ -248,11 +255,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
       n0 = (int64_t)nt * BN;
       rows_a = min(BM, gt.size[g] - local * BM);
       b_base = B + (int64_t)g * N * K;
-      sb_base = sB + (int64_t)g * N * (K / 32);
+      sb_base = sB + (int64_t)g * ((N + 31) / 32 * 32) * (K / 32);  // expert scale arrays hold ceil32(N) rows
     } else {
       build_group_table<kThreads>(group_end, G, (int64_t)1 << 40, 32, gt, scan_tmp);
       // largest groups first (their tiles carry the longest K loops)
-      __shared__ int32_t order[kMaxGroups];
+      int32_t* const order = gs.order;
       for (int g = t; g < G; g += kThreads) {
         const int32_t sz = gt.size[g];
         int rank = 0;
@@ -282,107 +289,101 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
     }
   }
   const int rows_b = (int)min<int64_t>(BN, N - n0);
+  if constexpr (MODE != kDense) __syncthreads();  // group scratch read; stage 3 may now be loaded
 
-  const Operand opa{A + m0 * lda, sA + m0 * (lda / 32), lda, rows_a};
-  const Operand opb{b_base + n0 * lda, sb_base + n0 * (lda / 32), lda, rows_b};
+  const Operand opa{A + m0 * lda, sA, m0, lda, rows_a};
+  const Operand opb{b_base + n0 * lda, sb_base, n0, lda, rows_b};
 
-  v4f acc[TM][TN];
+  v16f acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; i++)
 #pragma unroll
-    for (int j = 0; j < TN; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TN; j++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) acc[i][j][e] = 0.f;
 
   const int nk = (int)((k_end - k_begin + BK - 1) / BK);
-  // chunks / blocks of the last step that lie before k_end (7 / 3 when K steps evenly)
-  const int tail_chunks = (int)((k_end - k_begin) - (int64_t)(nk - 1) * BK) / 16;  // 2..8
-  const int tail_blocks = tail_chunks / 2;                                            // 1..4
+  const int last = nk - 1;
+  const int tail_chunks = nk > 0 ? (int)((k_end - k_begin) - (int64_t)last * BK) / 16 : 4;  // 2 or 4
+  uint8_t* const stages[4] = {stage0, stage1, stage2, stage3};
 
-  // Per step: (1) scale bytes of step s+1 to registers, (2) all fragments and
-  // scales of step s from LDS to registers, (3) direct loads of step s+1 into
-  // the other stage, (4) the 64 MFMAs.  Issuing the direct loads only after the
-  // LDS reads keeps the compiler from waiting on them before those reads, so
-  // they stream in while the MFMAs run.
-  auto last_block = [&](int s) { return s == nk - 1 ? tail_blocks - 1 : 3; };
-  auto load_step_scales = [&](int s, ScaleRaw& nsa, ScaleRaw& nsb) {
-    const int64_t k = k_begin + (int64_t)s * BK;
-    nsa = load_scales(opa, k, last_block(s));
-    nsb = load_scales(opb, k, last_block(s));
+  // issue step s into stage `slot`; steps past the last re-load the last step
+  // (every step issues the same loads, so the vmcnt arithmetic is fixed)
+  auto issue = [&](int slot, int s) {
+    const int sc = min(s, last);
+    const int64_t k = k_begin + (int64_t)sc * BK;
+    const int vc = sc == last ? tail_chunks : 4;
+    uint8_t* st = stages[slot];
+    issue_codes(opa, st, wave, lane, k, vc);
+    issue_codes(opb, st + kTileBytes, wave, lane, k, vc);
+    issue_scales(opa, st + 2 * kTileBytes, wave, lane, k, vc / 2);
+    issue_scales(opb, st + 2 * kTileBytes + kScaleRegion, wave, lane, k, vc / 2);
   };
-  auto load_step_codes = [&](uint8_t* dst, int s) {
-    const int64_t k = k_begin + (int64_t)s * BK;
-    const int lc = s == nk - 1 ? tail_chunks - 1 : 7;
-    issue_loads(opa, dst, wave, lane, k, lc);
-    issue_loads(opb, dst + kTileBytes, wave, lane, k, lc);
-  };
-  // after the loads of step s have landed in stage `dst`
-  auto settle = [&](uint8_t* dst, int s, const ScaleRaw& nsa, const ScaleRaw& nsb) {
-    store_scales(dst + 2 * kTileBytes, combine_scales(nsa, last_block(s)));
-    store_scales(dst + 2 * kTileBytes + kScaleBytes, combine_scales(nsb, last_block(s)));
-    const int lc = s == nk - 1 ? tail_chunks - 1 : 7;  // 7: nothing to zero
-    zero_tail(dst, wave, lane, lc);
-    zero_tail(dst + kTileBytes, wave, lane, lc);
-  };
-
-  ScaleRaw nsa{0u, 0u, 0}, nsb{0u, 0u, 0};
-  if (nk > 0) {
-    load_step_scales(0, nsa, nsb);
-    load_step_codes(lds, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    settle(lds, 0, nsa, nsb);
-  }
-  __syncthreads();
-  // The body is branch-free (one basic block) so the scheduling barrier below
-  // can keep the MFMAs ahead of the wait: the last step re-fetches itself into
-  // the idle stage instead of skipping the prefetch.
-  for (int kt = 0; kt < nk; kt++) {
-    uint8_t* cur = lds + (kt & 1) * kStageBytes;
-    uint8_t* nxt = lds + ((kt + 1) & 1) * kStageBytes;
-    const int sn = min(kt + 1, nk - 1);
-    load_step_scales(sn, nsa, nsb);
-    // fragments of step kt
-    const uint2 sa = *reinterpret_cast<const uint2*>(cur + 2 * kTileBytes + sidx(wm * 128 + (lane & 15), lane >> 4));
-    const uint2 sb = *reinterpret_cast<const uint2*>(cur + 2 * kTileBytes + kScaleBytes +
-                                                     sidx(wn * 128 + (lane & 15), lane >> 4));
-    v8i fa[TM], fb[TN];
-#pragma unroll
-    for (int i = 0; i < TM; i++) fa[i] = load_frag(cur, wm * WM + i * 16, lane);
-#pragma unroll
-    for (int j = 0; j < TN; j++) fb[j] = load_frag(cur + kTileBytes, wn * WN + j * 16, lane);
-    load_step_codes(nxt, sn);
-#pragma unroll
-    for (int j = 0; j < TN; j++) {
-      const int sbj = (int)(j < 4 ? sb.x : sb.y);
-#pragma unroll
-      for (int i = 0; i < TM; i++) {
-        const int sai = (int)(i < 4 ? sa.x : sa.y);
-        acc[i][j] = mfma_scaled(i & 3, j & 3, fa[i], fb[j], acc[i][j], sai, sbj);
-      }
+  // once step s has landed in `slot` (this wave's part): zero the chunks past
+  // the end of K, or the whole step if it only pads the loop to a multiple of four
+  auto fix = [&](int slot, int s) {
+    const int vc = s > last ? 0 : s == last ? tail_chunks : 4;
+    if (vc < 4) {
+      zero_codes(stages[slot], wave, lane, vc);
+      zero_codes(stages[slot] + kTileBytes, wave, lane, vc);
     }
-    // Keep the MFMAs ahead of the wait: they only touch registers, so the
-    // compiler would otherwise sink them below it (even into the next
-    // iteration) and serialise the loads and the math.  An empty volatile asm
-    // reading each accumulator pins every MFMA before the wait.
+  };
+
+  if (nk > 0) {
+    const int nsteps = (nk + 3) & ~3;
+    issue(0, 0);
+    issue(1, 1);
+    issue(2, 2);
+    issue(3, 3);
+    wait_vmcnt<3 * kVmemPerStep>();  // step 0 landed
+    fix(0, 0);
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    Frags f0, f1;
+    read_frags(stage0, wm, wn, lane, f0);
+    wait_lgkmcnt0();
+    // step k: publish stage k+1, refill stage k with step k+4, read step k+1's
+    // fragments while the MFMAs of step k run
+    auto step = [&](int cur, int s, Frags& fc, Frags& fn) {
+      wait_vmcnt<2 * kVmemPerStep>();  // this wave's loads of step s+1 landed
+      fix((cur + 1) & 3, s + 1);
+      wait_lgkmcnt0();
+      __builtin_amdgcn_s_barrier();  // step s+1 complete; every wave done with stage `cur`
+      __builtin_amdgcn_sched_barrier(0);
+      // LDS reads first (the scheduler would otherwise sink them under the
+      // MFMAs, leaving their latency exposed at the end of the step)
+      read_frags(stages[(cur + 1) & 3], wm, wn, lane, fn);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(cur, s + 4);
+      mfma_step(acc, fc);
+      wait_lgkmcnt0();
 #pragma unroll
-    for (int i = 0; i < TM; i++)
+      for (int i = 0; i < TM; i++)
 #pragma unroll
-      for (int j = 0; j < TN; j++) asm volatile("" : "+a"(acc[i][j]));
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0);
-    settle(nxt, sn, nsa, nsb);
-    __syncthreads();
+        for (int j = 0; j < TN; j++) asm volatile("" : "+a"(acc[i][j]));
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int kt = 0; kt < nsteps; kt += 4) {
+      step(0, kt + 0, f0, f1);
+      step(1, kt + 1, f1, f0);
+      step(2, kt + 2, f0, f1);
+      step(3, kt + 3, f1, f0);
+    }
+    wait_vmcnt<0>();  // the loads still in flight land before the LDS goes away
   }
 
-  // ---- epilogue: fp32 stores, rows/cols past the tile's valid range skipped
+  // ---- epilogue: fp32 stores (32 consecutive floats per half-wave), rows/cols
+  // past the tile's valid range skipped
   const int64_t ldo = MODE == kRaggedK ? N : ldc;
 #pragma unroll
   for (int i = 0; i < TM; i++) {
 #pragma unroll
     for (int j = 0; j < TN; j++) {
-      const int col = wn * WN + j * 16 + (lane & 15);
+      const int col = wn * WN + j * 32 + (lane & 31);
       if (col >= rows_b) continue;
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const int row = wm * WM + i * 16 + 4 * (lane >> 4) + e;
+      for (int e = 0; e < 16; e++) {
+        const int row = wm * WM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         if (row < rows_a) c_base[(m0 + row) * ldo + n0 + col] = acc[i][j][e];
       }
     }

@@ -75,6 +75,14 @@ __device__ __forceinline__ uint32_t e4m3_encode4(uint32_t lo, uint32_t hi, float
 
 __device__ __forceinline__ float e8m0_as_scale(uint32_t byte) { return __uint_as_float(byte << 23); }
 
+// Byte offset of the scale of row r, block b in an MXFP8 operand's scale array
+// (nblk blocks per row), 32-row interleaved: the scales of rows 32q .. 32q+31
+// for one block are 32 consecutive bytes, so a GEMM tile fetches the scales of
+// many rows for one K-block in a few cache lines.
+__device__ __forceinline__ int64_t scale_offset(int64_t r, int64_t b, int64_t nblk) {
+  return ((r >> 5) * nblk + b) * 32 + (r & 31);
+}
+
 // ---------------------------------------------------------------- MXFP4 (E2M1)
 // Exact round(log2(amax/6)) clamped at -30 from the fp32 bits of amax: with
 // amax = m * 2^E (m in [1,2)), log2(amax/6) rounds up to E-2 iff m >= 3/(2*sqrt 2),

@@ -7,7 +7,8 @@
 // element = E4M3 round-to-nearest-even of v / 2^(byte-127), saturated at 448.
 // The element conversion is the hardware scaled conversion plus a saturation
 // fix-up (see mxq_device.h); it was checked exhaustively over every bf16 value
-// and every scale byte against the CPU oracle.
+// and every scale byte against the CPU oracle.  Scales are written in the
+// 32-row interleaved layout of scale_offset().
 #include "mxq_device.h"
 #include "mxq_groups.h"
 #include "mxq_internal.h"
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(const uint16_t* __r
       codes.y = e4m3_encode4(w[2], w[3], sc);
       if (row_ok) {
         *reinterpret_cast<uint2*>(q + row * Cp + col) = codes;
-        if ((c8 & 3) == 0) s[row * (Cp / 32) + c8 / 4] = (uint8_t)byte;
+        if ((c8 & 3) == 0) s[scale_offset(row, c8 / 4, Cp / 32)] = (uint8_t)byte;
       }
     }
   }
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
       codes.y = e4m3_encode4(w[2], w[3], sc);
       if (row_ok && col < Cp) {
         *reinterpret_cast<uint2*>(q_row + src * Cp + col) = codes;
-        if ((c16 & 3) == 0) s_row[src * (Cp / 32) + col / 32] = (uint8_t)byte;
+        if ((c16 & 3) == 0) s_row[scale_offset(src, col / 32, Cp / 32)] = (uint8_t)byte;
       }
     }
     *reinterpret_cast<uint4*>(tile + lr * kLdsStride + c16 * 16) = make_uint4(w[0], w[1], w[2], w[3]);
@@ -189,12 +190,12 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
   uint8_t* dst = q_colT + col * ldq + pb * 32;
   reinterpret_cast<uint4*>(dst)[0] = make_uint4(clo[0], clo[1], clo[2], clo[3]);
   reinterpret_cast<uint4*>(dst)[1] = make_uint4(clo[4], clo[5], clo[6], clo[7]);
-  s_colT[col * nsb + pb] = (uint8_t)byte_lo;
+  s_colT[scale_offset(col, pb, nsb)] = (uint8_t)byte_lo;
   if (col + 1 < C) {
     dst += ldq;
     reinterpret_cast<uint4*>(dst)[0] = make_uint4(chi[0], chi[1], chi[2], chi[3]);
     reinterpret_cast<uint4*>(dst)[1] = make_uint4(chi[4], chi[5], chi[6], chi[7]);
-    s_colT[(col + 1) * nsb + pb] = (uint8_t)byte_hi;
+    s_colT[scale_offset(col + 1, pb, nsb)] = (uint8_t)byte_hi;
   }
 }
 

@@ -8,6 +8,11 @@ is no fallback.
 Functions named like the C entry points take every buffer from the caller;
 the lower-case helpers (``quantize``, ``gemm`` ...) allocate the outputs with
 ``torch.empty`` and call them.
+
+MXFP8 scale arrays are uint8 tensors of shape ``scale_shape(rows, nblk)`` =
+``(ceil32(rows) // 32, nblk, 32)``: element ``[r // 32, b, r % 32]`` is the
+E8M0 scale of row ``r``, block ``b`` (the 32-row interleaved layout of
+include/mxq.h).
 """
 from __future__ import annotations
 
@@ -108,6 +113,19 @@ def ceil32(v: int) -> int:
     return (v + BLOCK - 1) // BLOCK * BLOCK
 
 
+def scale_shape(rows: int, nblk: int) -> tuple:
+    """Shape of the interleaved scale array of an operand with `rows` rows and `nblk` blocks per row."""
+    return (ceil32(rows) // BLOCK, nblk, BLOCK)
+
+
+def _need_out(t, name, shape):
+    if t is None:
+        return
+    _need(t, torch.uint8, name)
+    if tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous uint8 tensor of shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 # ------------------------------------------------------------------ C entry points
 def mxq_abi_version() -> int:
     return _lib.mxq_abi_version()
@@ -131,6 +149,10 @@ def mxq_quantize(x, axis_mask, q_row=None, s_row=None, q_colT=None, s_colT=None,
     if x.stride(1) != 1:
         raise ValueError("x must have unit stride along its last dim")
     R, C = x.shape
+    _need_out(q_row, "q_row", (R, ceil32(C)))
+    _need_out(s_row, "s_row", scale_shape(R, ceil32(C) // BLOCK))
+    _need_out(q_colT, "q_colT", (C, ceil32(R)))
+    _need_out(s_colT, "s_colT", scale_shape(C, ceil32(R) // BLOCK))
     _check(_lib.mxq_quantize(_ptr(x), R, C, x.stride(0), axis_mask, _ptr(q_row), _ptr(s_row),
                              _ptr(q_colT), _ptr(s_colT), _stream(stream, x.device)), "mxq_quantize")
 
@@ -142,6 +164,10 @@ def mxq_quantize_grouped(x, group_end, ldq, axis_mask, q_row=None, s_row=None, q
     if x.stride(1) != 1:
         raise ValueError("x must have unit stride along its last dim")
     T, C = x.shape
+    _need_out(q_row, "q_row", (T, ceil32(C)))
+    _need_out(s_row, "s_row", scale_shape(T, ceil32(C) // BLOCK))
+    _need_out(q_colT, "q_colT", (C, ldq))
+    _need_out(s_colT, "s_colT", scale_shape(C, ldq // BLOCK))
     _check(_lib.mxq_quantize_grouped(_ptr(x), T, C, x.stride(0), _ptr(group_end), group_end.numel(),
                                      ldq, axis_mask, _ptr(q_row), _ptr(s_row), _ptr(q_colT),
                                      _ptr(s_colT), _stream(stream, x.device)), "mxq_quantize_grouped")
@@ -160,14 +186,17 @@ def mxq_qdq_fp4(x, y, codes=None, scales=None, stream=None):
 
 
 def mxq_gemm(A, sA, B, sB, C, stream=None):
-    """A uint8 [M][K], sA [M][K/32], B [N][K], sB [N][K/32] -> C fp32 [M][ldc >= N]."""
+    """A uint8 [M][K] + scales scale_shape(M, K/32), B [N][K] + scale_shape(N, K/32) -> C fp32 [M][ldc >= N]."""
     for t, n in ((A, "A"), (sA, "sA"), (B, "B"), (sB, "sB")):
-        _need(t, torch.uint8, n, 2)
+        _need(t, torch.uint8, n)
     _need(C, torch.float32, "C", 2)
     M, K = A.shape
     N = B.shape[0]
-    if B.shape[1] != K or sA.shape != (M, K // BLOCK) or sB.shape != (N, K // BLOCK):
+    if (B.dim() != 2 or B.shape[1] != K or tuple(sA.shape) != scale_shape(M, K // BLOCK)
+            or tuple(sB.shape) != scale_shape(N, K // BLOCK)):
         raise ValueError("operand shapes disagree")
+    if not all(t.is_contiguous() for t in (A, sA, B, sB)):
+        raise ValueError("operands must be contiguous")
     if C.shape[0] != M or C.shape[1] < N or C.stride(1) != 1:
         raise ValueError("C must be [M][>=N] with unit column stride")
     _check(_lib.mxq_gemm(_ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(C), M, N, K, C.stride(0),
@@ -175,7 +204,9 @@ def mxq_gemm(A, sA, B, sB, C, stream=None):
 
 
 def mxq_grouped_gemm(mode, A, sA, B, sB, C, group_end, stream=None):
-    """RAGGED_M: A [M][K], B [G][N][K], C [M][N].  RAGGED_K: A [M][K], B [N][K], C [G][M][N]."""
+    """RAGGED_M: A [M][K], B [G][N][K], C [M][N].  RAGGED_K: A [M][K], B [N][K], C [G][M][N].
+
+    Scales: sA scale_shape(M, K/32); sB (G,) + scale_shape(N, K/32) (ragged M) or scale_shape(N, K/32)."""
     for t, n in ((A, "A"), (sA, "sA"), (B, "B"), (sB, "sB")):
         _need(t, torch.uint8, n)
     _need(C, torch.float32, "C")
@@ -184,12 +215,16 @@ def mxq_grouped_gemm(mode, A, sA, B, sB, C, group_end, stream=None):
     M, K = A.shape
     N = B.shape[-2]
     if mode == MXQ_GG_RAGGED_M:
-        ok = B.shape == (G, N, K) and sB.shape == (G, N, K // BLOCK) and C.shape == (M, N)
+        ok = (tuple(B.shape) == (G, N, K) and tuple(sB.shape) == (G,) + scale_shape(N, K // BLOCK)
+              and tuple(C.shape) == (M, N))
     else:
         N = B.shape[0]
-        ok = B.shape == (N, K) and sB.shape == (N, K // BLOCK) and C.shape == (G, M, N)
-    if not ok or sA.shape != (M, K // BLOCK) or not C.is_contiguous():
+        ok = (tuple(B.shape) == (N, K) and tuple(sB.shape) == scale_shape(N, K // BLOCK)
+              and tuple(C.shape) == (G, M, N))
+    if not ok or tuple(sA.shape) != scale_shape(M, K // BLOCK):
         raise ValueError("grouped GEMM operand shapes disagree")
+    if not all(t.is_contiguous() for t in (A, sA, B, sB, C)):
+        raise ValueError("operands must be contiguous")
     _check(_lib.mxq_grouped_gemm(mode, _ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(C), M, N, K,
                                  _ptr(group_end), G, MXQ_FMT_E4M3, _stream(stream, A.device)),
            "mxq_grouped_gemm")
@@ -213,10 +248,10 @@ def quantize(x, axis_mask=MXQ_AXIS_ROW | MXQ_AXIS_COLT, stream=None):
     out = {}
     if axis_mask & MXQ_AXIS_ROW:
         out["q_row"] = _u8((R, ceil32(C)), x.device)
-        out["s_row"] = _u8((R, ceil32(C) // BLOCK), x.device)
+        out["s_row"] = _u8(scale_shape(R, ceil32(C) // BLOCK), x.device)
     if axis_mask & MXQ_AXIS_COLT:
         out["q_colT"] = _u8((C, ceil32(R)), x.device)
-        out["s_colT"] = _u8((C, ceil32(R) // BLOCK), x.device)
+        out["s_colT"] = _u8(scale_shape(C, ceil32(R) // BLOCK), x.device)
     mxq_quantize(x, axis_mask, out.get("q_row"), out.get("s_row"), out.get("q_colT"),
                  out.get("s_colT"), stream)
     return out
@@ -229,10 +264,10 @@ def quantize_grouped(x, group_end, axis_mask=MXQ_AXIS_COLT, ldq=None, stream=Non
     out = {"ldq": ldq}
     if axis_mask & MXQ_AXIS_ROW:
         out["q_row"] = _u8((T, ceil32(C)), x.device)
-        out["s_row"] = _u8((T, ceil32(C) // BLOCK), x.device)
+        out["s_row"] = _u8(scale_shape(T, ceil32(C) // BLOCK), x.device)
     if axis_mask & MXQ_AXIS_COLT:
         out["q_colT"] = _u8((C, ldq), x.device)
-        out["s_colT"] = _u8((C, ldq // BLOCK), x.device)
+        out["s_colT"] = _u8(scale_shape(C, ldq // BLOCK), x.device)
     mxq_quantize_grouped(x, group_end, ldq, axis_mask, out.get("q_row"), out.get("s_row"),
                          out.get("q_colT"), out.get("s_colT"), stream)
     return out

@@ -18,6 +18,26 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
+def unpack_scales(s: torch.Tensor, rows: int) -> np.ndarray:
+    """Interleaved MXFP8 scale array of shape (ceil32(rows)/32, nblk, 32)
+    (element [r//32, b, r%32] = scale of row r, block b) -> row-major
+    [rows][nblk] on the host."""
+    q, nblk, b = s.shape
+    assert b == 32 and q * 32 >= rows > q * 32 - 32, (tuple(s.shape), rows)
+    return host(s.permute(0, 2, 1).reshape(q * 32, nblk)[:rows])
+
+
+def scale_rows(s: torch.Tensor, idx) -> np.ndarray:
+    """Rows `idx` of an interleaved scale array, row-major [len(idx)][nblk] on the host."""
+    i = torch.as_tensor(np.asarray(idx), device=s.device)
+    return host(s[i // 32, :, i % 32])
+
+
+def out_host(got: dict, key: str, rows: int) -> np.ndarray:
+    """A quantiser output on the host in the oracle's layout (scales unpacked)."""
+    return unpack_scales(got[key], rows) if key.startswith("s_") else host(got[key])
+
+
 def bits(x: torch.Tensor) -> np.ndarray:
     """bf16 tensor (any device) -> uint16 bit patterns on the host."""
     return bf16_bits(x)

@@ -51,7 +51,9 @@ def test_build_targets_gfx950_only():
 
 def test_abi_version_and_pure_host_helpers(lib):
     lib.mxq_abi_version.restype = ctypes.c_int
-    assert lib.mxq_abi_version() == 1
+    header = open(os.path.join(ROOT, "include", "mxq.h")).read()
+    declared = int(re.search(r"#define MXQ_ABI_VERSION (\d+)", header).group(1))
+    assert lib.mxq_abi_version() == declared
     f = lib.mxq_grouped_cols_max
     f.restype = ctypes.c_int64
     f.argtypes = [ctypes.c_int64, ctypes.c_int32]

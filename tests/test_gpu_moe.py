@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from gpu_util import (assert_gemm_close, bits, boundary_indices, host, mfma_group_bound, mxq, ragged_k_bound,
-                      ragged_m_bound, scaled_randn)
+                      ragged_m_bound, scale_rows, scaled_randn)
 from moe_grouped_gemm_mxq_amd import workloads
 
 pytestmark = pytest.mark.gpu
@@ -80,18 +80,18 @@ def moe_full():
     # forward (dual-axis schedule): X by rows; W[g] on both axes in one read
     qx = m.quantize(X, 1)
     qw = {"q_row": torch.empty((G * K, N), dtype=torch.uint8, device="cuda"),
-          "s_row": torch.empty((G * K, N // 32), dtype=torch.uint8, device="cuda"),
+          "s_row": torch.empty(m.scale_shape(G * K, N // 32), dtype=torch.uint8, device="cuda"),
           "q_colT": torch.empty((G, N, K), dtype=torch.uint8, device="cuda"),
-          "s_colT": torch.empty((G, N, K // 32), dtype=torch.uint8, device="cuda")}
-    for g in range(G):
-        m.mxq_quantize(W[g], 3, qw["q_row"][g * K:(g + 1) * K], qw["s_row"][g * K:(g + 1) * K],
+          "s_colT": torch.empty((G,) + m.scale_shape(N, K // 32), dtype=torch.uint8, device="cuda")}
+    for g in range(G):   # K % 32 == 0: expert g's rows are row groups [g*K/32, (g+1)*K/32)
+        m.mxq_quantize(W[g], 3, qw["q_row"][g * K:(g + 1) * K], qw["s_row"][g * K // 32:(g + 1) * K // 32],
                        qw["q_colT"][g], qw["s_colT"][g])
     Y = m.grouped_gemm(m.MXQ_GG_RAGGED_M, qx["q_row"], qx["s_row"], qw["q_colT"], qw["s_colT"], ge)
     # backward: dY by rows and grouped token axis in one read; X grouped token axis
     qy = m.quantize_grouped(dY, ge, 3)
     qxt = m.quantize_grouped(X, ge, 2, ldq=qy["ldq"])
     dX = m.grouped_gemm(m.MXQ_GG_RAGGED_M, qy["q_row"], qy["s_row"],
-                        qw["q_row"].view(G, K, N), qw["s_row"].view(G, K, N // 32), ge)
+                        qw["q_row"].view(G, K, N), qw["s_row"].view(G, K // 32, N // 32, 32), ge)
     dW = m.grouped_gemm(m.MXQ_GG_RAGGED_K, qxt["q_colT"], qxt["s_colT"], qy["q_colT"], qy["s_colT"], ge)
     torch.cuda.synchronize()
     return dict(X=X, W=W, dY=dY, ge=ge, ge_np=host(ge), qx=qx, qw=qw, qy=qy, qxt=qxt, Y=Y, dX=dX, dW=dW,
@@ -156,7 +156,7 @@ def test_moe_grouped_token_quant_sampled(moe_full):
         P = oracle.grouped_cols(ge_np)
         idx = torch.as_tensor(cols, device="cuda")
         assert np.array_equal(host(q["q_colT"][idx])[:, :P], qr[:, :P]), name
-        assert np.array_equal(host(q["s_colT"][idx])[:, :P // 32], sr[:, :P // 32]), name
+        assert np.array_equal(scale_rows(q["s_colT"], cols)[:, :P // 32], sr[:, :P // 32]), name
 
 
 def test_moe_wgrad_ragged_k_full_sampled(moe_full):
@@ -197,6 +197,6 @@ def test_moe_fb_split_equals_dual(moe_full):
     assert torch.equal(fwd_only["s_row"], moe_full["qw"]["s_row"])
     qy = moe_full["qy"]
     dX = m.grouped_gemm(m.MXQ_GG_RAGGED_M, qy["q_row"], qy["s_row"],
-                        fwd_only["q_row"].view(G, K, N), fwd_only["s_row"].view(G, K, N // 32), ge)
+                        fwd_only["q_row"].view(G, K, N), fwd_only["s_row"].view(G, K // 32, N // 32, 32), ge)
     torch.cuda.synchronize()
     assert torch.equal(dX, moe_full["dX"])

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import assert_bytes_equal, bits, host, mxq, scaled_randn
+from gpu_util import assert_bytes_equal, bits, host, mxq, out_host, scaled_randn, unpack_scales
 from moe_grouped_gemm_mxq_amd import workloads
 
 pytestmark = pytest.mark.gpu
@@ -79,7 +79,7 @@ def test_quantize_bitexact(shape, axis):
     torch.cuda.synchronize()
     ref = quant_ref(bits(x), axis)
     for k, v in ref.items():
-        assert_bytes_equal(host(got[k]), v, f"{k} {shape}")
+        assert_bytes_equal(out_host(got, k, v.shape[0]), v, f"{k} {shape}")
 
 
 @pytest.mark.parametrize("C,pad", [(200, 8), (203, 3)])
@@ -92,7 +92,7 @@ def test_quantize_strided_input(C, pad):
     torch.cuda.synchronize()
     ref = quant_ref(bits(big[:, :C].contiguous()), 3)
     for k, v in ref.items():
-        assert np.array_equal(host(got[k]), v), k
+        assert np.array_equal(out_host(got, k, v.shape[0]), v), k
 
 
 def test_quantize_extreme_values():
@@ -103,7 +103,7 @@ def test_quantize_extreme_values():
     got = mxq().quantize(x.cuda(), 3)
     torch.cuda.synchronize()
     for k, v in quant_ref(bits(x), 3).items():
-        assert np.array_equal(host(got[k]), v), k
+        assert np.array_equal(out_host(got, k, v.shape[0]), v), k
 
 
 def exhaustive_blocks():
@@ -131,14 +131,14 @@ def test_quantize_every_element_and_scale_pair():
     got = m.quantize(x.cuda(), 1)
     torch.cuda.synchronize()
     q, s = oracle.mxfp8_quant_row(xb)
-    assert np.array_equal(host(got["s_row"]), s)
+    assert np.array_equal(unpack_scales(got["s_row"], len(s)), s)
     assert np.array_equal(host(got["q_row"]), q)
     # the same blocks through the column path (blocks running down columns)
     xt = np.ascontiguousarray(xb[:4096].T)                # [32][4096]
     got = m.quantize(torch.from_numpy(xt.view(np.int16)).view(torch.bfloat16).cuda(), 2)
     torch.cuda.synchronize()
     qt, st = oracle.mxfp8_quant_colT(xt)
-    assert np.array_equal(host(got["q_colT"]), qt) and np.array_equal(host(got["s_colT"]), st)
+    assert np.array_equal(host(got["q_colT"]), qt) and np.array_equal(unpack_scales(got["s_colT"], len(st)), st)
 
 
 GROUPS = [[70], [0, 1, 31, 32, 33, 0], [0, 0, 5], [64, 0], [17, 40, 1, 0, 96],
@@ -158,10 +158,10 @@ def test_grouped_quantize_bitexact(sizes, C, axis):
     P = oracle.grouped_cols(ge)
     q, s = oracle.mxfp8_quant_grouped_colT(bits(x), ge, got["ldq"])
     assert np.array_equal(host(got["q_colT"])[:, :P], q[:, :P])
-    assert np.array_equal(host(got["s_colT"])[:, :P // 32], s[:, :P // 32])
+    assert np.array_equal(unpack_scales(got["s_colT"], C)[:, :P // 32], s[:, :P // 32])
     if axis & 1:
         qr, sr = oracle.mxfp8_quant_row(bits(x))
-        assert np.array_equal(host(got["q_row"]), qr) and np.array_equal(host(got["s_row"]), sr)
+        assert np.array_equal(host(got["q_row"]), qr) and np.array_equal(unpack_scales(got["s_row"], T), sr)
 
 
 def test_validate_group_end():
