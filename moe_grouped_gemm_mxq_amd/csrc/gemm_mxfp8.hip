@@ -15,16 +15,17 @@
 // step (one v_mfma_scale_f32_32x32x64_f8f6f4 per block and step).
 //
 // Pipeline: codes (global_load_lds_dwordx4) and scale bytes
-// (global_load_lds_ubyte) go from global memory straight into LDS, into a
-// ring of four stages; step k's loads are issued four steps ahead, into the
-// stage that step k-4 used.  Each wave keeps two register sets of MFMA
-// fragments: while the MFMAs of step k run on one, the LDS reads of step k+1
-// fill the other, so the matrix cores never wait on LDS.  One s_barrier per
-// step (raw, with explicit vmcnt / lgkmcnt waits: a full __syncthreads would
-// drain the loads in flight) publishes stage k+1 and retires stage k.  The four
-// stages are separate LDS arrays and the loop is unrolled by four, so the
-// compiler can tell the stage being read from the stages being filled and
-// never waits on the latter.
+// (global_load_lds_ubyte) go from global memory straight into LDS.  LDS holds
+// two stages of two steps each (128 codes per tile row, so every 16-byte lane
+// load belongs to a fully used 128-byte line); the loads of a stage are issued
+// two steps before its first use.  Each wave keeps two register sets of MFMA
+// fragments: while the MFMAs of one step run on one set, the LDS reads of the
+// next step fill the other, so the matrix cores never wait on LDS.  One
+// s_barrier per two steps (raw, with explicit vmcnt / lgkmcnt waits: a full
+// __syncthreads would drain the loads in flight) publishes the next stage and
+// retires the current one.  The two stages are separate LDS arrays and the
+// loop is unrolled over both, so the compiler can tell the stage being read
+// from the stage being filled and never waits on the latter.
 //
 // Operand layout of v_mfma_scale_f32_32x32x64_f8f6f4 for FP8 (found by
 // probing): lane l holds row l%32; its bytes 0-15 are K = 16g..16g+15 and
@@ -44,13 +45,14 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr int kThreads = 256;
-constexpr int BM = 256, BN = 256, BK = 64;   // BK in codes (bytes) per step
+constexpr int BM = 256, BN = 256, BK = 64;   // BK: codes (bytes) per MFMA step
+constexpr int BKS = 2 * BK;                   // codes per tile row per stage (two steps)
 constexpr int WM = 128, WN = 128;             // wave tile
 constexpr int TM = WM / 32, TN = WN / 32;     // MFMA blocks per wave
-constexpr int kTileBytes = BM * BK;           // codes of one operand tile per stage (16 KB)
-constexpr int kScaleRegion = 4 * 2 * BM;      // one dword per (tile row, K-block) of one operand
-constexpr int kStageBytes = 2 * kTileBytes + 2 * kScaleRegion;  // A, B codes, A, B scales (36 KB)
-constexpr int kVmemPerStep = 12;              // per wave and step: 4 + 4 code loads, 2 + 2 scale loads
+constexpr int kTileBytes = BM * BKS;          // codes of one operand tile per stage (32 KB)
+constexpr int kScaleRegion = 4 * 4 * BM;      // one dword per (tile row, K-block) of one operand (4 KB)
+constexpr int kStageBytes = 2 * kTileBytes + 2 * kScaleRegion;  // A, B codes, A, B scales (72 KB)
+constexpr int kVmemPerStage = 24;             // per wave and stage: 8 + 8 code loads, 4 + 4 scale loads
 constexpr int kXcds = 8;                      // XCDs per MI355X; workgroups are dealt round robin
 constexpr int kGroupM = 8;                    // m-tiles per raster group
 
@@ -60,9 +62,13 @@ __device__ __forceinline__ v16f mfma_scaled(const v8i& a, const v8i& b, const v1
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
-// LDS position of 16-byte chunk c (0..3) of tile row r (64 bytes): XOR swizzle
-// so that the 16 rows a fragment read touches at once fall in distinct banks.
-__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ ((r >> 2) & 3)) << 4); }
+// LDS position of 16-byte chunk c (0..7) of tile row r (128 bytes per stage),
+// XOR-swizzled with f(r) = (r & 7) ^ ((r >> 3) & 1): a fragment read has its
+// lanes on consecutive rows at one chunk, and f makes any 8 aligned
+// consecutive rows land on 8 distinct 16-byte bank groups of a 128-byte bank
+// row (32 banks) and any 16 on 16 distinct groups of a 256-byte one (64
+// banks), so the read is conflict-free either way.
+__device__ __forceinline__ int swz(int r, int c) { return r * BKS + ((c ^ ((r & 7) ^ ((r >> 3) & 1))) << 4); }
 
 // One operand of one workgroup tile: tile rows [0, rows_valid), which are rows
 // row0 .. row0 + rows_valid - 1 of a matrix with codes at base + (r - row0)*ld
@@ -77,58 +83,82 @@ struct Operand {
   int rows_valid;
 };
 
-// Direct loads of one operand's codes (16 KB) for the step at k: wave w issues
-// 4 dwordx4 loads; load j fills LDS bytes [(4w + j) * 1024, +1024) = tile rows
-// 16(4w+j) .. +16, lane l writing 16-byte slot l%4 of row 16(4w+j) + l/4, which
-// holds global chunk slot ^ swizzle(row) = (l%4) ^ ((l/16)%4).  Chunks past
-// the end of K (the tail step) are fetched from the last valid chunk (always
-// in bounds) and zeroed by zero_codes() once they have landed.
-__device__ __forceinline__ int dma_chunk(int lane) { return (lane & 3) ^ ((lane >> 4) & 3); }
+// Per-lane load addresses of one operand, computed once per tile: the loads
+// of a stage then only add the stage's K offset (uniform) to a per-lane
+// 32-bit offset, so the K loop spends almost no VALU on addressing.
+//
+// Codes (32 KB per operand and stage): wave w issues 8 dwordx4 loads; load j
+// fills LDS bytes [q * 1024, +1024), q = 8w + j, = tile rows 8q .. 8q+7, lane
+// l writing 16-byte slot l%8 of row 8q + l/8, which holds global chunk
+// c = slot ^ f(row) = (l%8) ^ (l/8) ^ (j%2).  One load thus reads eight whole
+// 128-byte lines.  Chunks at or past the valid ones (the tail of K) are
+// fetched from the last valid chunk (always in bounds) and zeroed by
+// zero_codes() once they have landed.
+//
+// Scales: slot d (0..1023) of one operand and stage, one dword each (the scale
+// in its low byte): d = (((s*2 + h)*2 + g)*32 + r)*4 + i holds the scale of
+// tile row h*128 + i*32 + r over K-block g of step s (0, 1) of the stage.  A
+// lane of wave half h reading the 16 bytes at slot (((s*2 + h)*2 + l/32)*32 +
+// l%32)*4 gets its four MFMA row blocks' scales for step s.  Wave w fills
+// slots [256w, 256w+256) with four ubyte loads; load j has s = w/2 and g = j/2
+// (uniform), so its lanes differ only in the row: in the interleaved scale
+// layout they read 4 runs of 16 consecutive bytes.  A K-block past the end of
+// K re-reads the last valid one (its codes are zeroed).
+struct OperandAddr {
+  const uint8_t* cbase;  // codes of tile row 0
+  const uint8_t* sbase;  // scale bytes of the tile's first 32-row group, block 0
+  uint32_t coff[8];      // per load: row offset of the lane's row
+  uint32_t soff[4];      // per load: offset of the lane's scale row inside the groups
+};
 
-__device__ __forceinline__ void issue_codes(const Operand& op, uint8_t* tile, int wave, int lane, int64_t k,
-                                            int valid_chunks) {
-  int l = lane;
-  asm volatile("" : "+v"(l));  // keep the addresses from being hoisted out of the K loop
-  const int c = dma_chunk(l);
-  const int cc = c < valid_chunks ? c : valid_chunks - 1;
+__device__ __forceinline__ int dma_chunk(int j, int lane) { return (lane & 7) ^ (lane >> 3) ^ (j & 1); }
+
+__device__ __forceinline__ OperandAddr make_addr(const Operand& op, int wave, int lane) {
+  OperandAddr ad;
+  const int64_t nblk = op.ld / 32;
+  ad.cbase = op.base;
+  ad.sbase = op.sbase + (op.row0 >> 5) * nblk * 32;
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const int row = min((wave * 8 + j) * 8 + (lane >> 3), op.rows_valid - 1);
+    ad.coff[j] = (uint32_t)((int64_t)row * op.ld);
+  }
 #pragma unroll
   for (int j = 0; j < 4; j++) {
-    const int r = min((wave * 4 + j) * 16 + (l >> 2), op.rows_valid - 1);
-    __builtin_amdgcn_global_load_lds(op.base + (int64_t)r * op.ld + k + cc * 16,
-                                     (lds_ptr)(tile + (wave * 4 + j) * 1024), 16, 0, 0);
+    const int i = lane & 3, r = ((j & 1) * 16 + (lane >> 2)) & 31, h = wave & 1;
+    const int64_t R = op.row0 + min(h * 128 + i * 32 + r, op.rows_valid - 1);
+    ad.soff[j] = (uint32_t)(((R >> 5) - (op.row0 >> 5)) * nblk * 32 + (R & 31));
   }
+  return ad;
 }
 
-// Zero the code chunks at or past valid_chunks (0 zeroes the whole step) in
+__device__ __forceinline__ void issue_codes(const OperandAddr& ad, uint8_t* tile, int wave, int lane, int64_t k,
+                                            int valid_chunks) {
+  const uint8_t* base = ad.cbase + k;
+  const uint32_t c0 = (uint32_t)min(dma_chunk(0, lane), valid_chunks - 1) * 16;
+  const uint32_t c1 = (uint32_t)min(dma_chunk(1, lane), valid_chunks - 1) * 16;
+#pragma unroll
+  for (int j = 0; j < 8; j++)
+    __builtin_amdgcn_global_load_lds(base + (ad.coff[j] + ((j & 1) ? c1 : c0)),
+                                     (lds_ptr)(tile + (wave * 8 + j) * 1024), 16, 0, 0);
+}
+
+// Zero the code chunks at or past valid_chunks (0 zeroes the whole stage) in
 // the bytes this wave's own loads wrote; called after those loads landed.
 __device__ __forceinline__ void zero_codes(uint8_t* tile, int wave, int lane, int valid_chunks) {
-  if (dma_chunk(lane) >= valid_chunks)
 #pragma unroll
-    for (int j = 0; j < 4; j++)
-      *reinterpret_cast<uint4*>(tile + (wave * 4 + j) * 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
+  for (int j = 0; j < 8; j++)
+    if (dma_chunk(j, lane) >= valid_chunks)
+      *reinterpret_cast<uint4*>(tile + (wave * 8 + j) * 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// Scale slot d (0..511) of one operand and step, one dword each (the scale in
-// its low byte): d = ((h*2 + g)*32 + r)*4 + i holds the scale of tile row
-// h*128 + i*32 + r over K-block g of the step.  A lane of wave half h reading
-// the 16 bytes at slot ((h*2 + l/32)*32 + l%32)*4 gets its four MFMA row
-// blocks' scales.  Wave w fills slots [128w, 128w+128) with two ubyte loads;
-// in the interleaved scale layout the 64 lanes of one load read 4 runs of 16
-// consecutive bytes.  A K-block past the end of K re-reads block 0 (its codes
-// are zeroed).
-__device__ __forceinline__ void issue_scales(const Operand& op, uint8_t* region, int wave, int lane, int64_t k,
+__device__ __forceinline__ void issue_scales(const OperandAddr& ad, uint8_t* region, int wave, int64_t k,
                                              int valid_blocks) {
-  int l = lane;
-  asm volatile("" : "+v"(l));
-  const int64_t nblk = op.ld / 32;
 #pragma unroll
-  for (int j = 0; j < 2; j++) {
-    const int d = (wave * 2 + j) * 64 + l;
-    const int i = d & 3, r = (d >> 2) & 31, g = (d >> 7) & 1, h = d >> 8;
-    const int row = min(h * 128 + i * 32 + r, op.rows_valid - 1);
-    const int gg = min(g, valid_blocks - 1);
-    __builtin_amdgcn_global_load_lds(op.sbase + scale_offset(op.row0 + row, k / 32 + gg, nblk),
-                                     (lds_ptr)(region + (wave * 2 + j) * 256), 1, 0, 0);
+  for (int j = 0; j < 4; j++) {
+    const int blk = min((wave >> 1) * 2 + ((j >> 1) & 1), valid_blocks - 1);  // uniform
+    __builtin_amdgcn_global_load_lds(ad.sbase + (k + blk * 32) + ad.soff[j],
+                                     (lds_ptr)(region + (wave * 4 + j) * 256), 1, 0, 0);
   }
 }
 
@@ -139,25 +169,26 @@ struct Frags {
   uint4 sa, sb;
 };
 
-__device__ __forceinline__ v8i load_frag(const uint8_t* codes, int r0, int lane) {
+// fragment of the MFMA row block starting at tile row r0, step s of the stage
+__device__ __forceinline__ v8i load_frag(const uint8_t* codes, int r0, int s, int lane) {
   const int r = r0 + (lane & 31);
   const int g = lane >> 5;
-  const uint4 lo = *reinterpret_cast<const uint4*>(codes + swz(r, g));
-  const uint4 hi = *reinterpret_cast<const uint4*>(codes + swz(r, 2 + g));
+  const uint4 lo = *reinterpret_cast<const uint4*>(codes + swz(r, 4 * s + g));
+  const uint4 hi = *reinterpret_cast<const uint4*>(codes + swz(r, 4 * s + 2 + g));
   v8i f;
   f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
   f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
   return f;
 }
 
-__device__ __forceinline__ void read_frags(const uint8_t* st, int wm, int wn, int lane, Frags& f) {
-  const int so = (((lane >> 5) * 32 + (lane & 31)) * 4) * 4;
-  f.sa = *reinterpret_cast<const uint4*>(st + 2 * kTileBytes + wm * 1024 + so);
-  f.sb = *reinterpret_cast<const uint4*>(st + 2 * kTileBytes + kScaleRegion + wn * 1024 + so);
+__device__ __forceinline__ void read_frags(const uint8_t* st, int s, int wm, int wn, int lane, Frags& f) {
+  const int so = ((lane >> 5) * 32 + (lane & 31)) * 16;
+  f.sa = *reinterpret_cast<const uint4*>(st + 2 * kTileBytes + (s * 2 + wm) * 1024 + so);
+  f.sb = *reinterpret_cast<const uint4*>(st + 2 * kTileBytes + kScaleRegion + (s * 2 + wn) * 1024 + so);
 #pragma unroll
-  for (int i = 0; i < TM; i++) f.a[i] = load_frag(st, wm * WM + i * 32, lane);
+  for (int i = 0; i < TM; i++) f.a[i] = load_frag(st, wm * WM + i * 32, s, lane);
 #pragma unroll
-  for (int j = 0; j < TN; j++) f.b[j] = load_frag(st + kTileBytes, wn * WN + j * 32, lane);
+  for (int j = 0; j < TN; j++) f.b[j] = load_frag(st + kTileBytes, wn * WN + j * 32, s, lane);
 }
 
 __device__ __forceinline__ int u4_get(const uint4& v, int i) {
@@ -201,8 +232,8 @@ __device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int& mt,
   nt = r / gm;
 }
 
-// group bookkeeping of the grouped modes, placed in the last stage (used
-// only before that stage's first load is issued)
+// group bookkeeping of the grouped modes, placed in stage 1 (used only
+// before the first load is issued)
 struct GroupScratch {
   GroupTable gt;
   int32_t scan_tmp[kThreads];
@@ -217,8 +248,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
     int64_t ldc, const int32_t* __restrict__ group_end, int32_t G, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage2[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage3[kStageBytes];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -238,7 +267,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
     n0 = (int64_t)nt * BN;
     rows_a = (int)min<int64_t>(BM, M - m0);
   } else {
-    GroupScratch& gs = *reinterpret_cast<GroupScratch*>(stage3);
+    GroupScratch& gs = *reinterpret_cast<GroupScratch*>(stage1);
     GroupTable& gt = gs.gt;
     int32_t* const scan_tmp = gs.scan_tmp;
     if constexpr (MODE == kRaggedM) {
@@ -289,10 +318,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
     }
   }
   const int rows_b = (int)min<int64_t>(BN, N - n0);
-  if constexpr (MODE != kDense) __syncthreads();  // group scratch read; stage 3 may now be loaded
+  if constexpr (MODE != kDense) __syncthreads();  // group scratch read; stage 1 may now be loaded
 
   const Operand opa{A + m0 * lda, sA, m0, lda, rows_a};
   const Operand opb{b_base + n0 * lda, sb_base, n0, lda, rows_b};
+  const OperandAddr ada = make_addr(opa, wave, lane);
+  const OperandAddr adb = make_addr(opb, wave, lane);
 
   v16f acc[TM][TN];
 #pragma unroll
@@ -302,72 +333,107 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
 #pragma unroll
       for (int e = 0; e < 16; e++) acc[i][j][e] = 0.f;
 
-  const int nk = (int)((k_end - k_begin + BK - 1) / BK);
-  const int last = nk - 1;
-  const int tail_chunks = nk > 0 ? (int)((k_end - k_begin) - (int64_t)last * BK) / 16 : 4;  // 2 or 4
-  uint8_t* const stages[4] = {stage0, stage1, stage2, stage3};
+  // stages of two steps: ns stages, the last holding tail_chunks 16-byte
+  // chunks per row (2, 4, 6 or 8; K is a multiple of 32)
+  const int64_t klen = k_end - k_begin;
+  const int ns = (int)((klen + BKS - 1) / BKS);
+  const int last = ns - 1;
+  const int tail_chunks = ns > 0 ? (int)(klen - (int64_t)last * BKS) / 16 : 8;
+  uint8_t* const stages[2] = {stage0, stage1};
 
-  // issue step s into stage `slot`; steps past the last re-load the last step
-  // (every step issues the same loads, so the vmcnt arithmetic is fixed)
+  // issue stage s into LDS stage `slot`; stages past the last re-load the last
+  // one (every stage issues the same loads, so the vmcnt arithmetic is fixed)
   auto issue = [&](int slot, int s) {
     const int sc = min(s, last);
-    const int64_t k = k_begin + (int64_t)sc * BK;
-    const int vc = sc == last ? tail_chunks : 4;
+    const int64_t k = k_begin + (int64_t)sc * BKS;
+    const int vc = sc == last ? tail_chunks : 8;
     uint8_t* st = stages[slot];
-    issue_codes(opa, st, wave, lane, k, vc);
-    issue_codes(opb, st + kTileBytes, wave, lane, k, vc);
-    issue_scales(opa, st + 2 * kTileBytes, wave, lane, k, vc / 2);
-    issue_scales(opb, st + 2 * kTileBytes + kScaleRegion, wave, lane, k, vc / 2);
+    issue_codes(ada, st, wave, lane, k, vc);
+    issue_codes(adb, st + kTileBytes, wave, lane, k, vc);
+    issue_scales(ada, st + 2 * kTileBytes, wave, k, vc / 2);
+    issue_scales(adb, st + 2 * kTileBytes + kScaleRegion, wave, k, vc / 2);
   };
-  // once step s has landed in `slot` (this wave's part): zero the chunks past
-  // the end of K, or the whole step if it only pads the loop to a multiple of four
+  // once stage s has landed in `slot` (this wave's part): zero the chunks past
+  // the end of K, or all of it if it only pads the loop to an even count
   auto fix = [&](int slot, int s) {
-    const int vc = s > last ? 0 : s == last ? tail_chunks : 4;
-    if (vc < 4) {
+    const int vc = s > last ? 0 : s == last ? tail_chunks : 8;
+    if (vc < 8) {
       zero_codes(stages[slot], wave, lane, vc);
       zero_codes(stages[slot] + kTileBytes, wave, lane, vc);
     }
   };
+  auto pin = [&]() {
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+      for (int j = 0; j < TN; j++) asm volatile("" : "+a"(acc[i][j]));
+  };
 
-  if (nk > 0) {
-    const int nsteps = (nk + 3) & ~3;
+  if (ns > 0) {
+    const int nstages = (ns + 1) & ~1;  // the loop covers both LDS stages per trip
     issue(0, 0);
     issue(1, 1);
-    issue(2, 2);
-    issue(3, 3);
-    wait_vmcnt<3 * kVmemPerStep>();  // step 0 landed
+    wait_vmcnt<kVmemPerStage>();  // stage 0 landed (stage 1 may still be in flight)
     fix(0, 0);
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
     Frags f0, f1;
-    read_frags(stage0, wm, wn, lane, f0);
+    read_frags(stage0, 0, wm, wn, lane, f0);
     wait_lgkmcnt0();
-    // step k: publish stage k+1, refill stage k with step k+4, read step k+1's
-    // fragments while the MFMAs of step k run
-    auto step = [&](int cur, int s, Frags& fc, Frags& fn) {
-      wait_vmcnt<2 * kVmemPerStep>();  // this wave's loads of step s+1 landed
-      fix((cur + 1) & 3, s + 1);
-      wait_lgkmcnt0();
-      __builtin_amdgcn_s_barrier();  // step s+1 complete; every wave done with stage `cur`
-      __builtin_amdgcn_sched_barrier(0);
-      // LDS reads first (the scheduler would otherwise sink them under the
-      // MFMAs, leaving their latency exposed at the end of the step)
-      read_frags(stages[(cur + 1) & 3], wm, wn, lane, fn);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(cur, s + 4);
-      mfma_step(acc, fc);
-      wait_lgkmcnt0();
+    // the two steps of stage s (in LDS stage `cur`); on entry f0 holds step 0's
+    // fragments; on exit f0 holds step 0 of stage s+1
+    // Instruction order inside a step (one wave per SIMD issues everything in
+    // order, so a queue-full LDS or memory instruction would hold up the
+    // MFMAs behind it): the first MFMA goes first, the 18 LDS reads of the next
+    // step follow three per MFMA, and the stage's 24 loads two per MFMA after
+    // that, so the matrix pipe always has work queued.
+    auto interleave = [](bool with_loads) {
 #pragma unroll
-      for (int i = 0; i < TM; i++)
+      for (int m = 0; m < 6; m++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // LDS reads
+      }
+      if (with_loads) {
 #pragma unroll
-        for (int j = 0; j < TN; j++) asm volatile("" : "+a"(acc[i][j]));
+        for (int m = 0; m < 4; m++) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 3, 0);  // global loads (into LDS)
+        }
+#pragma unroll
+        for (int m = 0; m < 6; m++) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+        }
+      }
+    };
+    auto stage_steps = [&](int cur, int s) {
+      // step 0: fragments of step 1 (same stage) while step 0's MFMAs run
+      read_frags(stages[cur], 1, wm, wn, lane, f1);
+      mfma_step(acc, f0);
+      interleave(false);
+      __builtin_amdgcn_sched_barrier(0);  // the wait must not rise above the MFMAs
+      wait_lgkmcnt0();
+      pin();
+      __builtin_amdgcn_sched_barrier(0);
+      // step 1: publish stage s+1, refill this stage with s+2, read stage s+1's
+      // first fragments while step 1's MFMAs run
+      wait_vmcnt<0>();  // this wave's loads of stage s+1 landed
+      fix(cur ^ 1, s + 1);
+      wait_lgkmcnt0();
+      __builtin_amdgcn_s_barrier();  // stage s+1 complete; every wave done reading stage `cur`
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(stages[cur ^ 1], 0, wm, wn, lane, f0);
+      issue(cur, s + 2);
+      mfma_step(acc, f1);
+      interleave(true);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_lgkmcnt0();
+      pin();
       __builtin_amdgcn_sched_barrier(0);
     };
-    for (int kt = 0; kt < nsteps; kt += 4) {
-      step(0, kt + 0, f0, f1);
-      step(1, kt + 1, f1, f0);
-      step(2, kt + 2, f0, f1);
-      step(3, kt + 3, f1, f0);
+    for (int s = 0; s < nstages; s += 2) {
+      stage_steps(0, s);
+      stage_steps(1, s + 1);
     }
     wait_vmcnt<0>();  // the loads still in flight land before the LDS goes away
   }
