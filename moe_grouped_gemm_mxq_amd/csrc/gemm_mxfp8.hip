@@ -10,20 +10,20 @@
 //   ragged K -- the reduction axis split into groups, one output per group
 //               (expert weight gradient over each group's padded tokens).
 //
-// Tiling: 256 x 256 output tile per workgroup of 4 waves (2 x 2), each wave a
-// 128 x 128 sub-tile of 4 x 4 MFMA blocks of 32 x 32; K advances 64 codes per
-// step (one v_mfma_scale_f32_32x32x64_f8f6f4 per block and step).
+// Tiling: 256 x 256 output tile per workgroup of 8 waves (2 x 4, two per
+// SIMD), each wave a 128 x 64 sub-tile of 4 x 2 MFMA blocks of 32 x 32; K
+// advances 64 codes per step (one v_mfma_scale_f32_32x32x64_f8f6f4 per block
+// and step).  Two waves per SIMD let one wave's MFMAs run while the other
+// waits on its LDS reads, and keep enough LDS requests in flight for the LDS
+// to serve both the fragment reads and the direct loads writing into it.
 //
 // Pipeline: codes (global_load_lds_dwordx4) and scale bytes
 // (global_load_lds_ubyte) go from global memory straight into LDS.  LDS holds
 // two stages of two steps each (128 codes per tile row, so every 16-byte lane
 // load belongs to a fully used 128-byte line); the loads of a stage are issued
-// two steps before its first use.  Each wave keeps two register sets of MFMA
-// fragments: while the MFMAs of one step run on one set, the LDS reads of the
-// next step fill the other, so the matrix cores never wait on LDS.  One
-// s_barrier per two steps (raw, with explicit vmcnt / lgkmcnt waits: a full
-// __syncthreads would drain the loads in flight) publishes the next stage and
-// retires the current one.  The two stages are separate LDS arrays and the
+// two steps before its first use.  One s_barrier per two steps (raw, with
+// explicit vmcnt / lgkmcnt waits: a full __syncthreads would drain the loads
+// in flight) publishes the next stage and retires the current one.  The two stages are separate LDS arrays and the
 // loop is unrolled over both, so the compiler can tell the stage being read
 // from the stage being filled and never waits on the latter.
 //
@@ -44,15 +44,14 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int BM = 256, BN = 256, BK = 64;   // BK: codes (bytes) per MFMA step
 constexpr int BKS = 2 * BK;                   // codes per tile row per stage (two steps)
-constexpr int WM = 128, WN = 128;             // wave tile
+constexpr int WM = 128, WN = 64;              // wave tile
 constexpr int TM = WM / 32, TN = WN / 32;     // MFMA blocks per wave
 constexpr int kTileBytes = BM * BKS;          // codes of one operand tile per stage (32 KB)
 constexpr int kScaleRegion = 4 * 4 * BM;      // one dword per (tile row, K-block) of one operand (4 KB)
 constexpr int kStageBytes = 2 * kTileBytes + 2 * kScaleRegion;  // A, B codes, A, B scales (72 KB)
-constexpr int kVmemPerStage = 24;             // per wave and stage: 8 + 8 code loads, 4 + 4 scale loads
 constexpr int kXcds = 8;                      // XCDs per MI355X; workgroups are dealt round robin
 constexpr int kGroupM = 8;                    // m-tiles per raster group
 
@@ -87,8 +86,8 @@ struct Operand {
 // of a stage then only add the stage's K offset (uniform) to a per-lane
 // 32-bit offset, so the K loop spends almost no VALU on addressing.
 //
-// Codes (32 KB per operand and stage): wave w issues 8 dwordx4 loads; load j
-// fills LDS bytes [q * 1024, +1024), q = 8w + j, = tile rows 8q .. 8q+7, lane
+// Codes (32 KB per operand and stage): wave w issues 4 dwordx4 loads; load j
+// fills LDS bytes [q * 1024, +1024), q = 4w + j, = tile rows 8q .. 8q+7, lane
 // l writing 16-byte slot l%8 of row 8q + l/8, which holds global chunk
 // c = slot ^ f(row) = (l%8) ^ (l/8) ^ (j%2).  One load thus reads eight whole
 // 128-byte lines.  Chunks at or past the valid ones (the tail of K) are
@@ -99,16 +98,17 @@ struct Operand {
 // in its low byte): d = (((s*2 + h)*2 + g)*32 + r)*4 + i holds the scale of
 // tile row h*128 + i*32 + r over K-block g of step s (0, 1) of the stage.  A
 // lane of wave half h reading the 16 bytes at slot (((s*2 + h)*2 + l/32)*32 +
-// l%32)*4 gets its four MFMA row blocks' scales for step s.  Wave w fills
-// slots [256w, 256w+256) with four ubyte loads; load j has s = w/2 and g = j/2
-// (uniform), so its lanes differ only in the row: in the interleaved scale
-// layout they read 4 runs of 16 consecutive bytes.  A K-block past the end of
+// l%32)*4 gets the scales of the four 32-row blocks of half h for step s.
+// Wave w fills slots [128w, 128w+128) with two ubyte loads; load j has
+// s = w/4, h = (w/2)%2 and g = w%2 (uniform), so its lanes differ only in the
+// row: in the interleaved scale layout they read 4 runs of 16 consecutive
+// bytes.  A K-block past the end of
 // K re-reads the last valid one (its codes are zeroed).
 struct OperandAddr {
   const uint8_t* cbase;  // codes of tile row 0
   const uint8_t* sbase;  // scale bytes of the tile's first 32-row group, block 0
-  uint32_t coff[8];      // per load: row offset of the lane's row
-  uint32_t soff[4];      // per load: offset of the lane's scale row inside the groups
+  uint32_t coff[4];      // per load: row offset of the lane's row
+  uint32_t soff[2];      // per load: offset of the lane's scale row inside the groups
 };
 
 __device__ __forceinline__ int dma_chunk(int j, int lane) { return (lane & 7) ^ (lane >> 3) ^ (j & 1); }
@@ -119,13 +119,13 @@ __device__ __forceinline__ OperandAddr make_addr(const Operand& op, int wave, in
   ad.cbase = op.base;
   ad.sbase = op.sbase + (op.row0 >> 5) * nblk * 32;
 #pragma unroll
-  for (int j = 0; j < 8; j++) {
-    const int row = min((wave * 8 + j) * 8 + (lane >> 3), op.rows_valid - 1);
+  for (int j = 0; j < 4; j++) {
+    const int row = min((wave * 4 + j) * 8 + (lane >> 3), op.rows_valid - 1);
     ad.coff[j] = (uint32_t)((int64_t)row * op.ld);
   }
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int i = lane & 3, r = ((j & 1) * 16 + (lane >> 2)) & 31, h = wave & 1;
+  for (int j = 0; j < 2; j++) {
+    const int i = lane & 3, r = (j * 16 + (lane >> 2)) & 31, h = (wave >> 1) & 1;
     const int64_t R = op.row0 + min(h * 128 + i * 32 + r, op.rows_valid - 1);
     ad.soff[j] = (uint32_t)(((R >> 5) - (op.row0 >> 5)) * nblk * 32 + (R & 31));
   }
@@ -138,35 +138,36 @@ __device__ __forceinline__ void issue_codes(const OperandAddr& ad, uint8_t* tile
   const uint32_t c0 = (uint32_t)min(dma_chunk(0, lane), valid_chunks - 1) * 16;
   const uint32_t c1 = (uint32_t)min(dma_chunk(1, lane), valid_chunks - 1) * 16;
 #pragma unroll
-  for (int j = 0; j < 8; j++)
+  for (int j = 0; j < 4; j++)
     __builtin_amdgcn_global_load_lds(base + (ad.coff[j] + ((j & 1) ? c1 : c0)),
-                                     (lds_ptr)(tile + (wave * 8 + j) * 1024), 16, 0, 0);
+                                     (lds_ptr)(tile + (wave * 4 + j) * 1024), 16, 0, 0);
 }
 
 // Zero the code chunks at or past valid_chunks (0 zeroes the whole stage) in
 // the bytes this wave's own loads wrote; called after those loads landed.
 __device__ __forceinline__ void zero_codes(uint8_t* tile, int wave, int lane, int valid_chunks) {
 #pragma unroll
-  for (int j = 0; j < 8; j++)
+  for (int j = 0; j < 4; j++)
     if (dma_chunk(j, lane) >= valid_chunks)
-      *reinterpret_cast<uint4*>(tile + (wave * 8 + j) * 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(tile + (wave * 4 + j) * 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
 }
 
 __device__ __forceinline__ void issue_scales(const OperandAddr& ad, uint8_t* region, int wave, int64_t k,
                                              int valid_blocks) {
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int blk = min((wave >> 1) * 2 + ((j >> 1) & 1), valid_blocks - 1);  // uniform
+  for (int j = 0; j < 2; j++) {
+    const int blk = min((wave >> 2) * 2 + (wave & 1), valid_blocks - 1);  // uniform
     __builtin_amdgcn_global_load_lds(ad.sbase + (k + blk * 32) + ad.soff[j],
-                                     (lds_ptr)(region + (wave * 4 + j) * 256), 1, 0, 0);
+                                     (lds_ptr)(region + (wave * 2 + j) * 256), 1, 0, 0);
   }
 }
 
-// MFMA operands of one step for one wave: 4 row blocks of A, 4 of B (32 bytes
-// per lane each), and the lane's 4 + 4 block scales.
+// MFMA operands of one step for one wave: 4 row blocks of A, 2 of B (32 bytes
+// per lane each), and the lane's 4 + 2 block scales.
 struct Frags {
   v8i a[TM], b[TN];
-  uint4 sa, sb;
+  uint4 sa;
+  uint2 sb;
 };
 
 // fragment of the MFMA row block starting at tile row r0, step s of the stage
@@ -181,10 +182,13 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* codes, int r0, int s, in
   return f;
 }
 
+// B rows wn*64 .. wn*64+63 are 32-row blocks 2*(wn%2) and 2*(wn%2)+1 of half
+// wn/2: their two scale dwords sit 8*(wn%2) bytes into the lane's 16.
 __device__ __forceinline__ void read_frags(const uint8_t* st, int s, int wm, int wn, int lane, Frags& f) {
   const int so = ((lane >> 5) * 32 + (lane & 31)) * 16;
   f.sa = *reinterpret_cast<const uint4*>(st + 2 * kTileBytes + (s * 2 + wm) * 1024 + so);
-  f.sb = *reinterpret_cast<const uint4*>(st + 2 * kTileBytes + kScaleRegion + (s * 2 + wn) * 1024 + so);
+  f.sb = *reinterpret_cast<const uint2*>(st + 2 * kTileBytes + kScaleRegion + (s * 2 + (wn >> 1)) * 1024 + so +
+                                         (wn & 1) * 8);
 #pragma unroll
   for (int i = 0; i < TM; i++) f.a[i] = load_frag(st, wm * WM + i * 32, s, lane);
 #pragma unroll
@@ -199,7 +203,8 @@ __device__ __forceinline__ void mfma_step(v16f (&acc)[TM][TN], const Frags& f) {
 #pragma unroll
   for (int i = 0; i < TM; i++)
 #pragma unroll
-    for (int j = 0; j < TN; j++) acc[i][j] = mfma_scaled(f.a[i], f.b[j], acc[i][j], u4_get(f.sa, i), u4_get(f.sb, j));
+    for (int j = 0; j < TN; j++)
+      acc[i][j] = mfma_scaled(f.a[i], f.b[j], acc[i][j], u4_get(f.sa, i), (int)(j == 0 ? f.sb.x : f.sb.y));
 }
 
 // s_waitcnt with vmcnt(n) only (expcnt / lgkmcnt left at their maximum), gfx9 encoding
@@ -251,7 +256,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int bid = blockIdx.x;
 
   // ---- which output tile, and the operands behind it
@@ -372,63 +377,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
   if (ns > 0) {
     const int nstages = (ns + 1) & ~1;  // the loop covers both LDS stages per trip
     issue(0, 0);
-    issue(1, 1);
-    wait_vmcnt<kVmemPerStage>();  // stage 0 landed (stage 1 may still be in flight)
+    wait_vmcnt<0>();  // stage 0 landed
     fix(0, 0);
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
-    Frags f0, f1;
-    read_frags(stage0, 0, wm, wn, lane, f0);
-    wait_lgkmcnt0();
-    // the two steps of stage s (in LDS stage `cur`); on entry f0 holds step 0's
-    // fragments; on exit f0 holds step 0 of stage s+1
-    // Instruction order inside a step (one wave per SIMD issues everything in
-    // order, so a queue-full LDS or memory instruction would hold up the
-    // MFMAs behind it): the first MFMA goes first, the 18 LDS reads of the next
-    // step follow three per MFMA, and the stage's 24 loads two per MFMA after
-    // that, so the matrix pipe always has work queued.
-    auto interleave = [](bool with_loads) {
-#pragma unroll
-      for (int m = 0; m < 6; m++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // LDS reads
-      }
-      if (with_loads) {
-#pragma unroll
-        for (int m = 0; m < 4; m++) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 3, 0);  // global loads (into LDS)
-        }
-#pragma unroll
-        for (int m = 0; m < 6; m++) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-        }
-      }
-    };
+    Frags f;
+    // The two steps of stage s (in LDS stage `cur`, published by the last
+    // barrier).  Each wave reads a step's fragments and runs its 8 MFMAs as
+    // soon as they arrive (the compiler waits per fragment); the other wave
+    // on the SIMD keeps the matrix pipe busy meanwhile.  The loads of stage
+    // s+1 go out right after step 0's fragment reads, into the other LDS
+    // stage (every wave finished reading it before the last barrier), and
+    // have the two steps to land.
     auto stage_steps = [&](int cur, int s) {
-      // step 0: fragments of step 1 (same stage) while step 0's MFMAs run
-      read_frags(stages[cur], 1, wm, wn, lane, f1);
-      mfma_step(acc, f0);
-      interleave(false);
-      __builtin_amdgcn_sched_barrier(0);  // the wait must not rise above the MFMAs
-      wait_lgkmcnt0();
+      // step 0
+      read_frags(stages[cur], 0, wm, wn, lane, f);
+      issue(cur ^ 1, s + 1);
+      mfma_step(acc, f);
       pin();
       __builtin_amdgcn_sched_barrier(0);
-      // step 1: publish stage s+1, refill this stage with s+2, read stage s+1's
-      // first fragments while step 1's MFMAs run
+      // step 1
+      read_frags(stages[cur], 1, wm, wn, lane, f);
+      mfma_step(acc, f);
+      pin();
+      __builtin_amdgcn_sched_barrier(0);
+      // publish stage s+1; after the barrier every wave is done reading `cur`
       wait_vmcnt<0>();  // this wave's loads of stage s+1 landed
       fix(cur ^ 1, s + 1);
       wait_lgkmcnt0();
-      __builtin_amdgcn_s_barrier();  // stage s+1 complete; every wave done reading stage `cur`
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags(stages[cur ^ 1], 0, wm, wn, lane, f0);
-      issue(cur, s + 2);
-      mfma_step(acc, f1);
-      interleave(true);
-      __builtin_amdgcn_sched_barrier(0);
-      wait_lgkmcnt0();
-      pin();
+      __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
     };
     for (int s = 0; s < nstages; s += 2) {
