@@ -246,6 +246,54 @@ struct GroupScratch {
 };
 static_assert(sizeof(GroupScratch) <= kStageBytes, "group scratch must fit in one stage");
 
+// One output tile: where its operands and output live and which K range it
+// reduces over.  All fields are workgroup-uniform.
+struct Tile {
+  int64_t m0, n0;          // first output row / column
+  int rows_a, rows_b;      // valid rows of the A and B tiles (<= 256)
+  int64_t k_begin, klen;   // reduction range; klen == 0: an empty expert (zeros)
+  const uint8_t* b_base;   // B codes of the tile's expert (ragged M) or B
+  const uint8_t* sb_base;  // B scales of the tile's expert
+  float* c_base;           // output matrix of the tile (ragged K: the expert's)
+  int nst;                 // stages of two steps, rounded up to even (0 if klen == 0)
+  int last, tail_chunks;   // last real stage and its valid 16-byte chunks per row
+};
+
+// fp32 stores of one tile's accumulators (32 consecutive floats per half
+// wave); rows / columns past the tile's valid range are skipped.  The row
+// pointer advances one row at a time (a 64-bit add), so the stores need no
+// per-element address arithmetic and few registers.
+__device__ __forceinline__ void store_tile(const v16f (&acc)[TM][TN], const Tile& tl, int64_t ldo, int wm,
+                                           int wn, int lane) {
+  const int col0 = wn * WN + (lane & 31);
+  const int row0 = wm * WM + 4 * (lane >> 5);
+  float* p = tl.c_base + (tl.m0 + row0) * ldo + tl.n0 + col0;
+  const bool c_ok0 = col0 < tl.rows_b, c_ok1 = col0 + 32 < tl.rows_b;
+#pragma unroll
+  for (int i = 0; i < TM; i++) {
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int row = row0 + i * 32 + 8 * q + r;
+        if (row < tl.rows_a) {
+          if (c_ok0) p[0] = acc[i][0][q * 4 + r];
+          if (c_ok1) p[32] = acc[i][1][q * 4 + r];
+        }
+        // next row of this lane: +1 within a run of 4, else +5 (27 -> 32 too)
+        p += (r < 3 ? 1 : 5) * ldo;
+        asm volatile("" : "+v"(p));
+      }
+    }
+  }
+}
+
+// Ragged M runs persistent: one workgroup per CU walks its tiles (see
+// tile_id), and a tile's last stage loads the next tile's first, so the
+// pipeline does not drain between tiles and the output stores of one tile
+// drain while the next one computes.  Dense and ragged K are launched with
+// one workgroup per tile (measured faster for dense; ragged-K tiles differ in
+// length, so the hardware's dynamic dispatch balances them better).
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, const uint8_t* __restrict__ B,
@@ -258,77 +306,127 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   const int bid = blockIdx.x;
-
-  // ---- which output tile, and the operands behind it
-  int64_t m0, n0 = 0, k_begin = 0, k_end = K;
-  int rows_a;
-  const uint8_t *b_base = B, *sb_base = sB;
-  float* c_base = C;
   const int64_t lda = K;
+  const int64_t ldo = MODE == kRaggedK ? N : ldc;
+
+  // ---- the tile list
+  int n_tiles;
+  const GroupTable* gtp = nullptr;  // ragged M and K: group starts, sizes, 32- or 256-row block starts
+  const int32_t* orderp = nullptr;  // ragged K: groups, largest first
   if constexpr (MODE == kDense) {
-    int mt, nt;
-    raster(xcd_remap(bid, gridDim.x), tiles_m, tiles_n, mt, nt);
-    m0 = (int64_t)mt * BM;
-    n0 = (int64_t)nt * BN;
-    rows_a = (int)min<int64_t>(BM, M - m0);
+    n_tiles = tiles_m * tiles_n;
+  } else if constexpr (MODE == kRaggedM) {
+    __shared__ GroupTable gt;  // read by every tile of the workgroup
+    build_group_table<kThreads>(group_end, G, M, BM, gt, reinterpret_cast<GroupScratch*>(stage1)->scan_tmp);
+    n_tiles = gt.bstart[G] * tiles_n;  // real m-tiles x n-tiles
+    gtp = &gt;
   } else {
+    // one tile per workgroup: the table and the order live in stage 1, which
+    // is read before the first load
     GroupScratch& gs = *reinterpret_cast<GroupScratch*>(stage1);
     GroupTable& gt = gs.gt;
-    int32_t* const scan_tmp = gs.scan_tmp;
-    if constexpr (MODE == kRaggedM) {
-      build_group_table<kThreads>(group_end, G, M, BM, gt, scan_tmp);
-      // the grid covers an upper bound of m-tiles; the real ones are bstart[G]
-      const int real_m = gt.bstart[G];
-      const int n_real = real_m * tiles_n;
-      if (bid >= n_real) return;  // uniform
-      int mt, nt;
-      raster(xcd_remap(bid, n_real), real_m, tiles_n, mt, nt);
-      const int g = find_group(gt, G, mt);
-      const int local = mt - gt.bstart[g];
-      m0 = (int64_t)gt.start[g] + (int64_t)local * BM;
-      n0 = (int64_t)nt * BN;
-      rows_a = min(BM, gt.size[g] - local * BM);
-      b_base = B + (int64_t)g * N * K;
-      sb_base = sB + (int64_t)g * ((N + 31) / 32 * 32) * (K / 32);  // expert scale arrays hold ceil32(N) rows
-    } else {
-      build_group_table<kThreads>(group_end, G, (int64_t)1 << 40, 32, gt, scan_tmp);
-      // largest groups first (their tiles carry the longest K loops)
-      int32_t* const order = gs.order;
-      for (int g = t; g < G; g += kThreads) {
-        const int32_t sz = gt.size[g];
-        int rank = 0;
-        for (int h = 0; h < G; h++) {
-          const int32_t sh = gt.size[h];
-          rank += (sh > sz) || (sh == sz && h < g);
-        }
-        order[rank] = g;
+    build_group_table<kThreads>(group_end, G, (int64_t)1 << 40, 32, gt, gs.scan_tmp);
+    // largest groups first (their tiles carry the longest K loops)
+    for (int g = t; g < G; g += kThreads) {
+      const int32_t sz = gt.size[g];
+      int rank = 0;
+      for (int h = 0; h < G; h++) {
+        const int32_t sh = gt.size[h];
+        rank += (sh > sz) || (sh == sz && h < g);
       }
-      __syncthreads();
-      // groups are taken largest first; inside a group's run of workgroups the
-      // XCD remap gives every XCD an equal, contiguous share of that group's
-      // tiles (balanced across XCDs, and each XCD's concurrent tiles share
-      // operand panels in its L2)
-      const int per_g = tiles_m * tiles_n;
-      const int gi = bid / per_g;
-      const int g = order[gi];
-      int mt, nt;
-      raster(xcd_remap(bid - gi * per_g, per_g), tiles_m, tiles_n, mt, nt);
-      m0 = (int64_t)mt * BM;
-      n0 = (int64_t)nt * BN;
-      rows_a = (int)min<int64_t>(BM, M - m0);
-      k_begin = (int64_t)gt.bstart[g] * 32;
-      k_end = min<int64_t>((int64_t)gt.bstart[g + 1] * 32, K);  // never past the row length
-      if (k_end < k_begin) k_end = k_begin;
-      c_base = C + (int64_t)g * M * N;
+      gs.order[rank] = g;
     }
+    __syncthreads();
+    orderp = gs.order;
+    n_tiles = G * tiles_m * tiles_n;
+    gtp = &gt;
   }
-  const int rows_b = (int)min<int64_t>(BN, N - n0);
-  if constexpr (MODE != kDense) __syncthreads();  // group scratch read; stage 1 may now be loaded
 
-  const Operand opa{A + m0 * lda, sA, m0, lda, rows_a};
-  const Operand opb{b_base + n0 * lda, sb_base, n0, lda, rows_b};
-  const OperandAddr ada = make_addr(opa, wave, lane);
-  const OperandAddr adb = make_addr(opb, wave, lane);
+  const int P = gridDim.x;
+  // Logical tile of round r for this workgroup, or -1.  Workgroups are dealt
+  // to the XCDs round robin (XCD = bid % 8).
+  //  - dense and ragged K are launched with one workgroup per tile (round 0
+  //    only); dense gives XCD x the contiguous range [x * per, (x + 1) * per)
+  //    of the raster, so the tiles an XCD runs at once share operand panels
+  //    in its L2 (ragged K remaps inside each group, in make_tile);
+  //  - ragged M runs persistent with all XCDs in lockstep: round r covers the
+  //    tiles [r * P, (r + 1) * P), XCD x its slice [x * P/8, (x + 1) * P/8),
+  //    so every XCD works on the same experts at once and their weight panels
+  //    are shared in the Infinity Cache.
+  auto tile_id = [&](int r) -> int {
+    if constexpr (MODE == kRaggedK) {
+      return r == 0 && bid < n_tiles ? bid : -1;
+    } else if constexpr (MODE == kDense) {
+      return r == 0 ? xcd_remap(bid, n_tiles) : -1;
+    } else {
+      const int base = r * P;
+      if (base >= n_tiles) return -1;
+      const int id = base + P <= n_tiles ? base + xcd_remap(bid, P) : base + bid;
+      return id < n_tiles ? id : -1;
+    }
+  };
+  auto make_tile = [&](int id) {
+    Tile tl;
+    tl.k_begin = 0;
+    tl.klen = K;
+    tl.b_base = B;
+    tl.sb_base = sB;
+    tl.c_base = C;
+    int mt, nt;
+    if constexpr (MODE == kDense) {
+      raster(id, tiles_m, tiles_n, mt, nt);
+      tl.m0 = (int64_t)mt * BM;
+      tl.rows_a = (int)min<int64_t>(BM, M - tl.m0);
+    } else if constexpr (MODE == kRaggedM) {
+      raster(id, n_tiles / tiles_n, tiles_n, mt, nt);
+      const int g = __builtin_amdgcn_readfirstlane(find_group(*gtp, G, mt));
+      const int local = mt - __builtin_amdgcn_readfirstlane(gtp->bstart[g]);
+      tl.m0 = (int64_t)__builtin_amdgcn_readfirstlane(gtp->start[g]) + (int64_t)local * BM;
+      tl.rows_a = min(BM, __builtin_amdgcn_readfirstlane(gtp->size[g]) - local * BM);
+      tl.b_base = B + (int64_t)g * N * K;
+      tl.sb_base = sB + (int64_t)g * ((N + 31) / 32 * 32) * (K / 32);  // expert scale arrays hold ceil32(N) rows
+    } else {
+      // groups largest first; inside a group's run of workgroups the XCD remap
+      // gives every XCD an equal, contiguous share of that group's tiles
+      const int per_g = tiles_m * tiles_n;
+      const int gi = id / per_g;
+      const int g = __builtin_amdgcn_readfirstlane(orderp[gi]);
+      raster(xcd_remap(id - gi * per_g, per_g), tiles_m, tiles_n, mt, nt);
+      tl.m0 = (int64_t)mt * BM;
+      tl.rows_a = (int)min<int64_t>(BM, M - tl.m0);
+      tl.k_begin = (int64_t)__builtin_amdgcn_readfirstlane(gtp->bstart[g]) * 32;
+      // never past the row length
+      const int64_t k_end = min<int64_t>((int64_t)__builtin_amdgcn_readfirstlane(gtp->bstart[g + 1]) * 32, K);
+      tl.klen = k_end > tl.k_begin ? k_end - tl.k_begin : 0;
+      tl.c_base = C + (int64_t)g * M * N;
+    }
+    tl.n0 = (int64_t)nt * BN;
+    tl.rows_b = (int)min<int64_t>(BN, N - tl.n0);
+    const int ns = (int)((tl.klen + BKS - 1) / BKS);
+    tl.nst = (ns + 1) & ~1;
+    tl.last = ns - 1;
+    tl.tail_chunks = ns > 0 ? (int)(tl.klen - (int64_t)tl.last * BKS) / 16 : 8;
+    return tl;
+  };
+  OperandAddr ada, adb;
+  auto addr_of = [&](const Tile& tl) {
+    const Operand opa{A + tl.m0 * lda, sA, tl.m0, lda, tl.rows_a};
+    const Operand opb{tl.b_base + tl.n0 * lda, tl.sb_base, tl.n0, lda, tl.rows_b};
+    ada = make_addr(opa, wave, lane);
+    adb = make_addr(opb, wave, lane);
+  };
+  // ragged K (one tile per workgroup) reads its tile from the scratch in
+  // stage 1: do that before any load
+  const int id0 = tile_id(0);
+  Tile first{};
+  if constexpr (MODE == kRaggedK) {
+    if (id0 >= 0) first = make_tile(id0);
+  }
+  auto tile_of = [&](int id) {
+    if constexpr (MODE == kRaggedK) return first;
+    else return make_tile(id);
+  };
+  if constexpr (MODE != kDense) __syncthreads();  // group scratch read; stage 1 may now be loaded
 
   v16f acc[TM][TN];
 #pragma unroll
@@ -338,30 +436,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
 #pragma unroll
       for (int e = 0; e < 16; e++) acc[i][j][e] = 0.f;
 
-  // stages of two steps: ns stages, the last holding tail_chunks 16-byte
-  // chunks per row (2, 4, 6 or 8; K is a multiple of 32)
-  const int64_t klen = k_end - k_begin;
-  const int ns = (int)((klen + BKS - 1) / BKS);
-  const int last = ns - 1;
-  const int tail_chunks = ns > 0 ? (int)(klen - (int64_t)last * BKS) / 16 : 8;
   uint8_t* const stages[2] = {stage0, stage1};
-
-  // issue stage s into LDS stage `slot`; stages past the last re-load the last
-  // one (every stage issues the same loads, so the vmcnt arithmetic is fixed)
-  auto issue = [&](int slot, int s) {
-    const int sc = min(s, last);
-    const int64_t k = k_begin + (int64_t)sc * BKS;
-    const int vc = sc == last ? tail_chunks : 8;
+  // issue stage s of tile `tl` into LDS stage `slot`; stages past its last
+  // re-load the last one (every stage issues the same loads)
+  auto issue = [&](int slot, const Tile& tl, int s) {
+    const int sc = min(s, tl.last);
+    const int64_t k = tl.k_begin + (int64_t)sc * BKS;
+    const int vc = sc == tl.last ? tl.tail_chunks : 8;
     uint8_t* st = stages[slot];
     issue_codes(ada, st, wave, lane, k, vc);
     issue_codes(adb, st + kTileBytes, wave, lane, k, vc);
     issue_scales(ada, st + 2 * kTileBytes, wave, k, vc / 2);
     issue_scales(adb, st + 2 * kTileBytes + kScaleRegion, wave, k, vc / 2);
   };
-  // once stage s has landed in `slot` (this wave's part): zero the chunks past
-  // the end of K, or all of it if it only pads the loop to an even count
-  auto fix = [&](int slot, int s) {
-    const int vc = s > last ? 0 : s == last ? tail_chunks : 8;
+  // once stage s of `tl` has landed in `slot` (this wave's part): zero the
+  // chunks past the end of K, or all of it if it only pads the loop
+  auto fix = [&](int slot, const Tile& tl, int s) {
+    const int vc = s > tl.last ? 0 : s == tl.last ? tl.tail_chunks : 8;
     if (vc < 8) {
       zero_codes(stages[slot], wave, lane, vc);
       zero_codes(stages[slot] + kTileBytes, wave, lane, vc);
@@ -373,64 +464,89 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
 #pragma unroll
       for (int j = 0; j < TN; j++) asm volatile("" : "+a"(acc[i][j]));
   };
-
-  if (ns > 0) {
-    const int nstages = (ns + 1) & ~1;  // the loop covers both LDS stages per trip
-    issue(0, 0);
-    wait_vmcnt<0>();  // stage 0 landed
-    fix(0, 0);
+  Frags f;
+  // The two steps of a stage in LDS stage `cur` (published by the last
+  // barrier).  Each wave reads a step's fragments and runs its 8 MFMAs as
+  // soon as they arrive (the compiler waits per fragment); the other wave on
+  // the SIMD keeps the matrix pipe busy meanwhile.  The loads of the stage
+  // that follows (tile nt, stage ns) go out right after step 0's fragment
+  // reads, into the other LDS stage (every wave finished reading it before
+  // the last barrier), and have the two steps to land.
+  auto stage_steps = [&](int cur, const Tile& nt, int ns) {
+    // step 0
+    read_frags(stages[cur], 0, wm, wn, lane, f);
+    issue(cur ^ 1, nt, ns);
+    mfma_step(acc, f);
+    pin();
+    __builtin_amdgcn_sched_barrier(0);
+    // step 1
+    read_frags(stages[cur], 1, wm, wn, lane, f);
+    mfma_step(acc, f);
+    pin();
+    __builtin_amdgcn_sched_barrier(0);
+    // publish the following stage; after the barrier every wave is done reading `cur`
+    wait_vmcnt<0>();  // this wave's loads of the following stage landed
+    fix(cur ^ 1, nt, ns);
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
-    Frags f;
-    // The two steps of stage s (in LDS stage `cur`, published by the last
-    // barrier).  Each wave reads a step's fragments and runs its 8 MFMAs as
-    // soon as they arrive (the compiler waits per fragment); the other wave
-    // on the SIMD keeps the matrix pipe busy meanwhile.  The loads of stage
-    // s+1 go out right after step 0's fragment reads, into the other LDS
-    // stage (every wave finished reading it before the last barrier), and
-    // have the two steps to land.
-    auto stage_steps = [&](int cur, int s) {
-      // step 0
-      read_frags(stages[cur], 0, wm, wn, lane, f);
-      issue(cur ^ 1, s + 1);
-      mfma_step(acc, f);
-      pin();
-      __builtin_amdgcn_sched_barrier(0);
-      // step 1
-      read_frags(stages[cur], 1, wm, wn, lane, f);
-      mfma_step(acc, f);
-      pin();
-      __builtin_amdgcn_sched_barrier(0);
-      // publish stage s+1; after the barrier every wave is done reading `cur`
-      wait_vmcnt<0>();  // this wave's loads of stage s+1 landed
-      fix(cur ^ 1, s + 1);
-      wait_lgkmcnt0();
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    for (int s = 0; s < nstages; s += 2) {
-      stage_steps(0, s);
-      stage_steps(1, s + 1);
-    }
-    wait_vmcnt<0>();  // the loads still in flight land before the LDS goes away
-  }
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-  // ---- epilogue: fp32 stores (32 consecutive floats per half-wave), rows/cols
-  // past the tile's valid range skipped
-  const int64_t ldo = MODE == kRaggedK ? N : ldc;
-#pragma unroll
-  for (int i = 0; i < TM; i++) {
-#pragma unroll
-    for (int j = 0; j < TN; j++) {
-      const int col = wn * WN + j * 32 + (lane & 31);
-      if (col >= rows_b) continue;
-#pragma unroll
-      for (int e = 0; e < 16; e++) {
-        const int row = wm * WM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        if (row < rows_a) c_base[(m0 + row) * ldo + n0 + col] = acc[i][j][e];
+  int r = 0;
+  int id = id0;
+  bool ready = false;  // the current tile's stage 0 is loaded and published
+  while (id >= 0) {
+    const int nid = MODE == kRaggedM ? tile_id(r + 1) : -1;  // (one tile per workgroup otherwise)
+    bool nxt_ok = false;
+    {
+      const Tile cur = tile_of(id);
+      if (cur.nst > 0) {  // (an empty expert's tile only stores zeros)
+        if (!ready) {
+          wait_vmcnt<0>();  // loads of an earlier pass into the stages have landed
+          __builtin_amdgcn_s_barrier();
+          addr_of(cur);
+          issue(0, cur, 0);
+          wait_vmcnt<0>();  // stage 0 landed
+          fix(0, cur, 0);
+          wait_lgkmcnt0();
+          __builtin_amdgcn_s_barrier();
+        }
+        for (int s = 0; s < cur.nst - 2; s += 2) {
+          stage_steps(0, cur, s + 1);
+          stage_steps(1, cur, s + 2);
+        }
+        stage_steps(0, cur, cur.nst - 1);
+        // the last stage loads the next tile's first (or, with no next tile,
+        // re-loads this tile's last stage, which nobody reads)
+        Tile nxt = cur;
+        int ns = cur.nst;
+        if (nid >= 0) {
+          const Tile t2 = tile_of(nid);
+          if (t2.nst > 0) {
+            nxt = t2;
+            ns = 0;
+            nxt_ok = true;
+            addr_of(nxt);
+          }
+        }
+        stage_steps(1, nxt, ns);
       }
     }
+    {
+      const Tile cur = tile_of(id);  // (recomputed: keeps it out of registers during the K loop)
+      store_tile(acc, cur, ldo, wm, wn, lane);
+    }
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+      for (int j = 0; j < TN; j++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) acc[i][j][e] = 0.f;
+    ready = nxt_ok;
+    id = nid;
+    r++;
   }
+  wait_vmcnt<0>();  // the loads still in flight land before the LDS goes away
 }
 
 }  // namespace
@@ -438,26 +554,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
 hipError_t launch_gemm(int mode, const uint8_t* A, const uint8_t* sA, const uint8_t* B,
                        const uint8_t* sB, float* C, int64_t M, int64_t N, int64_t K, int64_t ldc,
                        const int32_t* group_end, int32_t G, hipStream_t st) {
-  const int tiles_n = (int)((N + BN - 1) / BN);
+  // 32-bit per-lane load offsets: 256 rows of codes of one tile
+  if ((int64_t)BM * K >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const int64_t tiles_n = (N + BN - 1) / BN;
+  const int64_t tiles_m = (M + BM - 1) / BM;
+  const int64_t cus = device_cu_count();
   if (mode == kDense) {
-    const int tiles_m = (int)((M + BM - 1) / BM);
-    const int64_t grid = (int64_t)tiles_m * tiles_n;
-    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-    gemm_mxfp8_kernel<kDense><<<(unsigned)grid, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, ldc,
-                                                                    nullptr, 1, tiles_m, tiles_n);
+    const int64_t total = tiles_m * tiles_n;  // one workgroup per tile
+    if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const int64_t grid = total;
+    gemm_mxfp8_kernel<kDense><<<(unsigned)grid, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, ldc, nullptr, 1,
+                                                                    (int)tiles_m, (int)tiles_n);
   } else if (mode == kRaggedM) {
-    // every group adds at most one partial tile
-    const int tiles_m = (int)((M + BM - 1) / BM + G);
-    const int64_t grid = (int64_t)tiles_m * tiles_n;
-    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+    // every group adds at most one partial m-tile: an upper bound of the tiles
+    const int64_t total = (tiles_m + G) * tiles_n;
+    if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const int64_t grid = total < cus ? total : cus;
     gemm_mxfp8_kernel<kRaggedM><<<(unsigned)grid, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, ldc,
-                                                                      group_end, G, tiles_m, tiles_n);
+                                                                      group_end, G, (int)tiles_m, (int)tiles_n);
   } else {
-    const int tiles_m = (int)((M + BM - 1) / BM);
-    const int64_t grid = (int64_t)G * tiles_m * tiles_n;
-    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-    gemm_mxfp8_kernel<kRaggedK><<<(unsigned)grid, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, N,
-                                                                      group_end, G, tiles_m, tiles_n);
+    const int64_t total = (int64_t)G * tiles_m * tiles_n;  // one workgroup per tile
+    if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
+    gemm_mxfp8_kernel<kRaggedK><<<(unsigned)total, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, N,
+                                                                       group_end, G, (int)tiles_m, (int)tiles_n);
   }
   return hipGetLastError();
 }
