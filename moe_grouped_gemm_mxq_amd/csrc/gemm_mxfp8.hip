@@ -288,12 +288,11 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[TM][TN], const Tile
   }
 }
 
-// Ragged M runs persistent: one workgroup per CU walks its tiles (see
+// The grouped modes run persistent: one workgroup per CU walks its tiles (see
 // tile_id), and a tile's last stage loads the next tile's first, so the
 // pipeline does not drain between tiles and the output stores of one tile
-// drain while the next one computes.  Dense and ragged K are launched with
-// one workgroup per tile (measured faster for dense; ragged-K tiles differ in
-// length, so the hardware's dynamic dispatch balances them better).
+// drain while the next one computes.  Dense is launched with one workgroup
+// per tile (measured faster).
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, const uint8_t* __restrict__ B,
@@ -311,7 +310,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
 
   // ---- the tile list
   int n_tiles;
-  const GroupTable* gtp = nullptr;  // ragged M and K: group starts, sizes, 32- or 256-row block starts
+  const GroupTable* gtp = nullptr;  // ragged M: group starts, sizes, m-tile starts
+  const int32_t* kbp = nullptr;     // ragged K: padded 32-token block starts per group (G + 1)
   const int32_t* orderp = nullptr;  // ragged K: groups, largest first
   if constexpr (MODE == kDense) {
     n_tiles = tiles_m * tiles_n;
@@ -321,11 +321,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
     n_tiles = gt.bstart[G] * tiles_n;  // real m-tiles x n-tiles
     gtp = &gt;
   } else {
-    // one tile per workgroup: the table and the order live in stage 1, which
-    // is read before the first load
+    // the table is built in stage 1 (free until the first load); the tile
+    // walk keeps only the block starts and the order
+    __shared__ int32_t kb[kMaxGroups + 1];
+    __shared__ int32_t order[kMaxGroups];
     GroupScratch& gs = *reinterpret_cast<GroupScratch*>(stage1);
     GroupTable& gt = gs.gt;
     build_group_table<kThreads>(group_end, G, (int64_t)1 << 40, 32, gt, gs.scan_tmp);
+    for (int g = t; g <= G; g += kThreads) kb[g] = gt.bstart[g];
     // largest groups first (their tiles carry the longest K loops)
     for (int g = t; g < G; g += kThreads) {
       const int32_t sz = gt.size[g];
@@ -334,29 +337,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
         const int32_t sh = gt.size[h];
         rank += (sh > sz) || (sh == sz && h < g);
       }
-      gs.order[rank] = g;
+      order[rank] = g;
     }
-    __syncthreads();
-    orderp = gs.order;
+    kbp = kb;
+    orderp = order;
     n_tiles = G * tiles_m * tiles_n;
-    gtp = &gt;
   }
 
   const int P = gridDim.x;
   // Logical tile of round r for this workgroup, or -1.  Workgroups are dealt
   // to the XCDs round robin (XCD = bid % 8).
-  //  - dense and ragged K are launched with one workgroup per tile (round 0
-  //    only); dense gives XCD x the contiguous range [x * per, (x + 1) * per)
-  //    of the raster, so the tiles an XCD runs at once share operand panels
-  //    in its L2 (ragged K remaps inside each group, in make_tile);
-  //  - ragged M runs persistent with all XCDs in lockstep: round r covers the
-  //    tiles [r * P, (r + 1) * P), XCD x its slice [x * P/8, (x + 1) * P/8),
-  //    so every XCD works on the same experts at once and their weight panels
-  //    are shared in the Infinity Cache.
+  //  - dense is launched with one workgroup per tile (round 0 only) and gives
+  //    XCD x the contiguous range [x * per, (x + 1) * per) of the raster, so
+  //    the tiles an XCD runs at once share operand panels in its L2;
+  //  - the grouped modes run persistent with all XCDs in lockstep: round r
+  //    covers the tiles [r * P, (r + 1) * P), XCD x its slice
+  //    [x * P/8, (x + 1) * P/8), so every XCD works on the same experts at
+  //    once and their panels are shared in the Infinity Cache.  Ragged-K
+  //    tiles come largest group first, so the round-robin walk gives every
+  //    workgroup a similar share of long and short tiles.
   auto tile_id = [&](int r) -> int {
-    if constexpr (MODE == kRaggedK) {
-      return r == 0 && bid < n_tiles ? bid : -1;
-    } else if constexpr (MODE == kDense) {
+    if constexpr (MODE == kDense) {
       return r == 0 ? xcd_remap(bid, n_tiles) : -1;
     } else {
       const int base = r * P;
@@ -386,17 +387,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
       tl.b_base = B + (int64_t)g * N * K;
       tl.sb_base = sB + (int64_t)g * ((N + 31) / 32 * 32) * (K / 32);  // expert scale arrays hold ceil32(N) rows
     } else {
-      // groups largest first; inside a group's run of workgroups the XCD remap
-      // gives every XCD an equal, contiguous share of that group's tiles
       const int per_g = tiles_m * tiles_n;
       const int gi = id / per_g;
       const int g = __builtin_amdgcn_readfirstlane(orderp[gi]);
-      raster(xcd_remap(id - gi * per_g, per_g), tiles_m, tiles_n, mt, nt);
+      raster(id - gi * per_g, tiles_m, tiles_n, mt, nt);
       tl.m0 = (int64_t)mt * BM;
       tl.rows_a = (int)min<int64_t>(BM, M - tl.m0);
-      tl.k_begin = (int64_t)__builtin_amdgcn_readfirstlane(gtp->bstart[g]) * 32;
+      tl.k_begin = (int64_t)__builtin_amdgcn_readfirstlane(kbp[g]) * 32;
       // never past the row length
-      const int64_t k_end = min<int64_t>((int64_t)__builtin_amdgcn_readfirstlane(gtp->bstart[g + 1]) * 32, K);
+      const int64_t k_end = min<int64_t>((int64_t)__builtin_amdgcn_readfirstlane(kbp[g + 1]) * 32, K);
       tl.klen = k_end > tl.k_begin ? k_end - tl.k_begin : 0;
       tl.c_base = C + (int64_t)g * M * N;
     }
@@ -415,18 +414,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
     ada = make_addr(opa, wave, lane);
     adb = make_addr(opb, wave, lane);
   };
-  // ragged K (one tile per workgroup) reads its tile from the scratch in
-  // stage 1: do that before any load
   const int id0 = tile_id(0);
-  Tile first{};
-  if constexpr (MODE == kRaggedK) {
-    if (id0 >= 0) first = make_tile(id0);
-  }
-  auto tile_of = [&](int id) {
-    if constexpr (MODE == kRaggedK) return first;
-    else return make_tile(id);
-  };
-  if constexpr (MODE != kDense) __syncthreads();  // group scratch read; stage 1 may now be loaded
+  auto tile_of = [&](int id) { return make_tile(id); };
+  if constexpr (MODE != kDense) __syncthreads();  // group tables ready; stage 1 may now be loaded
 
   v16f acc[TM][TN];
 #pragma unroll
@@ -496,7 +486,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
   int id = id0;
   bool ready = false;  // the current tile's stage 0 is loaded and published
   while (id >= 0) {
-    const int nid = MODE == kRaggedM ? tile_id(r + 1) : -1;  // (one tile per workgroup otherwise)
+    const int nid = MODE != kDense ? tile_id(r + 1) : -1;  // (dense: one tile per workgroup)
     bool nxt_ok = false;
     {
       const Tile cur = tile_of(id);
@@ -573,10 +563,11 @@ hipError_t launch_gemm(int mode, const uint8_t* A, const uint8_t* sA, const uint
     gemm_mxfp8_kernel<kRaggedM><<<(unsigned)grid, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, ldc,
                                                                       group_end, G, (int)tiles_m, (int)tiles_n);
   } else {
-    const int64_t total = (int64_t)G * tiles_m * tiles_n;  // one workgroup per tile
+    const int64_t total = (int64_t)G * tiles_m * tiles_n;
     if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-    gemm_mxfp8_kernel<kRaggedK><<<(unsigned)total, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, N,
-                                                                       group_end, G, (int)tiles_m, (int)tiles_n);
+    const int64_t grid = total < cus ? total : cus;
+    gemm_mxfp8_kernel<kRaggedK><<<(unsigned)grid, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, N,
+                                                                      group_end, G, (int)tiles_m, (int)tiles_n);
   }
   return hipGetLastError();
 }
