@@ -22,14 +22,34 @@ constexpr int kThreads = 256;
 // ------------------------------------------------------------------ row copy
 // A row is Cp/8 chunks of 8 bf16 (16 bytes); four consecutive lanes hold one
 // block.  `tpr` (threads per row, a power of two >= 4) lanes share a row and
-// 256/tpr rows are processed per step, so no division is needed.
+// 256/tpr rows are processed per step, so no division is needed.  A lane
+// takes up to kRowUnroll chunks of its row at once and issues all their loads
+// before any arithmetic, so enough bytes are in flight to cover the HBM
+// latency.
+constexpr int kRowUnroll = 4;
+
+template <bool VEC>
+__device__ __forceinline__ void load_chunk(const uint16_t* xr, int64_t col, int64_t C, uint32_t (&w)[4]) {
+  if (VEC && col + 8 <= C) {
+    const uint4 v = *reinterpret_cast<const uint4*>(xr + col);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const uint32_t lo = col + 2 * j < C ? xr[col + 2 * j] : 0u;
+      const uint32_t hi = col + 2 * j + 1 < C ? xr[col + 2 * j + 1] : 0u;
+      w[j] = lo | (hi << 16);
+    }
+  }
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void quant_row_kernel(const uint16_t* __restrict__ x, int64_t R,
                                                             int64_t C, int64_t ldx, int tpr_log2,
                                                             uint8_t* __restrict__ q,
                                                             uint8_t* __restrict__ s) {
   const int64_t Cp = (C + 31) / 32 * 32;
-  const int cpr = (int)(Cp / 8);  // chunks per row
+  const int cpr = (int)(Cp / 8);  // chunks per row (a multiple of 4)
   const int tpr = 1 << tpr_log2;
   const int rps = kThreads >> tpr_log2;  // rows per step
   const int t = threadIdx.x;
@@ -37,30 +57,45 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(const uint16_t* __r
     const int64_t row = row0 + (t >> tpr_log2);
     const bool row_ok = row < R;  // uniform per quad
     const uint16_t* xr = x + (row_ok ? row : 0) * ldx;
-    for (int c8 = t & (tpr - 1); c8 < cpr; c8 += tpr) {
-      const int64_t col = (int64_t)c8 * 8;
-      uint32_t w[4];
-      if (VEC && col + 8 <= C) {
-        uint4 v = *reinterpret_cast<const uint4*>(xr + col);
-        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    for (int c0 = t & (tpr - 1); c0 < cpr; c0 += kRowUnroll * tpr) {
+      // (c < cpr is uniform per quad: cpr and tpr are multiples of 4)
+      uint32_t w[kRowUnroll][4];
+      if (VEC && C % 8 == 0) {
+        // unconditional 16-byte loads from clamped columns (chunks past C are
+        // zeroed), so the loads issue back to back with no wait between them
+#pragma unroll
+        for (int u = 0; u < kRowUnroll; u++) {
+          const int64_t col = (int64_t)(c0 + u * tpr) * 8;
+          const uint4 v = *reinterpret_cast<const uint4*>(xr + min(col, C - 8));
+          const bool ok = col < C;
+          w[u][0] = ok ? v.x : 0u;
+          w[u][1] = ok ? v.y : 0u;
+          w[u][2] = ok ? v.z : 0u;
+          w[u][3] = ok ? v.w : 0u;
+        }
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          uint32_t lo = col + 2 * j < C ? xr[col + 2 * j] : 0u;
-          uint32_t hi = col + 2 * j + 1 < C ? xr[col + 2 * j + 1] : 0u;
-          w[j] = lo | (hi << 16);
+        for (int u = 0; u < kRowUnroll; u++) {
+          const int c8 = c0 + u * tpr;
+          if (c8 < cpr) load_chunk<VEC>(xr, (int64_t)c8 * 8, C, w[u]);
         }
       }
-      uint32_t m = hmax_u16x2(pkmax_u16(absmax_bf16x2(w[0], w[1]), absmax_bf16x2(w[2], w[3])));
-      m = quad_max_u32(m);
-      const uint32_t byte = mxfp8_scale_byte(m);
-      const float sc = e8m0_as_scale(byte);
-      uint2 codes;
-      codes.x = e4m3_encode4(w[0], w[1], sc);
-      codes.y = e4m3_encode4(w[2], w[3], sc);
-      if (row_ok) {
-        *reinterpret_cast<uint2*>(q + row * Cp + col) = codes;
-        if ((c8 & 3) == 0) s[scale_offset(row, c8 / 4, Cp / 32)] = (uint8_t)byte;
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; u++) {
+        const int c8 = c0 + u * tpr;
+        if (c8 >= cpr) break;
+        const int64_t col = (int64_t)c8 * 8;
+        uint32_t m = hmax_u16x2(pkmax_u16(absmax_bf16x2(w[u][0], w[u][1]), absmax_bf16x2(w[u][2], w[u][3])));
+        m = quad_max_u32(m);
+        const uint32_t byte = mxfp8_scale_byte(m);
+        const float sc = e8m0_as_scale(byte);
+        uint2 codes;
+        codes.x = e4m3_encode4(w[u][0], w[u][1], sc);
+        codes.y = e4m3_encode4(w[u][2], w[u][3], sc);
+        if (row_ok) {
+          *reinterpret_cast<uint2*>(q + row * Cp + col) = codes;
+          if ((c8 & 3) == 0) s[scale_offset(row, c8 / 4, Cp / 32)] = (uint8_t)byte;
+        }
       }
     }
   }
@@ -117,45 +152,58 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
   if (rb_valid[0] <= 0) return;  // tile lies past the last block (uniform)
 
   const int64_t Cp = (C + 31) / 32 * 32;
-  // ---- phase 1: load (+ row copy), stage in LDS
+  // ---- phase 1: load (+ row copy), stage in LDS.  All eight loads of a
+  // thread are issued before any arithmetic, so they are in flight together.
+  const int c16 = t & 15;
+  const int64_t col1 = c0 + c16 * 8;
+  uint32_t w[8][4];
+  if (VEC && c0 + kTC <= C) {
+    // no column tail in this tile: unconditional 16-byte loads (rows past the
+    // valid range read the tile's first row, always valid, and are zeroed),
+    // so the eight loads issue back to back with no wait between them
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int lr = (t >> 4) + 16 * i;  // tile row
+      const int rb = lr >> 5;
+      const bool row_ok = (lr & 31) < rb_valid[rb];
+      const int64_t src = row_ok ? rb_src[rb] + (lr & 31) : rb_src[0];
+      const uint4 v = *reinterpret_cast<const uint4*>(x + src * ldx + col1);
+      w[i][0] = row_ok ? v.x : 0u;
+      w[i][1] = row_ok ? v.y : 0u;
+      w[i][2] = row_ok ? v.z : 0u;
+      w[i][3] = row_ok ? v.w : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int lr = (t >> 4) + 16 * i;
+      const int rb = lr >> 5;
+      const bool row_ok = (lr & 31) < rb_valid[rb];
+      const int64_t src = rb_src[rb] + (lr & 31);
+      w[i][0] = w[i][1] = w[i][2] = w[i][3] = 0u;
+      if (row_ok) load_chunk<VEC>(x + src * ldx, col1, C, w[i]);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    const int lr = (t >> 4) + 16 * i;  // tile row
-    const int c16 = t & 15;
-    const int rb = lr >> 5;
-    const int32_t valid = rb_valid[rb];
-    const bool row_ok = (lr & 31) < valid;
-    const int64_t src = rb_src[rb] + (lr & 31);
-    const int64_t col = c0 + c16 * 8;
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (row_ok) {
-      const uint16_t* xr = x + src * ldx;
-      if (VEC && col + 8 <= C) {
-        uint4 v = *reinterpret_cast<const uint4*>(xr + col);
-        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          uint32_t lo = col + 2 * j < C ? xr[col + 2 * j] : 0u;
-          uint32_t hi = col + 2 * j + 1 < C ? xr[col + 2 * j + 1] : 0u;
-          w[j] = lo | (hi << 16);
-        }
-      }
-    }
+    const int lr = (t >> 4) + 16 * i;
     if constexpr (ROW) {
-      uint32_t m = hmax_u16x2(pkmax_u16(absmax_bf16x2(w[0], w[1]), absmax_bf16x2(w[2], w[3])));
+      const int rb = lr >> 5;
+      const bool row_ok = (lr & 31) < rb_valid[rb];
+      const int64_t src = rb_src[rb] + (lr & 31);
+      uint32_t m = hmax_u16x2(pkmax_u16(absmax_bf16x2(w[i][0], w[i][1]), absmax_bf16x2(w[i][2], w[i][3])));
       m = quad_max_u32(m);
       const uint32_t byte = mxfp8_scale_byte(m);
       const float sc = e8m0_as_scale(byte);
       uint2 codes;
-      codes.x = e4m3_encode4(w[0], w[1], sc);
-      codes.y = e4m3_encode4(w[2], w[3], sc);
-      if (row_ok && col < Cp) {
-        *reinterpret_cast<uint2*>(q_row + src * Cp + col) = codes;
-        if ((c16 & 3) == 0) s_row[scale_offset(src, col / 32, Cp / 32)] = (uint8_t)byte;
+      codes.x = e4m3_encode4(w[i][0], w[i][1], sc);
+      codes.y = e4m3_encode4(w[i][2], w[i][3], sc);
+      if (row_ok && col1 < Cp) {
+        *reinterpret_cast<uint2*>(q_row + src * Cp + col1) = codes;
+        if ((c16 & 3) == 0) s_row[scale_offset(src, col1 / 32, Cp / 32)] = (uint8_t)byte;
       }
     }
-    *reinterpret_cast<uint4*>(tile + lr * kLdsStride + c16 * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(tile + lr * kLdsStride + c16 * 16) = make_uint4(w[i][0], w[i][1], w[i][2], w[i][3]);
   }
   __syncthreads();
 
@@ -199,8 +247,6 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
   }
 }
 
-int grid_cap() { return device_cu_count() * 8; }
-
 }  // namespace
 
 hipError_t launch_quant_row(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q,
@@ -210,7 +256,10 @@ hipError_t launch_quant_row(const uint16_t* x, int64_t R, int64_t C, int64_t ldx
   while ((1 << tpr_log2) < cpr && tpr_log2 < 8) tpr_log2++;
   const int64_t rps = kThreads >> tpr_log2;
   const int64_t want = (R + rps - 1) / rps;
-  const int grid = (int)(want < grid_cap() ? want : grid_cap());
+  // one workgroup per row step (many short workgroups stream HBM faster than
+  // a grid-stride loop over a CU-sized grid); capped by the grid-size limit
+  const int64_t cap = 0x7FFFFFFF;
+  const int grid = (int)(want < cap ? want : cap);
   const bool vec = (ldx % 8 == 0) && ((uintptr_t)x % 16 == 0);
   if (vec)
     quant_row_kernel<true><<<grid, kThreads, 0, st>>>(x, R, C, ldx, tpr_log2, q, s);
