@@ -148,11 +148,12 @@ def main():
     R, C = mxq.MXQ_AXIS_ROW, mxq.MXQ_AXIS_COLT
 
     def quant_w_experts(mask):
-        for g in range(G):
-            mxq.mxq_quantize(Wm[g], mask,
-                             mw["q_row"][g * H:(g + 1) * H] if mask & R else None,
-                             mw["s_row"][g * H // 32:(g + 1) * H // 32] if mask & R else None,
-                             mw["q_colT"][g] if mask & C else None, mw["s_colT"][g] if mask & C else None)
+        # all experts in one launch; the row copy / scales of expert g are rows
+        # [g*H, (g+1)*H) of the stacked buffers (H is a multiple of 32)
+        mxq.mxq_quantize_batched(Wm, mask,
+                                 mw["q_row"].view(G, H, F) if mask & R else None,
+                                 mw["s_row"].view(G, H // 32, F // 32, 32) if mask & R else None,
+                                 mw["q_colT"] if mask & C else None, mw["s_colT"] if mask & C else None)
 
     def moe_fwd(tl, schedule):
         tl("moe_quant_x_row")

@@ -114,6 +114,20 @@ mxq_status mxq_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, in
                         hipStream_t st);
 
 /*
+ * mxq_quantize over `batch` matrices in one launch: matrix b is
+ * x + b * x_stride (bf16 elements), each [R][ldx] (R x C used) -- the
+ * per-expert weights [G][K][N] of the MoE layer (torchtitan-npu guide,
+ * "MoE 专家层低精度"; MindSpeed PR 3852, "主要改动").  The outputs of
+ * matrix b are exactly what mxq_quantize writes for it, back to back:
+ * q_row + b*R*Cp, s_row + b*ceil32(R)*(Cp/32), q_colT + b*C*Rp,
+ * s_colT + b*ceil32(C)*(Rp/32).  1 <= batch <= 65535;
+ * x_stride >= (R-1)*ldx + C when batch > 1.
+ */
+mxq_status mxq_quantize_batched(const uint16_t* x, int64_t batch, int64_t R, int64_t C, int64_t ldx,
+                                int64_t x_stride, int axis_mask, uint8_t* q_row, uint8_t* s_row,
+                                uint8_t* q_colT, uint8_t* s_colT, hipStream_t st);
+
+/*
  * Grouped token-axis MXFP8 quantisation for the expert weight gradient
  * (torchtitan-npu guide, "MoE 专家层低精度").  x bf16 [T][ldx] (T x C used);
  * group g owns rows [end_{g-1}, end_g) with end_g = group_end[g] (device

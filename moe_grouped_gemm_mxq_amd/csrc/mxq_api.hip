@@ -136,6 +136,35 @@ mxq_status mxq_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, in
                   "mxq_quantize(colT)");
 }
 
+mxq_status mxq_quantize_batched(const uint16_t* x, int64_t batch, int64_t R, int64_t C, int64_t ldx,
+                                int64_t x_stride, int axis_mask, uint8_t* q_row, uint8_t* s_row,
+                                uint8_t* q_colT, uint8_t* s_colT, hipStream_t st) {
+  MXQ_REQUIRE(x != nullptr, "mxq_quantize_batched: x is NULL");
+  MXQ_REQUIRE(batch >= 1 && batch <= 65535, "mxq_quantize_batched: batch must be in [1, 65535] (got %lld)",
+              (long long)batch);
+  MXQ_REQUIRE(R >= 1 && C >= 1, "mxq_quantize_batched: R and C must be >= 1 (got %lld x %lld)",
+              (long long)R, (long long)C);
+  MXQ_REQUIRE(ldx >= C, "mxq_quantize_batched: ldx (%lld) < C (%lld)", (long long)ldx, (long long)C);
+  MXQ_REQUIRE(batch == 1 || x_stride >= (R - 1) * ldx + C,
+              "mxq_quantize_batched: x_stride (%lld) smaller than one matrix", (long long)x_stride);
+  MXQ_REQUIRE(axis_mask >= 1 && axis_mask <= 3, "mxq_quantize_batched: axis_mask must be ROW, COLT or ROW|COLT");
+  const bool row = axis_mask & MXQ_AXIS_ROW, col = axis_mask & MXQ_AXIS_COLT;
+  MXQ_REQUIRE(!row || (q_row && s_row), "mxq_quantize_batched: row outputs are NULL");
+  MXQ_REQUIRE(!col || (q_colT && s_colT), "mxq_quantize_batched: colT outputs are NULL");
+  MXQ_REQUIRE((!row || aligned16(q_row)) && (!col || aligned16(q_colT)),
+              "mxq_quantize_batched: code outputs must be 16-byte aligned");
+  MXQ_REQUIRE(((uintptr_t)x & 1u) == 0, "mxq_quantize_batched: x must be 2-byte aligned");
+  MXQ_REQUIRE_DEVICE();
+  const int64_t Cp = (C + 31) / 32 * 32, Rp = (R + 31) / 32 * 32;
+  // each matrix's outputs exactly as mxq_quantize lays them out, back to back
+  const BatchStrides bs{x_stride, R * Cp, Rp * (Cp / 32), C * Rp, (C + 31) / 32 * 32 * (Rp / 32)};
+  if (!col)
+    return launched(launch_quant_row(x, R, C, ldx, q_row, s_row, st, (int)batch, bs), "mxq_quantize_batched(row)");
+  return launched(launch_quant_tile(x, R, C, ldx, nullptr, 1, Rp, row ? q_row : nullptr, row ? s_row : nullptr,
+                                    q_colT, s_colT, st, (int)batch, bs),
+                  "mxq_quantize_batched(colT)");
+}
+
 mxq_status mxq_quantize_grouped(const uint16_t* x, int64_t T, int64_t C, int64_t ldx,
                                 const int32_t* group_end, int32_t G, int64_t ldq, int axis_mask,
                                 uint8_t* q_row, uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT,

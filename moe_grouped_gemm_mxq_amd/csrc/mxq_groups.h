@@ -19,10 +19,24 @@ struct GroupTable {
   int32_t bstart[kMaxGroups + 1];
 };
 
+// Clamped start row and size of group g (ends clamped into [0, R]; a group
+// ending before it starts is empty).
+__device__ __forceinline__ void group_span(const int32_t* __restrict__ group_end, int g, int64_t R,
+                                           int32_t& start, int32_t& size) {
+  int64_t e = group_end[g];
+  int64_t b = g ? (int64_t)group_end[g - 1] : 0;
+  e = e < 0 ? 0 : (e > R ? R : e);
+  b = b < 0 ? 0 : (b > R ? R : b);
+  start = (int32_t)b;
+  size = e > b ? (int32_t)(e - b) : 0;
+}
+
 // All THREADS threads of the workgroup must call this; G <= 4 * THREADS.
+// start / size may be null (only the block starts are written then).
 template <int THREADS>
-__device__ void build_group_table(const int32_t* __restrict__ group_end, int32_t G, int64_t R,
-                                  int32_t unit, GroupTable& gt, int32_t* scan_tmp /* [THREADS] */) {
+__device__ void build_block_starts(const int32_t* __restrict__ group_end, int32_t G, int64_t R,
+                                   int32_t unit, int32_t* start, int32_t* size, int32_t* bstart /* [G + 1] */,
+                                   int32_t* scan_tmp /* [THREADS] */) {
   static_assert(4 * THREADS >= kMaxGroups, "each thread owns at most four groups");
   const int t = threadIdx.x;
   int local = 0;
@@ -32,13 +46,10 @@ __device__ void build_group_table(const int32_t* __restrict__ group_end, int32_t
     const int g = t * 4 + j;
     nb[j] = 0;
     if (g < G) {
-      int64_t e = group_end[g];
-      int64_t b = g ? (int64_t)group_end[g - 1] : 0;
-      e = e < 0 ? 0 : (e > R ? R : e);
-      b = b < 0 ? 0 : (b > R ? R : b);
-      const int32_t m = e > b ? (int32_t)(e - b) : 0;
-      gt.start[g] = (int32_t)b;
-      gt.size[g] = m;
+      int32_t b, m;
+      group_span(group_end, g, R, b, m);
+      if (start) start[g] = b;
+      if (size) size[g] = m;
       nb[j] = (m + unit - 1) / unit;
       local += nb[j];
     }
@@ -57,12 +68,28 @@ __device__ void build_group_table(const int32_t* __restrict__ group_end, int32_t
   for (int j = 0; j < 4; j++) {
     const int g = t * 4 + j;
     if (g < G) {
-      gt.bstart[g] = run;
+      bstart[g] = run;
       run += nb[j];
     }
   }
-  if (t == THREADS - 1) gt.bstart[G] = scan_tmp[t];
+  if (t == THREADS - 1) bstart[G] = scan_tmp[t];
   __syncthreads();
+}
+
+template <int THREADS>
+__device__ void build_group_table(const int32_t* __restrict__ group_end, int32_t G, int64_t R,
+                                  int32_t unit, GroupTable& gt, int32_t* scan_tmp /* [THREADS] */) {
+  build_block_starts<THREADS>(group_end, G, R, unit, gt.start, gt.size, gt.bstart, scan_tmp);
+}
+
+// largest g with bstart[g] <= u (u < bstart[G] assumed)
+__device__ __forceinline__ int find_block_group(const int32_t* bstart, int G, int32_t u) {
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (bstart[mid] <= u) lo = mid; else hi = mid - 1;
+  }
+  return lo;
 }
 
 // largest g with bstart[g] <= u (u < bstart[G] assumed)

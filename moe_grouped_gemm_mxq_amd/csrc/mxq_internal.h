@@ -10,15 +10,22 @@ namespace mxq {
 int device_cu_count();
 
 // MXFP8 row copy: x bf16 [R][ldx] -> q [R][Cp], s [R][Cp/32]
+// Element (x, bf16) and byte (outputs) offsets between the matrices of a
+// batch; matrix b is handled by blockIdx.y == b.
+struct BatchStrides {
+  int64_t x, q_row, s_row, q_colT, s_colT;
+};
+
 hipError_t launch_quant_row(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
-                            uint8_t* q, uint8_t* s, hipStream_t st);
+                            uint8_t* q, uint8_t* s, hipStream_t st, int batch = 1,
+                            BatchStrides bs = BatchStrides{0, 0, 0, 0, 0});
 
 // MXFP8 column copy (and optionally the row copy from the same read).
 // grouped: group_end != nullptr; colT width ldq (multiple of 32).
 hipError_t launch_quant_tile(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
                              const int32_t* group_end, int32_t G, int64_t ldq,
                              uint8_t* q_row, uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT,
-                             hipStream_t st);
+                             hipStream_t st, int batch = 1, BatchStrides bs = BatchStrides{0, 0, 0, 0, 0});
 
 // MXFP4 quant-dequant
 hipError_t launch_qdq_fp4(const float* x, float* y, int64_t rows, int64_t L,

@@ -47,7 +47,11 @@ template <bool VEC>
 __global__ __launch_bounds__(kThreads) void quant_row_kernel(const uint16_t* __restrict__ x, int64_t R,
                                                             int64_t C, int64_t ldx, int tpr_log2,
                                                             uint8_t* __restrict__ q,
-                                                            uint8_t* __restrict__ s) {
+                                                            uint8_t* __restrict__ s, BatchStrides bs) {
+  // matrix blockIdx.y of a batch
+  x += blockIdx.y * bs.x;
+  q += blockIdx.y * bs.q_row;
+  s += blockIdx.y * bs.s_row;
   const int64_t Cp = (C + 31) / 32 * 32;
   const int cpr = (int)(Cp / 8);  // chunks per row (a multiple of 4)
   const int tpr = 1 << tpr_log2;
@@ -113,7 +117,15 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
     const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx,
     const int32_t* __restrict__ group_end, int32_t G, int64_t ldq, int n_col_tiles,
     uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row, uint8_t* __restrict__ q_colT,
-    uint8_t* __restrict__ s_colT) {
+    uint8_t* __restrict__ s_colT, BatchStrides bs) {
+  // matrix blockIdx.y of a batch
+  x += blockIdx.y * bs.x;
+  if constexpr (ROW) {
+    q_row += blockIdx.y * bs.q_row;
+    s_row += blockIdx.y * bs.s_row;
+  }
+  q_colT += blockIdx.y * bs.q_colT;
+  s_colT += blockIdx.y * bs.s_colT;
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTR * kLdsStride];
   __shared__ int64_t rb_src[kTR / 32];   // first source row of each block of the tile
   __shared__ int32_t rb_valid[kTR / 32]; // valid rows in that block (0: no output block)
@@ -124,18 +136,23 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
   const int64_t c0 = (int64_t)ct * kTC;
 
   if constexpr (GROUPED) {
-    __shared__ GroupTable gt;
-    __shared__ int32_t scan_tmp[kThreads];
-    build_group_table<kThreads>(group_end, G, R, 32, gt, scan_tmp);
+    // block starts only (the tile's few groups re-read their spans from
+    // group_end), keeping LDS small enough for four workgroups per CU;
+    // the scan's scratch is the tile buffer, not yet in use
+    __shared__ int32_t bstart[kMaxGroups + 1];
+    build_block_starts<kThreads>(group_end, G, R, 32, nullptr, nullptr, bstart,
+                                 reinterpret_cast<int32_t*>(tile));
     if (t < kTR / 32) {
       const int64_t pb = p0 / 32 + t;
       int64_t src = 0;
       int32_t valid = 0;
-      if (pb < gt.bstart[G] && (pb + 1) * 32 <= ldq) {
-        const int g = find_group(gt, G, (int32_t)pb);
-        const int32_t off = ((int32_t)pb - gt.bstart[g]) * 32;
-        src = (int64_t)gt.start[g] + off;
-        valid = min(32, gt.size[g] - off);
+      if (pb < bstart[G] && (pb + 1) * 32 <= ldq) {
+        const int g = find_block_group(bstart, G, (int32_t)pb);
+        int32_t gstart, gsize;
+        group_span(group_end, g, R, gstart, gsize);
+        const int32_t off = ((int32_t)pb - bstart[g]) * 32;
+        src = (int64_t)gstart + off;
+        valid = min(32, gsize - off);
         if (valid <= 0) valid = -1;  // cannot happen for consistent tables
       }
       rb_src[t] = src;
@@ -250,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
 }  // namespace
 
 hipError_t launch_quant_row(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q,
-                            uint8_t* s, hipStream_t st) {
+                            uint8_t* s, hipStream_t st, int batch, BatchStrides bs) {
   const int64_t cpr = (C + 31) / 32 * 4;
   int tpr_log2 = 2;
   while ((1 << tpr_log2) < cpr && tpr_log2 < 8) tpr_log2++;
@@ -260,28 +277,30 @@ hipError_t launch_quant_row(const uint16_t* x, int64_t R, int64_t C, int64_t ldx
   // a grid-stride loop over a CU-sized grid); capped by the grid-size limit
   const int64_t cap = 0x7FFFFFFF;
   const int grid = (int)(want < cap ? want : cap);
-  const bool vec = (ldx % 8 == 0) && ((uintptr_t)x % 16 == 0);
+  const bool vec = (ldx % 8 == 0) && ((uintptr_t)x % 16 == 0) && (batch == 1 || bs.x % 8 == 0);
+  const dim3 g((unsigned)grid, (unsigned)batch);
   if (vec)
-    quant_row_kernel<true><<<grid, kThreads, 0, st>>>(x, R, C, ldx, tpr_log2, q, s);
+    quant_row_kernel<true><<<g, kThreads, 0, st>>>(x, R, C, ldx, tpr_log2, q, s, bs);
   else
-    quant_row_kernel<false><<<grid, kThreads, 0, st>>>(x, R, C, ldx, tpr_log2, q, s);
+    quant_row_kernel<false><<<g, kThreads, 0, st>>>(x, R, C, ldx, tpr_log2, q, s, bs);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_tile(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
                              const int32_t* group_end, int32_t G, int64_t ldq, uint8_t* q_row,
-                             uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT, hipStream_t st) {
+                             uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT, hipStream_t st, int batch,
+                             BatchStrides bs) {
   const bool grouped = group_end != nullptr;
   const bool row = q_row != nullptr;
-  const bool vec = (ldx % 8 == 0) && ((uintptr_t)x % 16 == 0);
+  const bool vec = (ldx % 8 == 0) && ((uintptr_t)x % 16 == 0) && (batch == 1 || bs.x % 8 == 0);
   const int64_t padded = grouped ? (R + 31 * (int64_t)G) : R;
   const int64_t n_row_tiles = (padded + kTR - 1) / kTR;
   const int n_col_tiles = (int)((C + kTC - 1) / kTC);
   const int64_t grid = n_row_tiles * n_col_tiles;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
 #define MXQ_TILE_LAUNCH(ROWv, GRPv, VECv)                                                     \
-  quant_tile_kernel<ROWv, GRPv, VECv><<<(unsigned)grid, kThreads, 0, st>>>(                 \
-      x, R, C, ldx, group_end, G, ldq, n_col_tiles, q_row, s_row, q_colT, s_colT)
+  quant_tile_kernel<ROWv, GRPv, VECv><<<dim3((unsigned)grid, (unsigned)batch), kThreads, 0, st>>>( \
+      x, R, C, ldx, group_end, G, ldq, n_col_tiles, q_row, s_row, q_colT, s_colT, bs)
   if (row && grouped) { if (vec) MXQ_TILE_LAUNCH(true, true, true); else MXQ_TILE_LAUNCH(true, true, false); }
   else if (row) { if (vec) MXQ_TILE_LAUNCH(true, false, true); else MXQ_TILE_LAUNCH(true, false, false); }
   else if (grouped) { if (vec) MXQ_TILE_LAUNCH(false, true, true); else MXQ_TILE_LAUNCH(false, true, false); }

@@ -42,7 +42,8 @@ MAX_GROUPS = 1024
 
 EXPORTED = [
     "mxq_abi_version", "mxq_last_error", "mxq_device_check", "mxq_grouped_cols_max",
-    "mxq_quantize", "mxq_quantize_grouped", "mxq_qdq_fp4", "mxq_gemm", "mxq_grouped_gemm",
+    "mxq_quantize", "mxq_quantize_batched", "mxq_quantize_grouped", "mxq_qdq_fp4", "mxq_gemm",
+    "mxq_grouped_gemm",
     "mxq_validate_group_end",
 ]
 
@@ -60,6 +61,7 @@ def _load(path: str = LIB_PATH):
         "mxq_device_check": ([I], I),
         "mxq_grouped_cols_max": ([I64, I32], I64),
         "mxq_quantize": ([P, I64, I64, I64, I, P, P, P, P, P], I),
+        "mxq_quantize_batched": ([P, I64, I64, I64, I64, I64, I, P, P, P, P, P], I),
         "mxq_quantize_grouped": ([P, I64, I64, I64, P, I32, I64, I, P, P, P, P, P], I),
         "mxq_qdq_fp4": ([P, P, I64, I64, P, P, P], I),
         "mxq_gemm": ([P, P, P, P, P, I64, I64, I64, I64, I, P], I),
@@ -155,6 +157,22 @@ def mxq_quantize(x, axis_mask, q_row=None, s_row=None, q_colT=None, s_colT=None,
     _need_out(s_colT, "s_colT", scale_shape(C, ceil32(R) // BLOCK))
     _check(_lib.mxq_quantize(_ptr(x), R, C, x.stride(0), axis_mask, _ptr(q_row), _ptr(s_row),
                              _ptr(q_colT), _ptr(s_colT), _stream(stream, x.device)), "mxq_quantize")
+
+
+def mxq_quantize_batched(x, axis_mask, q_row=None, s_row=None, q_colT=None, s_colT=None, stream=None):
+    """x bf16 [batch][R][C] (unit stride along C).  Outputs: q_row [batch][R][Cp],
+    s_row (batch,) + scale_shape(R, Cp/32), q_colT [batch][C][Rp], s_colT (batch,) + scale_shape(C, Rp/32)."""
+    _need(x, torch.bfloat16, "x", 3)
+    if x.stride(2) != 1:
+        raise ValueError("x must have unit stride along its last dim")
+    nb, R, C = x.shape
+    _need_out(q_row, "q_row", (nb, R, ceil32(C)))
+    _need_out(s_row, "s_row", (nb,) + scale_shape(R, ceil32(C) // BLOCK))
+    _need_out(q_colT, "q_colT", (nb, C, ceil32(R)))
+    _need_out(s_colT, "s_colT", (nb,) + scale_shape(C, ceil32(R) // BLOCK))
+    _check(_lib.mxq_quantize_batched(_ptr(x), nb, R, C, x.stride(1), x.stride(0), axis_mask, _ptr(q_row),
+                                     _ptr(s_row), _ptr(q_colT), _ptr(s_colT), _stream(stream, x.device)),
+           "mxq_quantize_batched")
 
 
 def mxq_quantize_grouped(x, group_end, ldq, axis_mask, q_row=None, s_row=None, q_colT=None,
@@ -254,6 +272,21 @@ def quantize(x, axis_mask=MXQ_AXIS_ROW | MXQ_AXIS_COLT, stream=None):
         out["s_colT"] = _u8(scale_shape(C, ceil32(R) // BLOCK), x.device)
     mxq_quantize(x, axis_mask, out.get("q_row"), out.get("s_row"), out.get("q_colT"),
                  out.get("s_colT"), stream)
+    return out
+
+
+def quantize_batched(x, axis_mask=MXQ_AXIS_ROW | MXQ_AXIS_COLT, stream=None):
+    """x bf16 [batch][R][C] -> dict of batched outputs (see mxq_quantize_batched)."""
+    nb, R, C = x.shape
+    out = {}
+    if axis_mask & MXQ_AXIS_ROW:
+        out["q_row"] = _u8((nb, R, ceil32(C)), x.device)
+        out["s_row"] = _u8((nb,) + scale_shape(R, ceil32(C) // BLOCK), x.device)
+    if axis_mask & MXQ_AXIS_COLT:
+        out["q_colT"] = _u8((nb, C, ceil32(R)), x.device)
+        out["s_colT"] = _u8((nb,) + scale_shape(C, ceil32(R) // BLOCK), x.device)
+    mxq_quantize_batched(x, axis_mask, out.get("q_row"), out.get("s_row"), out.get("q_colT"), out.get("s_colT"),
+                         stream)
     return out
 
 

@@ -101,6 +101,14 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     assert call(lib, "mxq_quantize_grouped", FAKE, I64(64), I64(32), I64(32), FAKE, ctypes.c_int32(2),
                 I64(40), 2, P(0), P(0), FAKE, FAKE, P(0)) == 1
     assert call(lib, "mxq_qdq_fp4", FAKE, P(0), I64(2), I64(33), P(0), P(0), P(0)) == 1
+    # batched: batch out of range, x_stride smaller than one matrix
+    assert call(lib, "mxq_quantize_batched", FAKE, I64(0), I64(4), I64(32), I64(32), I64(128), 1, FAKE, FAKE,
+                P(0), P(0), P(0)) == 1
+    assert call(lib, "mxq_quantize_batched", FAKE, I64(70000), I64(4), I64(32), I64(32), I64(128), 1, FAKE,
+                FAKE, P(0), P(0), P(0)) == 1
+    assert call(lib, "mxq_quantize_batched", FAKE, I64(2), I64(4), I64(32), I64(32), I64(64), 1, FAKE, FAKE,
+                P(0), P(0), P(0)) == 1
+    assert "x_stride" in err(lib)
     assert call(lib, "mxq_validate_group_end", FAKE, ctypes.c_int32(2000), I64(5), FAKE, P(0)) == 1
 
 

@@ -185,6 +185,22 @@ def test_moe_wgrad_ragged_k_full_sampled(moe_full):
         assert int(torch.count_nonzero(dW[g]).item()) == 0, f"empty expert {g} has nonzero dW"
 
 
+def test_moe_batched_expert_quant_equals_per_expert(moe_full):
+    """All 32 experts' dual-axis quantisation in one batched launch gives the
+    per-expert launches' bytes exactly (those are checked against the oracle
+    in test_moe_ragged_m_full_sampled)."""
+    m = mxq()
+    W = moe_full["W"]
+    G, K, N = W.shape
+    qb = m.quantize_batched(W, 3)
+    torch.cuda.synchronize()
+    qw = moe_full["qw"]
+    assert torch.equal(qb["q_row"].view(G * K, N), qw["q_row"])
+    assert torch.equal(qb["s_row"].view(qw["s_row"].shape), qw["s_row"])
+    assert torch.equal(qb["q_colT"], qw["q_colT"])
+    assert torch.equal(qb["s_colT"], qw["s_colT"])
+
+
 def test_moe_fb_split_equals_dual(moe_full):
     """fb-split: the forward quantises W[g] on its reduction axis only and the
     backward re-quantises it along N; the gradients must equal the dual-axis

@@ -141,6 +141,27 @@ def test_quantize_every_element_and_scale_pair():
     assert np.array_equal(host(got["q_colT"]), qt) and np.array_equal(unpack_scales(got["s_colT"], len(st)), st)
 
 
+@pytest.mark.parametrize("R,C,pad", [(70, 45, 0), (64, 128, 3), (33, 300, 1), (256, 96, 0)])
+@pytest.mark.parametrize("axis", [1, 2, 3])
+def test_quantize_batched_bitexact(R, C, pad, axis):
+    """Three matrices, each padded by `pad` rows in the stacked input (so the
+    batch stride exceeds one matrix); every output equals the oracle's."""
+    m = mxq()
+    nb = 3
+    big = scaled_randn((nb * (R + pad), C), seed=R * 3 + C + pad, zero_rows=2)
+    x3 = big.view(nb, R + pad, C)[:, :R, :]
+    xg = big.cuda().view(nb, R + pad, C)[:, :R, :]   # strided batch view on the device
+    assert xg.stride(0) == (R + pad) * C
+    got = m.quantize_batched(xg, axis)
+    torch.cuda.synchronize()
+    for b in range(nb):
+        ref = quant_ref(bits(x3[b].contiguous()), axis)
+        for k, v in ref.items():
+            g = got[k][b]
+            h = unpack_scales(g, v.shape[0]) if k.startswith("s_") else host(g)
+            assert_bytes_equal(h, v, f"{k} batch {b} {R}x{C}")
+
+
 GROUPS = [[70], [0, 1, 31, 32, 33, 0], [0, 0, 5], [64, 0], [17, 40, 1, 0, 96],
           [0, 0, 0, 200, 0, 0], [129, 1, 255, 0, 2, 64, 33]]
 
