@@ -47,6 +47,8 @@ def _declare(lib):
         "oracle_mxfp8_quant_grouped_colT": ([P, I64, I64, I64, P, I32, I64, P, P], ctypes.c_int),
         "oracle_mxfp8_dequant": ([P, P, I64, I64, P], None),
         "oracle_mxfp4_qdq": ([P, P, I64, I64, P, P], ctypes.c_int),
+        "oracle_mxfp4_qdq_ex": ([P, P, I64, I64, ctypes.c_float, P, P, P], ctypes.c_int),
+        "oracle_mxfp4_ste_backward": ([P, P, P, I64, I64], None),
         "oracle_gemm": ([P, P, P, P, I64, I64, I64, P, P], ctypes.c_int),
         "oracle_gemm_sampled": ([P, P, P, P, I64, I64, I64, P, P, I64, P, P], ctypes.c_int),
         "oracle_grouped_gemm_ragged_m": ([P, P, P, P, I64, I64, I64, P, I32, P, P], ctypes.c_int),
@@ -204,6 +206,37 @@ def mxfp4_qdq(x: np.ndarray, want_codes: bool = False):
     scales = np.zeros((rows, Lp // BLOCK), np.uint8) if want_codes else None
     _check(lib().oracle_mxfp4_qdq(_p(x), _p(y), rows, L, _p(codes), _p(scales)), "mxfp4_qdq")
     return (y, codes, scales) if want_codes else y
+
+
+def mxfp4_qdq_ex(x: np.ndarray, scale_factor: float = 6.0):
+    """QDQ with a runtime scale factor (an fp32 value; the page's
+    inv_scale_factor_scale is 6 / scale_factor).  Returns (y, codes [rows][Lp/2],
+    scales [rows][Lp/32], saturation mask [rows][Lp/8], bit j of byte k =
+    element 8k+j has |x| > 6*scale)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    shape = x.shape
+    L = shape[-1] if x.ndim else 1
+    rows = int(np.prod(shape[:-1])) if x.ndim > 1 else 1
+    y = np.zeros(shape, np.float32)
+    Lp = ceil32(L)
+    codes = np.zeros((rows, Lp // 2), np.uint8)
+    scales = np.zeros((rows, Lp // BLOCK), np.uint8)
+    mask = np.zeros((rows, Lp // 8), np.uint8)
+    _check(lib().oracle_mxfp4_qdq_ex(_p(x), _p(y), rows, L, float(np.float32(scale_factor)), _p(codes),
+                                     _p(scales), _p(mask)), "mxfp4_qdq_ex")
+    return y, codes, scales, mask
+
+
+def mxfp4_ste_backward(grad_y: np.ndarray, mask: np.ndarray) -> np.ndarray:
+    """Clipped-STE backward: grad_y where the element did not saturate, else 0."""
+    grad_y = np.ascontiguousarray(grad_y, dtype=np.float32)
+    L = grad_y.shape[-1]
+    rows = grad_y.size // L
+    gx = np.zeros_like(grad_y)
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    assert mask.shape == (rows, ceil32(L) // 8)
+    lib().oracle_mxfp4_ste_backward(_p(grad_y), _p(mask), _p(gx), rows, L)
+    return gx
 
 
 # ---------------------------------------------------------------- GEMMs

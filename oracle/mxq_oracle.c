@@ -269,30 +269,32 @@ void oracle_mxfp8_dequant(const uint8_t* q, const uint8_t* s, int64_t R, int64_t
 /* E2M1 codebook (magnitudes) and the midpoints between neighbours. */
 static const double fp4_codebook[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
 static const double fp4_midpoints[7] = {0.25, 0.75, 1.25, 1.75, 2.50, 3.50, 5.00};
-#define FP4_SCALE_FACTOR 6.0
+#define FP4_SCALE_FACTOR 6.0             /* default scale_factor [AMCT section 2] */
+#define FP4_CODE_MAX 6.0                 /* largest codebook magnitude */
 #define FP4_MIN_SCALE_EXP (-30)          /* raw scale clamped at 2^-30 */
 
-/* round(log2(amax / 6)) evaluated exactly.  log2 of a rational is never an
+/* round(log2(amax / sf)) evaluated exactly.  log2 of a rational is never an
  * odd multiple of 1/2, so there is no tie and the nearest integer n is the
- * one with 2^(n-1/2) <= amax/6 < 2^(n+1/2), i.e. 18*4^n <= amax^2 < 72*4^n.
- * amax is an fp32 value, so amax^2 (48 significant bits) and the bounds are
- * exact in fp64; a floating-point first guess is corrected by those exact
- * comparisons. */
-static int fp4_round_log2_over6(double amax)
+ * one with 2^(n-1/2) <= amax/sf < 2^(n+1/2), i.e.
+ * sf^2 * 2^(2n-1) <= amax^2 < sf^2 * 2^(2n+1) (18*4^n and 72*4^n for the
+ * default sf = 6).  amax and sf are fp32 values, so amax^2, sf^2 (48
+ * significant bits each) and the bounds are exact in fp64; a floating-point
+ * first guess is corrected by those exact comparisons. */
+static int fp4_round_log2_ratio(double amax, double sf)
 {
-    int n = (int)floor(log2(amax / FP4_SCALE_FACTOR) + 0.5);
-    double a2 = amax * amax;
-    while (a2 >= 72.0 * ldexp(1.0, 2 * n)) n++;
-    while (a2 < 18.0 * ldexp(1.0, 2 * n)) n--;
+    int n = (int)floor(log2(amax / sf) + 0.5);
+    double a2 = amax * amax, s2 = sf * sf;
+    while (a2 >= s2 * ldexp(2.0, 2 * n)) n++;
+    while (a2 < s2 * ldexp(0.5, 2 * n)) n--;
     return n;
 }
 
-/* Scale exponent of one block: raw = max(amax/6, 2^-30), e = round(log2 raw). */
-static int fp4_scale_exp(double amax)
+/* Scale exponent of one block: raw = max(amax/sf, 2^-30), e = round(log2 raw). */
+static int fp4_scale_exp(double amax, double sf)
 {
-    if (amax <= FP4_SCALE_FACTOR * ldexp(1.0, FP4_MIN_SCALE_EXP))
+    if (amax <= sf * ldexp(1.0, FP4_MIN_SCALE_EXP))
         return FP4_MIN_SCALE_EXP;                  /* clamped raw scale */
-    int n = fp4_round_log2_over6(amax);
+    int n = fp4_round_log2_ratio(amax, sf);
     return n < FP4_MIN_SCALE_EXP ? FP4_MIN_SCALE_EXP : n;
 }
 
@@ -308,18 +310,24 @@ static int fp4_code_index(double yabs)
 }
 
 /*
- * x fp32 [rows][L] -> y fp32 [rows][L].  Each row is padded with zeros to
+ * x fp32 [rows][L] -> y fp32 [rows][L], with scale = 2^round(log2(amax /
+ * scale_factor)) [AMCT section 2; the op's inv_scale_factor_scale is
+ * 6 / scale_factor, section 3.3].  Each row is padded with zeros to
  * Lp = ceil32(L) before blocking, so rows never share a block.
  * Optional outputs (may be NULL): codes [rows][Lp/2] E2M1 nibbles (element 2j
  * in the low nibble of byte j, nibble = sign<<3 | codebook index, which is
- * the OCP E2M1 bit pattern) and scales [rows][Lp/32] E8M0 bytes (e + 127).
- * Returns 1 for bad sizes, 2 if an input is NaN/Inf or a dequantised value
- * does not fit in fp32 (outside the method's contract).
+ * the OCP E2M1 bit pattern), scales [rows][Lp/32] E8M0 bytes (e + 127), and
+ * the clipped-STE saturation mask [rows][Lp/8] [AMCT section 4.1]: bit j of
+ * byte k is set iff |x| > 6 * scale for element 8k + j (padding: clear).
+ * Returns 1 for bad sizes or a scale factor that is not positive and finite,
+ * 2 if an input is NaN/Inf, a block scale exceeds 2^127 (not an E8M0 value)
+ * or a dequantised value does not fit in fp32 (outside the method's contract).
  */
-int oracle_mxfp4_qdq(const float* x, float* y, int64_t rows, int64_t L,
-                     uint8_t* codes, uint8_t* scales)
+int oracle_mxfp4_qdq_ex(const float* x, float* y, int64_t rows, int64_t L, float scale_factor_f32,
+                        uint8_t* codes, uint8_t* scales, uint8_t* sat_mask)
 {
-    if (rows < 0 || L < 0) return 1;
+    double scale_factor = (double)scale_factor_f32;   /* an fp32 value: its square is exact in fp64 */
+    if (rows < 0 || L < 0 || !(scale_factor > 0.0) || !isfinite(scale_factor)) return 1;
     int64_t Lp = ceil32(L), nb = Lp / MX_BLOCK;
     int bad = 0;
 #pragma omp parallel for schedule(static) reduction(| : bad)
@@ -334,7 +342,8 @@ int oracle_mxfp4_qdq(const float* x, float* y, int64_t rows, int64_t L,
                 if (fabs(v[i]) > amax) amax = fabs(v[i]);
             }
             if (!isfinite(amax)) { bad = 1; continue; }
-            int e = fp4_scale_exp(amax);
+            int e = fp4_scale_exp(amax, scale_factor);
+            if (e > 127) { bad = 1; continue; }               /* E8M0 tops out at 2^127 (0xFF is NaN) */
             double scale = ldexp(1.0, e);
             if (scales) scales[r * nb + b] = (uint8_t)(e + 127);
             for (int i = 0; i < MX_BLOCK; i++) {
@@ -352,10 +361,38 @@ int oracle_mxfp4_qdq(const float* x, float* y, int64_t rows, int64_t L,
                     if (col % 2 == 0) *byte = (uint8_t)((*byte & 0xF0) | nib);
                     else *byte = (uint8_t)((*byte & 0x0F) | (nib << 4));
                 }
+                if (sat_mask) {
+                    uint8_t* byte = &sat_mask[r * (Lp / 8) + col / 8];
+                    uint8_t bit = (uint8_t)(1u << (col % 8));
+                    if (fabs(v[i]) > FP4_CODE_MAX * scale) *byte |= bit;
+                    else *byte &= (uint8_t)~bit;
+                }
             }
         }
     }
     return bad ? 2 : 0;
+}
+
+int oracle_mxfp4_qdq(const float* x, float* y, int64_t rows, int64_t L,
+                     uint8_t* codes, uint8_t* scales)
+{
+    return oracle_mxfp4_qdq_ex(x, y, rows, L, (float)FP4_SCALE_FACTOR, codes, scales, NULL);
+}
+
+/*
+ * Clipped-STE backward [AMCT section 4.1]: the gradient passes straight
+ * through the quantiser except where the element saturated, where it is 0:
+ * grad_x = mask ? 0 : grad_y, mask as written by oracle_mxfp4_qdq_ex.
+ */
+void oracle_mxfp4_ste_backward(const float* grad_y, const uint8_t* sat_mask, float* grad_x,
+                               int64_t rows, int64_t L)
+{
+    int64_t Lp = ceil32(L);
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t c = 0; c < L; c++) {
+            int sat = (sat_mask[r * (Lp / 8) + c / 8] >> (c % 8)) & 1;
+            grad_x[r * L + c] = sat ? 0.0f : grad_y[r * L + c];
+        }
 }
 
 /* ---------------------------------------------------------------------- */

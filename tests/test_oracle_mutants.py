@@ -20,9 +20,18 @@ MUTANTS = {
                             "if (yabs > fp4_midpoints[i]) idx = i + 1;",
                             [lambda: t4.test_midpoint_ties_go_to_larger_magnitude(0)]),
     "fp4 exponent floor instead of round": (
-        "while (a2 >= 72.0 * ldexp(1.0, 2 * n)) n++;\n    while (a2 < 18.0 * ldexp(1.0, 2 * n)) n--;",
-        "while (a2 >= 144.0 * ldexp(1.0, 2 * n)) n++;\n    while (a2 < 36.0 * ldexp(1.0, 2 * n)) n--;",
+        "while (a2 >= s2 * ldexp(2.0, 2 * n)) n++;\n    while (a2 < s2 * ldexp(0.5, 2 * n)) n--;",
+        "while (a2 >= s2 * ldexp(4.0, 2 * n)) n++;\n    while (a2 < s2 * ldexp(1.0, 2 * n)) n--;",
                                [t4.test_exponent_round_half_threshold]),
+    "fp4 saturation mask uses >=": ("if (fabs(v[i]) > FP4_CODE_MAX * scale) *byte |= bit;",
+                                    "if (fabs(v[i]) >= FP4_CODE_MAX * scale) *byte |= bit;",
+                                    [t4.test_saturation_mask_marks_values_beyond_six_scales]),
+    "fp4 scale factor ignored": ("int e = fp4_scale_exp(amax, scale_factor);",
+                                 "int e = fp4_scale_exp(amax, 6.0);",
+                                 [t4.test_scale_factor_threshold_for_several_factors]),
+    "fp4 ste mask row stride": ("int sat = (sat_mask[r * (Lp / 8) + c / 8] >> (c % 8)) & 1;",
+                                "int sat = (sat_mask[r * (L / 8) + c / 8] >> (c % 8)) & 1;",
+                                [t4.test_ste_backward_zeroes_only_clipped_elements]),
     "fp4 min scale 2^-31": ("#define FP4_MIN_SCALE_EXP (-30)", "#define FP4_MIN_SCALE_EXP (-31)",
                             [t4.test_zero_and_tiny_blocks_use_minimum_scale]),
     "fp4 drops sign of zero": ("double out = copysign(fp4_codebook[idx] * scale, v[i]);",

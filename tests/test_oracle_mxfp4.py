@@ -255,3 +255,143 @@ def test_largest_finite_input_stays_finite():
     y, _, e = qdq_scales(np.array([[fmax, -fmax] + [1.0] * 30], np.float32))
     assert e[0, 0] == 125
     assert y[0, 0] == 6 * 2.0 ** 125 and y[0, 1] == -6 * 2.0 ** 125
+
+
+# ---------------------------------------------------------------- runtime scale factor
+# The op takes scale_factor (default 6) and divides amax by it before the
+# logarithm (AMCT FakeQuant article, section 2 parameters and section 3.3,
+# where the op's inv_scale_factor_scale is 6 / scale_factor).
+FACTORS = [6.0, 5.0, 7.25, 1.0, 0.75, 4.0, 12.0]
+
+
+def brute_qdq_sf(x: np.ndarray, sf: float):
+    """Exact-rational QDQ with scale factor sf: returns y and the saturation mask
+    as booleans (|x| > 6 * scale), both [rows][L]."""
+    cb = [Fraction(c) for c in (0, 0.5, 1, 1.5, 2, 3, 4, 6)]
+    rows = x.reshape(-1, x.shape[-1])
+    L = rows.shape[1]
+    out = np.zeros_like(rows)
+    sat = np.zeros(rows.shape, bool)
+    fsf = Fraction(float(np.float32(sf)))
+    for r, row in enumerate(rows):
+        for b0 in range(0, L, 32):
+            blk = [Fraction(float(v)) for v in row[b0:b0 + 32]]
+            amax = max(abs(v) for v in blk)
+            e = -30 if amax == 0 else dec_round_log2(max(amax / fsf, Fraction(1, 2 ** 30)))
+            e = max(e, -30)
+            sc = Fraction(2) ** e
+            for i, v in enumerate(blk):
+                y = abs(v) / sc
+                best = min(cb, key=lambda c: (abs(y - c), -c))
+                out[r, b0 + i] = math.copysign(float(best * sc), float(row[b0 + i]))
+                sat[r, b0 + i] = abs(v) > 6 * sc
+    return out.reshape(x.shape), sat
+
+
+def unpack_mask(mask: np.ndarray, L: int) -> np.ndarray:
+    return np.unpackbits(mask, axis=1, bitorder="little")[:, :L].astype(bool)
+
+
+def test_default_factor_equals_plain_qdq():
+    x = torch.randn(9, 100, generator=torch.Generator().manual_seed(11)).numpy()
+    y0, c0, s0 = oracle.mxfp4_qdq(x, want_codes=True)
+    y, c, s, _ = oracle.mxfp4_qdq_ex(x, 6.0)
+    assert np.array_equal(bits(y), bits(y0)) and np.array_equal(c, c0) and np.array_equal(s, s0)
+
+
+@pytest.mark.parametrize("sf", FACTORS)
+def test_scale_factor_bruteforce_exact_rational(sf):
+    x = torch.randn(3, 70, generator=torch.Generator().manual_seed(int(sf * 8))).numpy()
+    x[1] *= 2.0 ** 17
+    x[2, :40] *= 2.0 ** -9
+    y, _, _, mask = oracle.mxfp4_qdq_ex(x, sf)
+    want_y, want_sat = brute_qdq_sf(x, sf)
+    assert np.array_equal(bits(y), bits(want_y))
+    assert np.array_equal(unpack_mask(mask, 70), want_sat)
+
+
+def test_scale_factor_threshold_for_several_factors():
+    """round(log2(amax/sf)) steps from n to n+1 where amax crosses sf*sqrt(2)*2^n,
+    i.e. where amax^2 >= 2*sf^2*4^n.  The fp32 neighbours straddling that point
+    are found with exact rationals and must get scale bytes n+127 and n+128."""
+    for sf in [5.0, 7.25, 1.0, 0.75, 3.0, 6.0, 10.5]:
+        fsf = Fraction(float(np.float32(sf)))
+        for n in (-20, -3, 0, 1, 4, 30):
+            t2 = 2 * fsf * fsf * Fraction(4) ** n if n >= 0 else 2 * fsf * fsf / Fraction(4) ** -n
+            a = np.float32(float(np.float32(sf)) * math.sqrt(2.0) * 2.0 ** n)
+            while Fraction(float(a)) ** 2 >= t2:
+                a = np.nextafter(a, np.float32(0))
+            while Fraction(float(a)) ** 2 < t2:
+                a = np.nextafter(a, np.float32(np.inf))
+            below = np.nextafter(a, np.float32(0))
+            for v, want in ((below, n), (a, n + 1)):
+                x = np.zeros((1, 32), np.float32)
+                x[0, 5] = v
+                _, _, s, _ = oracle.mxfp4_qdq_ex(x, sf)
+                assert int(s[0, 0]) - 127 == max(want, -30), (sf, n, float(v))
+
+
+@pytest.mark.parametrize("j", [-3, -1, 1, 2, 5])
+def test_scale_byte_shifts_with_power_of_two_factor(j):
+    """Multiplying sf by 2^j divides amax/sf by 2^j: every unclamped scale byte
+    drops by exactly j."""
+    x = (torch.randn(16, 64, generator=torch.Generator().manual_seed(3)) * 100).numpy()
+    _, _, s0, _ = oracle.mxfp4_qdq_ex(x, 5.0)
+    _, _, s1, _ = oracle.mxfp4_qdq_ex(x, 5.0 * 2.0 ** j)
+    assert np.all(s0.astype(int) - 127 > -20)
+    assert np.array_equal(s1.astype(int), s0.astype(int) - j)
+
+
+def test_saturation_mask_marks_values_beyond_six_scales():
+    """sf = 6 and amax = 8: log2(8/6) = 0.415 rounds to 0, scale 1, so 6 is the
+    largest code and is reached without clipping; anything above 6 clipped."""
+    six_up = float(np.nextafter(np.float32(6), np.float32(7)))
+    vals = [8.0, 6.0, six_up, -7.0, 5.99, 0.0, -6.0, 6.5, 5.0, -0.0] + [1.0] * 22
+    x = np.array([vals], np.float32)
+    y, _, s, mask = oracle.mxfp4_qdq_ex(x, 6.0)
+    assert s[0, 0] == 127
+    want = np.array([abs(v) > 6.0 for v in vals])
+    assert np.array_equal(unpack_mask(mask, 32)[0], want)
+    assert y[0, 0] == 6.0 and y[0, 2] == 6.0 and y[0, 3] == -6.0 and y[0, 1] == 6.0
+    # on random data with several factors the mask is exactly |x| > 6 * scale
+    for sf in (6.0, 4.0, 9.0):
+        x = torch.randn(5, 77, generator=torch.Generator().manual_seed(2)).numpy()
+        _, _, s, mask = oracle.mxfp4_qdq_ex(x, sf)
+        scale = np.repeat(2.0 ** (s.astype(np.float64) - 127), 32, axis=1)[:, :77]
+        assert np.array_equal(unpack_mask(mask, 77), np.abs(x.astype(np.float64)) > 6 * scale)
+        # padding bits past L stay clear
+        assert not np.unpackbits(mask, axis=1, bitorder="little")[:, 77:].any()
+    # sf <= 6 never clips: amax / scale < sf * sqrt(2) <= 6 * sqrt(2) only above 6
+    x = torch.randn(8, 64, generator=torch.Generator().manual_seed(4)).numpy()
+    assert not oracle.mxfp4_qdq_ex(x, 4.0)[3].any()
+
+
+def test_ste_backward_zeroes_only_clipped_elements():
+    """Clipped STE (AMCT FakeQuant article, section 4.1): the gradient passes
+    through where the quantiser did not clip and is 0 where it did."""
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((6, 45)).astype(np.float32)
+    x[:, ::7] *= 4.0                                      # make some blocks clip
+    g = rng.standard_normal((6, 45)).astype(np.float32)
+    _, _, s, mask = oracle.mxfp4_qdq_ex(x, 8.0)
+    gx = oracle.mxfp4_ste_backward(g, mask)
+    scale = np.repeat(2.0 ** (s.astype(np.float64) - 127), 32, axis=1)[:, :45]
+    clipped = np.abs(x.astype(np.float64)) > 6 * scale
+    assert clipped.any() and not clipped.all()
+    assert np.array_equal(gx, np.where(clipped, np.float32(0), g))
+    # an all-clear mask is the identity; an all-set mask gives zeros
+    ones = np.full_like(mask, 0xFF)
+    assert np.array_equal(oracle.mxfp4_ste_backward(g, np.zeros_like(mask)), g)
+    assert not oracle.mxfp4_ste_backward(g, ones).any()
+
+
+def test_scale_factor_out_of_contract_is_rejected():
+    x = np.ones((1, 32), np.float32)
+    for sf in (0.0, -6.0, np.inf, np.nan):
+        with pytest.raises(ValueError):
+            oracle.mxfp4_qdq_ex(x, sf)
+    # a block scale above 2^127 is not an E8M0 value
+    big = np.full((1, 32), np.finfo(np.float32).max, np.float32)
+    with pytest.raises(ValueError):
+        oracle.mxfp4_qdq_ex(big, 0.5)
+    oracle.mxfp4_qdq_ex(big, 6.0)
