@@ -252,6 +252,89 @@ def main():
                 "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_FP8_TFLOPS, 4), "traffic": measured_traffic(dom),
                 "algorithmic_flops_per_launch": flops[dom], "avg_launch_ms": round(avg[dom], 4)}
 
+    # ---------------------------------------------------------------- dense schedules: time and memory
+    # dual: the forward quantises X and W on both axes and keeps X's column
+    # copy and W's row copy for the backward; fb-split: the forward quantises
+    # only what it uses (X rows, W columns) and the backward re-quantises X
+    # along M and W along N from bf16 (MindSpeed PR 3852, fp8-quant-fb-split).
+    def dense_fwd(sched):
+        if sched == "dual":
+            mxq.mxq_quantize(X, R | C, qx["q_row"], qx["s_row"], qx["q_colT"], qx["s_colT"])
+            mxq.mxq_quantize(W, R | C, qw["q_row"], qw["s_row"], qw["q_colT"], qw["s_colT"])
+        else:
+            mxq.mxq_quantize(X, R, qx["q_row"], qx["s_row"])
+            mxq.mxq_quantize(W, C, None, None, qw["q_colT"], qw["s_colT"])
+        mxq.mxq_gemm(qx["q_row"], qx["s_row"], qw["q_colT"], qw["s_colT"], Y)
+
+    def dense_bwd(sched):
+        if sched == "fb_split":
+            mxq.mxq_quantize(X, C, None, None, qx["q_colT"], qx["s_colT"])
+            mxq.mxq_quantize(W, R, qw["q_row"], qw["s_row"])
+        mxq.mxq_quantize(dY, R | C, qy["q_row"], qy["s_row"], qy["q_colT"], qy["s_colT"])
+        mxq.mxq_gemm(qy["q_row"], qy["s_row"], qw["q_row"], qw["s_row"], dX)
+        mxq.mxq_gemm(qx["q_colT"], qx["s_colT"], qy["q_colT"], qy["s_colT"], dW)
+
+    def time_schedule(fwd, bwd, sched):
+        for _ in range(2):
+            fwd(sched)
+            bwd(sched)
+        torch.cuda.synchronize()
+        fb = []
+        for _ in range(5):
+            tl = Timeline(torch)
+            tl("fwd")
+            fwd(sched)
+            tl("bwd")
+            bwd(sched)
+            tl(None)
+            fb.append(tl)
+        torch.cuda.synchronize()
+        d = {}
+        for tl in fb:
+            for k, v in tl.durations().items():
+                d.setdefault(k, []).extend(v)
+        return round(sum(d["fwd"]) / len(d["fwd"]), 3), round(sum(d["bwd"]) / len(d["bwd"]), 3)
+
+    dense_sched = {}
+    grads = {}
+    for sched in ("dual", "fb_split"):
+        f_ms, b_ms = time_schedule(dense_fwd, dense_bwd, sched)
+        held = (qx["q_colT"].numel() + qx["s_colT"].numel() + qw["q_row"].numel() + qw["s_row"].numel()
+                if sched == "dual" else 0)
+        dense_sched[sched] = {"fwd_ms": f_ms, "bwd_ms": b_ms, "quantised_held_fwd_to_bwd_bytes": held}
+        grads[sched] = (dX.clone(), dW.clone())
+    dense_sched["bitwise_equal_grads"] = bool(torch.equal(grads["dual"][0], grads["fb_split"][0]) and
+                                              torch.equal(grads["dual"][1], grads["fb_split"][1]))
+    del grads
+
+    # ---------------------------------------------------------------- clipped-STE fake quantiser
+    # MXFP4 QDQ that also writes the saturation bitmask (one bit per element),
+    # then the masked backward, on the same 8192x8192 tensor; y4 stands in for
+    # the incoming gradient.
+    mask4 = u8(x4.shape[0], x4.shape[1] // 8)
+    gx4 = torch.empty_like(x4)
+    n4 = x4.numel()
+    ste_bytes = {"fwd_qdq_with_mask": 8.0 * n4 + n4 / 8, "bwd_masked_grad": 8.0 * n4 + n4 / 8}
+    ste_runs = []
+    for i in range(12):
+        tl = Timeline(torch)
+        tl("fwd_qdq_with_mask")
+        mxq.mxq_qdq_fp4_ex(x4, y4, 6.0, None, None, mask4)
+        tl("bwd_masked_grad")
+        mxq.mxq_ste_backward_fp4(y4, mask4, gx4)
+        tl(None)
+        if i >= 2:
+            ste_runs.append(tl)
+    torch.cuda.synchronize()
+    fake_quant = {}
+    for tl in ste_runs:
+        for k, v in tl.durations().items():
+            fake_quant.setdefault(k, []).extend(v)
+    for k, v in list(fake_quant.items()):
+        ms = sum(v) / len(v)
+        gbs = ste_bytes[k] / (ms * 1e-3) / 1e9
+        fake_quant[k] = {"ms": round(ms, 4), "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
     # ---------------------------------------------------------------- MoE schedules: time and memory
     schedules = {}
     for sched in ("dual", "fb_split"):
@@ -308,6 +391,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "components": components,
+        "dense_schedules": dense_sched,
+        "mxfp4_clipped_ste": fake_quant,
         "moe_schedules": schedules,
     }
     print(json.dumps(out))

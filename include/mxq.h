@@ -166,6 +166,45 @@ mxq_status mxq_qdq_fp4(const float* x, float* y, int64_t rows, int64_t L,
                        uint8_t* codes, uint8_t* scales, hipStream_t st);
 
 /*
+ * MXFP4 quantise-dequantise with a runtime scale factor and the clipped-STE
+ * saturation mask (AMCT FakeQuant article: scale_factor among the section 2
+ * parameters, passed to the op as 6 / scale_factor in section 3.3; the
+ * clipped straight-through estimator of section 4.1).  As mxq_qdq_fp4, with
+ * scale = 2^round(log2(max|x| / scale_factor)) (raw scale clamped at 2^-30,
+ * round taken exactly); scale_factor = 6 gives mxq_qdq_fp4's results.
+ * scale_factor must be a normal fp32 value in [2^-64, 2^64), else
+ * MXQ_ERR_INVALID_ARGUMENT.  Blocks whose scale would exceed 2^127, or whose
+ * dequantised values overflow fp32, are outside the contract (only possible
+ * for scale_factor < 6 and inputs near the fp32 maximum).
+ * sat_mask (optional, NULL to skip; 4-byte aligned): device bytes
+ * [rows][Lp/8]; bit j of byte k is element 8k + j of the row, set iff
+ * |x| > 6 * scale (the element was clipped to the largest code); bits of the
+ * padding past L are 0.  codes and scales as for mxq_qdq_fp4.
+ */
+mxq_status mxq_qdq_fp4_ex(const float* x, float* y, int64_t rows, int64_t L, float scale_factor,
+                          uint8_t* codes, uint8_t* scales, uint8_t* sat_mask, hipStream_t st);
+
+/*
+ * Clipped-STE backward of the MXFP4 quantiser (AMCT FakeQuant article,
+ * section 4.1): grad_x = 0 where the forward clipped the element (its
+ * sat_mask bit, as written by mxq_qdq_fp4_ex for the same rows and L, is
+ * set), grad_x = grad_y elsewhere.  grad_y, grad_x fp32 [rows][L] on the
+ * device; grad_x may be grad_y (in place) but must not partly overlap it.
+ * All three pointers 4-byte aligned; rows, L >= 1.
+ */
+mxq_status mxq_ste_backward_fp4(const float* grad_y, const uint8_t* sat_mask, float* grad_x,
+                                int64_t rows, int64_t L, hipStream_t st);
+
+/*
+ * Host only (no device needed): the exponent threshold mxq_qdq_fp4_ex uses
+ * for a scale factor.  With scale_factor * sqrt(2) = (1 + t) * 2^F, a block's
+ * exponent is E - F + (m >= T) for max|x| = (1 + m / 2^23) * 2^E, where
+ * T = ceil(t * 2^23) (T = 2^23: never).  Writes F and T; rejects factors
+ * outside [2^-64, 2^64) with MXQ_ERR_INVALID_ARGUMENT.
+ */
+mxq_status mxq_fp4_scale_threshold(float scale_factor, int32_t* F, uint32_t* T);
+
+/*
  * Block-scaled GEMM C[m][n] = sum_k deq(A)[m][k] * deq(B)[n][k] (the FP8
  * linear GEMMs of the torchtitan-npu guide, "线性层低精度"), fp32
  * accumulation and fp32 output.  A codes [M][K] + scales (M rows);

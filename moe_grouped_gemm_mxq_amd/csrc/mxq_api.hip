@@ -195,8 +195,48 @@ mxq_status mxq_qdq_fp4(const float* x, float* y, int64_t rows, int64_t L, uint8_
   MXQ_REQUIRE(rows >= 1 && L >= 1, "mxq_qdq_fp4: rows and L must be >= 1");
   MXQ_REQUIRE(((uintptr_t)x & 3u) == 0 && ((uintptr_t)y & 3u) == 0, "mxq_qdq_fp4: x, y must be 4-byte aligned");
   MXQ_REQUIRE(!codes || aligned16(codes), "mxq_qdq_fp4: codes must be 16-byte aligned");
+  int F;
+  uint32_t T;
+  fp4_scale_params(6.0f, &F, &T);
   MXQ_REQUIRE_DEVICE();
-  return launched(launch_qdq_fp4(x, y, rows, L, codes, scales, st), "mxq_qdq_fp4");
+  return launched(launch_qdq_fp4(x, y, rows, L, F, T, codes, scales, nullptr, st), "mxq_qdq_fp4");
+}
+
+mxq_status mxq_qdq_fp4_ex(const float* x, float* y, int64_t rows, int64_t L, float scale_factor,
+                          uint8_t* codes, uint8_t* scales, uint8_t* sat_mask, hipStream_t st) {
+  MXQ_REQUIRE(x != nullptr && y != nullptr, "mxq_qdq_fp4_ex: x or y is NULL");
+  MXQ_REQUIRE(rows >= 1 && L >= 1, "mxq_qdq_fp4_ex: rows and L must be >= 1");
+  MXQ_REQUIRE(((uintptr_t)x & 3u) == 0 && ((uintptr_t)y & 3u) == 0, "mxq_qdq_fp4_ex: x, y must be 4-byte aligned");
+  MXQ_REQUIRE(!codes || aligned16(codes), "mxq_qdq_fp4_ex: codes must be 16-byte aligned");
+  MXQ_REQUIRE(!sat_mask || ((uintptr_t)sat_mask & 3u) == 0, "mxq_qdq_fp4_ex: sat_mask must be 4-byte aligned");
+  int F;
+  uint32_t T;
+  MXQ_REQUIRE(fp4_scale_params(scale_factor, &F, &T),
+              "mxq_qdq_fp4_ex: scale_factor must be a normal fp32 value in [2^-64, 2^64) (got %g)",
+              (double)scale_factor);
+  MXQ_REQUIRE_DEVICE();
+  return launched(launch_qdq_fp4(x, y, rows, L, F, T, codes, scales, sat_mask, st), "mxq_qdq_fp4_ex");
+}
+
+mxq_status mxq_ste_backward_fp4(const float* grad_y, const uint8_t* sat_mask, float* grad_x,
+                                int64_t rows, int64_t L, hipStream_t st) {
+  MXQ_REQUIRE(grad_y && sat_mask && grad_x, "mxq_ste_backward_fp4: NULL operand");
+  MXQ_REQUIRE(rows >= 1 && L >= 1, "mxq_ste_backward_fp4: rows and L must be >= 1");
+  MXQ_REQUIRE(((uintptr_t)grad_y & 3u) == 0 && ((uintptr_t)grad_x & 3u) == 0 && ((uintptr_t)sat_mask & 3u) == 0,
+              "mxq_ste_backward_fp4: grad_y, grad_x and sat_mask must be 4-byte aligned");
+  MXQ_REQUIRE(grad_x == grad_y || grad_x + rows * L <= grad_y || grad_y + rows * L <= grad_x,
+              "mxq_ste_backward_fp4: grad_x must be grad_y or not overlap it");
+  MXQ_REQUIRE_DEVICE();
+  return launched(launch_ste_backward_fp4(grad_y, sat_mask, grad_x, rows, L, st), "mxq_ste_backward_fp4");
+}
+
+mxq_status mxq_fp4_scale_threshold(float scale_factor, int32_t* F, uint32_t* T) {
+  MXQ_REQUIRE(F && T, "mxq_fp4_scale_threshold: NULL output");
+  int f;
+  MXQ_REQUIRE(fp4_scale_params(scale_factor, &f, T),
+              "mxq_fp4_scale_threshold: scale_factor must be a normal fp32 value in [2^-64, 2^64)");
+  *F = f;
+  return MXQ_OK;
 }
 
 mxq_status mxq_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,

@@ -88,10 +88,23 @@ __device__ __forceinline__ int64_t scale_offset(int64_t r, int64_t b, int64_t nb
 // amax = m * 2^E (m in [1,2)), log2(amax/6) rounds up to E-2 iff m >= 3/(2*sqrt 2),
 // i.e. iff the mantissa field is >= 0x7C3B7, else to E-3.  Subnormal or zero
 // maxima lie far below 6*2^-30.5, so they take the clamp.
-__device__ __forceinline__ int mxfp4_scale_exp(uint32_t amax_bits) {
+// Exponent rule of an MXFP4 block for an fp32 scale factor sf:
+// round(log2(amax / sf)), taken exactly.  Write sf * sqrt(2) = (1 + t) * 2^F
+// and amax = (1 + a) * 2^E; then round(log2(amax / sf)) =
+// floor(log2(amax / (sf sqrt 2))) + 1 = E - F + [a >= t].  t is irrational,
+// so with T = ceil(t * 2^23) the test is an integer compare of amax's
+// mantissa field (T = 2^23 never matches).  sf = 6 gives F = 3, T = 0x7C3B7.
+struct Fp4Scale {
+  int F;
+  uint32_t T;
+};
+
+// raw scale clamped at 2^-30: e >= -30; subnormal amax (and 0) lands on the
+// clamp for every sf >= 2^-64 (amax / sf < 2^-62).
+__device__ __forceinline__ int mxfp4_scale_exp(uint32_t amax_bits, Fp4Scale p) {
   int ef = (int)(amax_bits >> 23);
   if (ef == 0) return -30;
-  int e = ef - 127 - 3 + ((amax_bits & 0x7FFFFFu) >= 0x7C3B7u ? 1 : 0);
+  int e = ef - 127 - p.F + ((amax_bits & 0x7FFFFFu) >= p.T ? 1 : 0);
   return e < -30 ? -30 : e;
 }
 

@@ -27,9 +27,13 @@ hipError_t launch_quant_tile(const uint16_t* x, int64_t R, int64_t C, int64_t ld
                              uint8_t* q_row, uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT,
                              hipStream_t st, int batch = 1, BatchStrides bs = BatchStrides{0, 0, 0, 0, 0});
 
-// MXFP4 quant-dequant
-hipError_t launch_qdq_fp4(const float* x, float* y, int64_t rows, int64_t L,
-                          uint8_t* codes, uint8_t* scales, hipStream_t st);
+// MXFP4 quant-dequant.  (F, T) encode the scale factor's exponent threshold;
+// fp4_scale_params computes them and rejects factors outside [2^-64, 2^64).
+bool fp4_scale_params(float scale_factor, int* F, uint32_t* T);
+hipError_t launch_qdq_fp4(const float* x, float* y, int64_t rows, int64_t L, int F, uint32_t T,
+                          uint8_t* codes, uint8_t* scales, uint8_t* sat_mask, hipStream_t st);
+hipError_t launch_ste_backward_fp4(const float* grad_y, const uint8_t* sat_mask, float* grad_x,
+                                   int64_t rows, int64_t L, hipStream_t st);
 
 // Block-scaled GEMMs.  mode 0: dense (G = 1, no group_end); 1: ragged M; 2: ragged K.
 hipError_t launch_gemm(int mode, const uint8_t* A, const uint8_t* sA, const uint8_t* B,

@@ -1,10 +1,15 @@
 // MXFP4 quantise-dequantise for gfx950 (AMCT FakeQuant article, section 2
 // "MXFP4 数值模型" and section 3.3): blocks of 32 along the last dim, each row
-// padded on its own; scale 2^round(log2(max|x|/6)) with the raw scale clamped
-// at 2^-30 (round taken exactly); element -> nearest E2M1 codebook value with
-// ties to the larger magnitude (the page's midpoint cascade); output
-// sign(x) * code * scale.  One fused pass: read fp32 once, write fp32 once
-// (plus optional packed nibbles and scale bytes).
+// padded on its own; scale 2^round(log2(max|x| / scale_factor)) with the raw
+// scale clamped at 2^-30 (round taken exactly; scale_factor 6 by default);
+// element -> nearest E2M1 codebook value with ties to the larger magnitude
+// (the page's midpoint cascade); output sign(x) * code * scale.  One fused
+// pass: read fp32 once, write fp32 once, plus optional packed nibbles, scale
+// bytes and the clipped-STE saturation mask (section 4.1): one bit per
+// element, set where |x| > 6 * scale, i.e. where the quantiser clipped.
+// The STE backward reads that mask and passes the gradient where it is clear.
+#include <string.h>
+
 #include "mxq_device.h"
 #include "mxq_internal.h"
 
@@ -14,23 +19,28 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Four elements of one lane -> output bits, nibbles (packed into 16 bits).
+// Four elements of one lane -> output bits, nibbles (packed into 16 bits) and
+// saturation bits (low 4 bits).
 struct Qdq4 {
   uint32_t out[4];
   uint32_t nibbles;
+  uint32_t sat;
 };
 
 __device__ __forceinline__ Qdq4 qdq4(const uint32_t (&xb)[4], int e) {
-  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, e in [-30, 125]
   Qdq4 r;
   r.nibbles = 0;
+  r.sat = 0;
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const uint32_t sign = xb[j] & 0x80000000u;
-    const float yabs = __uint_as_float(xb[j] & 0x7FFFFFFFu) * inv;  // exact
+    // |x| * 2^-e: exact wherever the result is normal; a subnormal result is
+    // below 2^-126 and maps to code 0 however it rounds.
+    const float yabs = __builtin_amdgcn_ldexpf(__uint_as_float(xb[j] & 0x7FFFFFFFu), -e);
     const uint32_t idx = mxfp4_index(yabs);
     r.out[j] = mxfp4_value_bits(idx, e, sign);
     r.nibbles |= ((sign >> 28) | idx) << (4 * j);
+    r.sat |= (uint32_t)(yabs > 6.0f) << j;
   }
   return r;
 }
@@ -45,29 +55,44 @@ __device__ __forceinline__ uint32_t oct_max(uint32_t v) {
   return max(v, dpp_half_mirror(v));
 }
 
-// L % 32 == 0 and 16-byte aligned x / y: the tensor is a flat run of blocks.
+// OR over the eight lanes of a block (each lane contributes disjoint bits)
+__device__ __forceinline__ uint32_t oct_or(uint32_t v) {
+  v |= dpp_xor1(v);
+  v |= dpp_xor2(v);
+  return v | dpp_half_mirror(v);
+}
+
+// L % 32 == 0 and 16-byte aligned x / y: the tensor is a flat run of blocks,
+// chunk i = elements 4i..4i+3, block i / 8.
 __global__ __launch_bounds__(kThreads) void qdq_flat_kernel(const float* __restrict__ x,
                                                            float* __restrict__ y, int64_t n_chunks,
-                                                           uint8_t* __restrict__ codes,
-                                                           uint8_t* __restrict__ scales) {
+                                                           Fp4Scale p, uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ scales,
+                                                           uint32_t* __restrict__ sat_mask) {
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_chunks;
        i += (int64_t)gridDim.x * kThreads) {
     const uint4 v = reinterpret_cast<const uint4*>(x)[i];
     const uint32_t xb[4] = {v.x, v.y, v.z, v.w};
     const uint32_t amax = oct_max(absmax4(xb));
-    const int e = mxfp4_scale_exp(amax);
+    const int e = mxfp4_scale_exp(amax, p);
     const Qdq4 r = qdq4(xb, e);
     reinterpret_cast<uint4*>(y)[i] = make_uint4(r.out[0], r.out[1], r.out[2], r.out[3]);
     if (codes) reinterpret_cast<uint16_t*>(codes)[i] = (uint16_t)r.nibbles;
     if (scales && (i & 7) == 0) scales[i >> 3] = (uint8_t)(e + 127);
+    if (sat_mask) {
+      const uint32_t word = oct_or(r.sat << (4 * (i & 7)));
+      if ((i & 7) == 0) sat_mask[i >> 3] = word;
+    }
   }
 }
 
 // General L: eight lanes per (row, block), four guarded scalar elements each.
 __global__ __launch_bounds__(kThreads) void qdq_rows_kernel(const float* __restrict__ x,
                                                            float* __restrict__ y, int64_t rows,
-                                                           int64_t L, uint8_t* __restrict__ codes,
-                                                           uint8_t* __restrict__ scales) {
+                                                           int64_t L, Fp4Scale p,
+                                                           uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ scales,
+                                                           uint32_t* __restrict__ sat_mask) {
   const int64_t nbr = (L + 31) / 32;  // blocks per row
   const int64_t n_chunks = rows * nbr * 8;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_chunks;
@@ -79,33 +104,108 @@ __global__ __launch_bounds__(kThreads) void qdq_rows_kernel(const float* __restr
 #pragma unroll
     for (int j = 0; j < 4; j++) xb[j] = col + j < L ? __float_as_uint(x[row * L + col + j]) : 0u;
     const uint32_t amax = oct_max(absmax4(xb));
-    const int e = mxfp4_scale_exp(amax);
+    const int e = mxfp4_scale_exp(amax, p);
     const Qdq4 r = qdq4(xb, e);
 #pragma unroll
     for (int j = 0; j < 4; j++)
       if (col + j < L) y[row * L + col + j] = __uint_as_float(r.out[j]);
     if (codes) *reinterpret_cast<uint16_t*>(codes + row * (nbr * 16) + col / 2) = (uint16_t)r.nibbles;
     if (scales && (i & 7) == 0) scales[blk] = (uint8_t)(e + 127);
+    if (sat_mask) {
+      // padding elements are 0 and never saturate, so their bits stay clear
+      const uint32_t word = oct_or(r.sat << (4 * (i & 7)));
+      if ((i & 7) == 0) sat_mask[blk] = word;  // row stride Lp/8 bytes = nbr words
+    }
   }
+}
+
+// Clipped STE backward, flat layout: grad_x = bit ? 0 : grad_y.
+// grad_x may alias grad_y (each element is read, then written, by one lane).
+__global__ __launch_bounds__(kThreads) void ste_flat_kernel(const float* gy, const uint32_t* __restrict__ sat_mask,
+                                                           float* gx, int64_t n_chunks) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_chunks;
+       i += (int64_t)gridDim.x * kThreads) {
+    const uint4 g = reinterpret_cast<const uint4*>(gy)[i];
+    const uint32_t m = sat_mask[i >> 3] >> (4 * (i & 7));
+    reinterpret_cast<uint4*>(gx)[i] = make_uint4(m & 1u ? 0u : g.x, m & 2u ? 0u : g.y,
+                                                 m & 4u ? 0u : g.z, m & 8u ? 0u : g.w);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void ste_rows_kernel(const float* gy, const uint32_t* __restrict__ sat_mask,
+                                                           float* gx, int64_t rows, int64_t L) {
+  const int64_t nbr = (L + 31) / 32;
+  const int64_t n_chunks = rows * nbr * 8;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_chunks;
+       i += (int64_t)gridDim.x * kThreads) {
+    const int64_t blk = i >> 3;
+    const int64_t row = blk / nbr;
+    const int64_t col = (blk - row * nbr) * 32 + (i & 7) * 4;
+    const uint32_t m = sat_mask[blk] >> (4 * (i & 7));
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+      if (col + j < L) {
+        const int64_t o = row * L + col + j;
+        const float g = gy[o];
+        gx[o] = (m >> j) & 1u ? 0.0f : g;
+      }
+  }
+}
+
+// One chunk per thread and one workgroup per 256 chunks (4 KB of fp32),
+// capped only by the grid-size limit: measured on MI355X, many short
+// workgroups over contiguous chunks stream HBM faster (a plain copy:
+// 6.1 TB/s) than a grid-stride loop over a CU-sized grid (5.1-5.4 TB/s).
+int grid_for(int64_t n_chunks) {
+  const int cap = 0x7FFFFFFF / kThreads;
+  const int64_t want = (n_chunks + kThreads - 1) / kThreads;
+  return (int)(want < cap ? want : cap);
 }
 
 }  // namespace
 
-hipError_t launch_qdq_fp4(const float* x, float* y, int64_t rows, int64_t L, uint8_t* codes,
-                          uint8_t* scales, hipStream_t st) {
-  // One chunk per thread and one workgroup per 256 chunks (4 KB of fp32),
-  // capped only by the grid-size limit: measured on MI355X, many short
-  // workgroups over contiguous chunks stream HBM faster (a plain copy:
-  // 6.1 TB/s) than a grid-stride loop over a CU-sized grid (5.1-5.4 TB/s).
-  const int cap = 0x7FFFFFFF / kThreads;
+bool fp4_scale_params(float scale_factor, int* F, uint32_t* T) {
+  uint32_t b;
+  memcpy(&b, &scale_factor, 4);
+  const int ef = (int)(b >> 23);  // sign bit included: negatives fail the range test
+  if (ef < 127 - 64 || ef > 127 + 63) return false;  // sf in [2^-64, 2^64), normal, positive
+  const uint64_t ms = (1u << 23) | (b & 0x7FFFFFu);    // sf = ms * 2^(ef - 150)
+  // (1 + f) * sqrt(2) >= 2 exactly when ms^2 >= 2^47: then F is one above sf's exponent
+  const int d = ms * ms >= (1ull << 47) ? 1 : 0;
+  *F = ef - 127 + d;
+  // smallest M = 2^23 + T with M / 2^23 >= (1 + t) = ms * sqrt(2) / 2^(23 + d):
+  // M^2 >= 2 ms^2 (d = 0) or 2 M^2 >= ms^2 (d = 1), compared in integers
+  auto ok = [&](uint64_t M) { return d ? 2 * M * M >= ms * ms : M * M >= 2 * ms * ms; };
+  uint64_t M = (uint64_t)(d ? (double)ms * 0.70710678118654752 : (double)ms * 1.4142135623730951);
+  while (M < (1ull << 23)) M++;
+  while (!ok(M)) M++;
+  while (M > (1ull << 23) && ok(M - 1)) M--;
+  *T = (uint32_t)(M - (1ull << 23));
+  return true;
+}
+
+hipError_t launch_qdq_fp4(const float* x, float* y, int64_t rows, int64_t L, int F, uint32_t T,
+                          uint8_t* codes, uint8_t* scales, uint8_t* sat_mask, hipStream_t st) {
+  const Fp4Scale p{F, T};
   const bool flat = L % 32 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)y % 16 == 0;
   const int64_t n_chunks = flat ? rows * L / 4 : rows * ((L + 31) / 32) * 8;
-  const int64_t want = (n_chunks + kThreads - 1) / kThreads;
-  const int grid = (int)(want < cap ? want : cap);
+  uint32_t* mask = reinterpret_cast<uint32_t*>(sat_mask);
   if (flat)
-    qdq_flat_kernel<<<grid, kThreads, 0, st>>>(x, y, n_chunks, codes, scales);
+    qdq_flat_kernel<<<grid_for(n_chunks), kThreads, 0, st>>>(x, y, n_chunks, p, codes, scales, mask);
   else
-    qdq_rows_kernel<<<grid, kThreads, 0, st>>>(x, y, rows, L, codes, scales);
+    qdq_rows_kernel<<<grid_for(n_chunks), kThreads, 0, st>>>(x, y, rows, L, p, codes, scales, mask);
+  return hipGetLastError();
+}
+
+hipError_t launch_ste_backward_fp4(const float* grad_y, const uint8_t* sat_mask, float* grad_x,
+                                   int64_t rows, int64_t L, hipStream_t st) {
+  const bool flat = L % 32 == 0 && (uintptr_t)grad_y % 16 == 0 && (uintptr_t)grad_x % 16 == 0;
+  const int64_t n_chunks = flat ? rows * L / 4 : rows * ((L + 31) / 32) * 8;
+  const uint32_t* mask = reinterpret_cast<const uint32_t*>(sat_mask);
+  if (flat)
+    ste_flat_kernel<<<grid_for(n_chunks), kThreads, 0, st>>>(grad_y, mask, grad_x, n_chunks);
+  else
+    ste_rows_kernel<<<grid_for(n_chunks), kThreads, 0, st>>>(grad_y, mask, grad_x, rows, L);
   return hipGetLastError();
 }
 

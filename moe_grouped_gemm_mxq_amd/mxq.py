@@ -42,8 +42,8 @@ MAX_GROUPS = 1024
 
 EXPORTED = [
     "mxq_abi_version", "mxq_last_error", "mxq_device_check", "mxq_grouped_cols_max",
-    "mxq_quantize", "mxq_quantize_batched", "mxq_quantize_grouped", "mxq_qdq_fp4", "mxq_gemm",
-    "mxq_grouped_gemm",
+    "mxq_quantize", "mxq_quantize_batched", "mxq_quantize_grouped", "mxq_qdq_fp4", "mxq_qdq_fp4_ex",
+    "mxq_ste_backward_fp4", "mxq_fp4_scale_threshold", "mxq_gemm", "mxq_grouped_gemm",
     "mxq_validate_group_end",
 ]
 
@@ -64,6 +64,9 @@ def _load(path: str = LIB_PATH):
         "mxq_quantize_batched": ([P, I64, I64, I64, I64, I64, I, P, P, P, P, P], I),
         "mxq_quantize_grouped": ([P, I64, I64, I64, P, I32, I64, I, P, P, P, P, P], I),
         "mxq_qdq_fp4": ([P, P, I64, I64, P, P, P], I),
+        "mxq_qdq_fp4_ex": ([P, P, I64, I64, ctypes.c_float, P, P, P, P], I),
+        "mxq_ste_backward_fp4": ([P, P, P, I64, I64, P], I),
+        "mxq_fp4_scale_threshold": ([ctypes.c_float, P, P], I),
         "mxq_gemm": ([P, P, P, P, P, I64, I64, I64, I64, I, P], I),
         "mxq_grouped_gemm": ([I, P, P, P, P, P, I64, I64, I64, P, I32, I, P], I),
         "mxq_validate_group_end": ([P, I32, I64, P, P], I),
@@ -203,6 +206,54 @@ def mxq_qdq_fp4(x, y, codes=None, scales=None, stream=None):
                             _stream(stream, x.device)), "mxq_qdq_fp4")
 
 
+def _rows_L(x):
+    L = x.shape[-1] if x.dim() else 1
+    return (x.numel() // L if L else 0), L
+
+
+def _need_u8(t, name, shape):
+    if t is None:
+        return
+    _need(t, torch.uint8, name)
+    if tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous with shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def mxq_qdq_fp4_ex(x, y, scale_factor=6.0, codes=None, scales=None, sat_mask=None, stream=None):
+    """As mxq_qdq_fp4 with a runtime scale factor and the optional saturation
+    mask uint8 [rows][ceil32(L)/8] (bit j of byte k: element 8k+j clipped)."""
+    _need(x, torch.float32, "x")
+    _need(y, torch.float32, "y")
+    if not (x.is_contiguous() and y.is_contiguous()) or x.shape != y.shape:
+        raise ValueError("x and y must be contiguous and of the same shape")
+    rows, L = _rows_L(x)
+    _need_u8(codes, "codes", (rows, ceil32(L) // 2))
+    _need_u8(scales, "scales", (rows, ceil32(L) // BLOCK))
+    _need_u8(sat_mask, "sat_mask", (rows, ceil32(L) // 8))
+    _check(_lib.mxq_qdq_fp4_ex(_ptr(x), _ptr(y), rows, L, float(scale_factor), _ptr(codes), _ptr(scales),
+                               _ptr(sat_mask), _stream(stream, x.device)), "mxq_qdq_fp4_ex")
+
+
+def mxq_ste_backward_fp4(grad_y, sat_mask, grad_x, stream=None):
+    """grad_x = 0 where sat_mask marks a clipped element, grad_y elsewhere."""
+    _need(grad_y, torch.float32, "grad_y")
+    _need(grad_x, torch.float32, "grad_x")
+    if not (grad_y.is_contiguous() and grad_x.is_contiguous()) or grad_y.shape != grad_x.shape:
+        raise ValueError("grad_y and grad_x must be contiguous and of the same shape")
+    rows, L = _rows_L(grad_y)
+    _need_u8(sat_mask, "sat_mask", (rows, ceil32(L) // 8))
+    _check(_lib.mxq_ste_backward_fp4(_ptr(grad_y), _ptr(sat_mask), _ptr(grad_x), rows, L,
+                                     _stream(stream, grad_y.device)), "mxq_ste_backward_fp4")
+
+
+def mxq_fp4_scale_threshold(scale_factor):
+    """Host only: (F, T) of the exponent rule for this scale factor."""
+    F, T = ctypes.c_int32(), ctypes.c_uint32()
+    _check(_lib.mxq_fp4_scale_threshold(float(scale_factor), ctypes.byref(F), ctypes.byref(T)),
+           "mxq_fp4_scale_threshold")
+    return F.value, T.value
+
+
 def mxq_gemm(A, sA, B, sB, C, stream=None):
     """A uint8 [M][K] + scales scale_shape(M, K/32), B [N][K] + scale_shape(N, K/32) -> C fp32 [M][ldc >= N]."""
     for t, n in ((A, "A"), (sA, "sA"), (B, "B"), (sB, "sB")):
@@ -316,6 +367,26 @@ def qdq_fp4(x, want_codes=False, stream=None):
         scales = _u8((rows, ceil32(L) // BLOCK), x.device)
     mxq_qdq_fp4(x, y, codes, scales, stream)
     return (y, codes, scales) if want_codes else y
+
+
+def qdq_fp4_ste(x, scale_factor=6.0, want_codes=False, stream=None):
+    """Forward of the clipped-STE fake quantiser: returns (y, sat_mask) or,
+    with want_codes, (y, sat_mask, codes, scales)."""
+    rows, L = _rows_L(x)
+    y = torch.empty_like(x)
+    mask = _u8((rows, ceil32(L) // 8), x.device)
+    codes = scales = None
+    if want_codes:
+        codes = _u8((rows, ceil32(L) // 2), x.device)
+        scales = _u8((rows, ceil32(L) // BLOCK), x.device)
+    mxq_qdq_fp4_ex(x, y, scale_factor, codes, scales, mask, stream)
+    return (y, mask, codes, scales) if want_codes else (y, mask)
+
+
+def ste_backward_fp4(grad_y, sat_mask, stream=None):
+    grad_x = torch.empty_like(grad_y)
+    mxq_ste_backward_fp4(grad_y, sat_mask, grad_x, stream)
+    return grad_x
 
 
 def gemm(A, sA, B, sB, stream=None):

@@ -110,6 +110,16 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
                 P(0), P(0), P(0)) == 1
     assert "x_stride" in err(lib)
     assert call(lib, "mxq_validate_group_end", FAKE, ctypes.c_int32(2000), I64(5), FAKE, P(0)) == 1
+    # MXFP4 with a scale factor: factor out of range, misaligned mask
+    F32 = ctypes.c_float
+    for sf in (0.0, -6.0, float("inf"), float("nan"), 2.0 ** 64, 2.0 ** -65, 1e-40):
+        assert call(lib, "mxq_qdq_fp4_ex", FAKE, FAKE, I64(2), I64(64), F32(sf), P(0), P(0), P(0), P(0)) == 1
+    assert "scale_factor" in err(lib)
+    assert call(lib, "mxq_qdq_fp4_ex", FAKE, FAKE, I64(2), I64(64), F32(6.0), P(0), P(0), P(0x1002), P(0)) == 1
+    # STE backward: NULL mask, partial overlap of grad_x and grad_y
+    assert call(lib, "mxq_ste_backward_fp4", FAKE, P(0), FAKE, I64(2), I64(64), P(0)) == 1
+    assert call(lib, "mxq_ste_backward_fp4", P(0x1000), FAKE, P(0x1010), I64(2), I64(64), P(0)) == 1
+    assert "overlap" in err(lib)
 
 
 def _gpu_present():
@@ -132,3 +142,62 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
                        env=env, capture_output=True, text=True)
     assert r.returncode != 0
     assert "RuntimeError" in r.stderr and "libmxq.so not found" in r.stderr
+
+
+def _threshold(lib, sf):
+    F, T = ctypes.c_int32(), ctypes.c_uint32()
+    rc = call(lib, "mxq_fp4_scale_threshold", ctypes.c_float(sf), ctypes.byref(F), ctypes.byref(T))
+    return rc, F.value, T.value
+
+
+def _exact_threshold(sf):
+    """F = floor(log2(sf*sqrt2)), T = ceil((sf*sqrt2/2^F - 1) * 2^23), from
+    rationals: 4^F <= 2 sf^2 < 4^(F+1); T is the least integer with
+    ((2^23 + T) / 2^23)^2 >= 2 sf^2 / 4^F."""
+    from fractions import Fraction
+    q = 2 * Fraction(sf) ** 2
+    F = 0
+    while Fraction(4) ** F > q:
+        F -= 1
+    while Fraction(4) ** (F + 1) <= q:
+        F += 1
+    r = q / Fraction(4) ** F                   # (1 + t)^2 in [1, 4)
+    lo, hi = 0, 1 << 23                        # least T in [0, 2^23] with ((2^23+T)/2^23)^2 >= r
+    while lo < hi:
+        mid = (lo + hi) // 2
+        if Fraction((1 << 23) + mid, 1 << 23) ** 2 >= r:
+            hi = mid
+        else:
+            lo = mid + 1
+    return F, lo
+
+
+def test_fp4_scale_threshold_matches_exact_rationals(lib):
+    import numpy as np
+    assert _threshold(lib, 6.0) == (0, 3, 0x7C3B7)
+    rng = np.random.default_rng(1)
+    sfs = [1.0, 2.0 ** -64, float(np.nextafter(np.float32(2.0 ** 64), np.float32(0))), 0.75, 7.25, 12.0,
+           float(np.float32(2 ** 0.5)), float(np.nextafter(np.float32(2 ** 0.5), np.float32(2))),
+           float(np.nextafter(np.float32(2 ** 0.5), np.float32(0)))]
+    sfs += [float(v) for v in (2.0 ** rng.uniform(-60, 60, 40)).astype(np.float32)]
+    for sf in sfs:
+        rc, F, T = _threshold(lib, sf)
+        assert rc == 0 and (F, T) == _exact_threshold(sf), sf
+    for sf in (0.0, -1.0, float("inf"), float("nan"), 2.0 ** 64, 1e-30):
+        assert _threshold(lib, sf)[0] == 1
+
+
+def test_fp4_exponent_rule_from_threshold_matches_oracle(lib):
+    """The kernels' exponent rule E - F + (mantissa >= T), clamped at -30,
+    applied to the host helper's (F, T), gives the oracle's scale bytes."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(4)
+    for sf in (6.0, 5.0, 0.75, 13.5, 1.0):
+        _, F, T = _threshold(lib, sf)
+        x = (rng.standard_normal((64, 32)) * 2.0 ** rng.integers(-40, 40, (64, 1))).astype(np.float32)
+        _, _, s, _ = oracle.mxfp4_qdq_ex(x, sf)
+        amax = np.abs(x).max(axis=1).view(np.uint32).astype(np.int64)
+        e = (amax >> 23) - 127 - F + ((amax & 0x7FFFFF) >= T)
+        e = np.where(amax >> 23 == 0, -30, np.maximum(e, -30))
+        assert np.array_equal(s[:, 0].astype(np.int64) - 127, e), sf

@@ -99,6 +99,36 @@ def test_linear_forward_small_end_to_end():
     print(f"linear 256x512x256: max err/sum|ab| = {ratio:.3e}")
 
 
+def test_dense_fb_split_equals_dual():
+    """fb-split quantises X by rows and W by columns in the forward and
+    re-quantises X along M and W along N in the backward; every copy and the
+    input / weight gradients equal the dual-axis schedule's bit for bit."""
+    m = mxq()
+    M, K, N = 300, 544, 260
+    X = scaled_randn((M, K), 31, lo=-6, hi=6)
+    W = scaled_randn((K, N), 32, lo=-6, hi=6, axis=1)
+    dY = scaled_randn((M, N), 33, lo=-6, hi=6)
+    Xd, Wd, dYd = X.cuda(), W.cuda(), dY.cuda()
+    dual_x, dual_w = m.quantize(Xd, 3), m.quantize(Wd, 3)
+    fb_x = {**m.quantize(Xd, 1), **m.quantize(Xd, 2)}   # forward rows, backward columns
+    fb_w = {**m.quantize(Wd, 2), **m.quantize(Wd, 1)}
+    for k in ("q_row", "s_row", "q_colT", "s_colT"):
+        assert torch.equal(dual_x[k], fb_x[k]) and torch.equal(dual_w[k], fb_w[k]), k
+    qy = m.quantize(dYd, 3)
+    grads = []
+    for qx, qw in ((dual_x, dual_w), (fb_x, fb_w)):
+        dX = m.gemm(qy["q_row"], qy["s_row"], qw["q_row"], qw["s_row"])
+        dW = m.gemm(qx["q_colT"], qx["s_colT"], qy["q_colT"], qy["s_colT"])
+        grads.append((dX, dW))
+    torch.cuda.synchronize()
+    assert torch.equal(grads[0][0], grads[1][0]) and torch.equal(grads[0][1], grads[1][1])
+    # and the gradients are right: dX = dY W^T against the oracle
+    A, sA = oracle.mxfp8_quant_row(bits(dY))
+    B, sB = oracle.mxfp8_quant_row(bits(W))
+    Cr, Ca = oracle.gemm(A, sA, B, sB)
+    assert_gemm_close(host(grads[1][0]), Cr, Ca, "fb-split dgrad", hw_bound=mfma_group_bound(A, sA, B, sB))
+
+
 # ------------------------------------------------------------------ full size
 @pytest.fixture(scope="module")
 def dense_full():

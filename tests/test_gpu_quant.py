@@ -56,6 +56,99 @@ def test_qdq_full_size_8192x8192_one_percent_rows_scaled():
     check_qdq(x, "qdq 8192x8192")
 
 
+# ------------------------------------------ MXFP4 with a scale factor, clipped STE
+FACTORS = [6.0, 5.0, 7.25, 1.0, 0.75, 12.0, 3.0]
+
+
+def check_qdq_ex(x: torch.Tensor, sf: float, what: str, xdev=None):
+    """GPU y, codes, scales and saturation mask vs the oracle, bit for bit."""
+    m = mxq()
+    xd = x.cuda() if xdev is None else xdev
+    y, mask, codes, scales = m.qdq_fp4_ste(xd, sf, want_codes=True)
+    torch.cuda.synchronize()
+    yr, cr, sr, mr = oracle.mxfp4_qdq_ex(x.numpy(), sf)
+    assert np.array_equal(host(y).view(np.uint32), yr.view(np.uint32)), f"{what} sf={sf}: values differ"
+    assert np.array_equal(host(codes), cr), f"{what} sf={sf}: nibbles differ"
+    assert np.array_equal(host(scales), sr), f"{what} sf={sf}: scales differ"
+    assert np.array_equal(host(mask), mr), f"{what} sf={sf}: saturation masks differ"
+    return mask, mr
+
+
+@pytest.mark.parametrize("sf", FACTORS)
+@pytest.mark.parametrize("shape", [(1, 1), (5, 32), (3, 100), (9, 31), (64, 256), (2, 4097)])
+def test_qdq_scale_factor_and_mask_bitexact(shape, sf):
+    g = torch.Generator().manual_seed(sum(shape) + int(sf * 4))
+    x = torch.randn(shape, generator=g) * torch.exp2(torch.randint(-30, 30, (shape[0], 1), generator=g).float())
+    check_qdq_ex(x, sf, f"qdq_ex {shape}")
+
+
+@pytest.mark.parametrize("sf", FACTORS)
+def test_qdq_scale_factor_threshold_neighbours(sf):
+    """Block maxima at the fp32 neighbours (+-3 ulps) of sf*sqrt(2)*2^n, where
+    the exponent steps, in many binades."""
+    rows = []
+    for n in range(-28, 100, 7):
+        a0 = np.float32(np.float32(sf) * np.sqrt(2.0) * 2.0 ** n)
+        a = a0
+        for _ in range(3):
+            a = np.nextafter(a, np.float32(0))
+        for _ in range(7):
+            rows.append([a] + [a * f for f in (0.04, 0.13, 0.2, 0.37, 0.55, 0.71, -0.9)] + [0.0] * 24)
+            a = np.nextafter(a, np.float32(np.inf))
+    check_qdq_ex(torch.tensor(np.array(rows, np.float32)), sf, "thresholds")
+
+
+def test_qdq_scale_factor_unaligned_input_takes_general_path():
+    """x and y 4 bytes past a 16-byte boundary with L % 32 == 0: the general
+    (per-row) kernel must give the same bits."""
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn(17 * 64, generator=g) * 3
+    base = torch.empty(17 * 64 + 1, device="cuda")
+    base[1:] = x.cuda()
+    check_qdq_ex(x.view(17, 64), 7.25, "unaligned", xdev=base[1:].view(17, 64))
+
+
+def test_qdq_ex_at_six_equals_plain_qdq():
+    m = mxq()
+    x = workloads.qdq_small()[0].cuda()
+    y0, c0, s0 = m.qdq_fp4(x, want_codes=True)
+    y1, _, c1, s1 = m.qdq_fp4_ste(x, 6.0, want_codes=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int32), y1.view(torch.int32)) and torch.equal(c0, c1) and torch.equal(s0, s1)
+
+
+@pytest.mark.parametrize("shape", [(6, 45), (8, 64), (3, 4097), (1, 1)])
+@pytest.mark.parametrize("inplace", [False, True])
+def test_ste_backward_matches_oracle(shape, inplace):
+    m = mxq()
+    g = torch.Generator().manual_seed(shape[1])
+    x = torch.randn(shape, generator=g)
+    x[:, ::7] *= 4.0
+    gy = torch.randn(shape, generator=g)
+    mask, mr = check_qdq_ex(x, 8.0, f"ste fwd {shape}")
+    gyd = gy.cuda()
+    if inplace:
+        m.mxq_ste_backward_fp4(gyd, mask, gyd)
+        gx = gyd
+    else:
+        gx = m.ste_backward_fp4(gyd, mask)
+    torch.cuda.synchronize()
+    want = oracle.mxfp4_ste_backward(gy.numpy(), mr)
+    assert np.array_equal(host(gx).view(np.uint32), want.view(np.uint32))
+
+
+def test_ste_full_size_8192x8192():
+    """The QDQ workload at full size with the mask, then the masked backward."""
+    m = mxq()
+    x = workloads.qdq_large()
+    mask, mr = check_qdq_ex(x, 6.0, "qdq_ex 8192x8192")
+    gy = torch.randn(x.shape, generator=torch.Generator().manual_seed(1))
+    gx = m.ste_backward_fp4(gy.cuda(), mask)
+    torch.cuda.synchronize()
+    want = oracle.mxfp4_ste_backward(gy.numpy(), mr)
+    assert np.array_equal(host(gx).view(np.uint32), want.view(np.uint32))
+
+
 # ------------------------------------------------------------------ MXFP8
 SHAPES = [(1, 1), (1, 32), (2, 33), (33, 2), (3, 17), (65, 65), (128, 128), (127, 129),
           (300, 257), (256, 1000), (1000, 264), (4097, 40)]
