@@ -50,6 +50,9 @@ def _declare(lib):
         "oracle_mxfp4_qdq_ex": ([P, P, I64, I64, ctypes.c_float, P, P, P], ctypes.c_int),
         "oracle_mxfp4_ste_backward": ([P, P, P, I64, I64], None),
         "oracle_gemm": ([P, P, P, P, I64, I64, I64, P, P], ctypes.c_int),
+        "oracle_mxfp4_dequant": ([P, P, I64, I64, P], None),
+        "oracle_gemm_fp4": ([P, P, P, P, I64, I64, I64, P, P], ctypes.c_int),
+        "oracle_gemm_fp4_sampled": ([P, P, P, P, I64, I64, I64, P, P, I64, P, P], ctypes.c_int),
         "oracle_gemm_sampled": ([P, P, P, P, I64, I64, I64, P, P, I64, P, P], ctypes.c_int),
         "oracle_grouped_gemm_ragged_m": ([P, P, P, P, I64, I64, I64, P, I32, P, P], ctypes.c_int),
         "oracle_grouped_gemm_ragged_m_sampled":
@@ -237,6 +240,43 @@ def mxfp4_ste_backward(grad_y: np.ndarray, mask: np.ndarray) -> np.ndarray:
     assert mask.shape == (rows, ceil32(L) // 8)
     lib().oracle_mxfp4_ste_backward(_p(grad_y), _p(mask), _p(gx), rows, L)
     return gx
+
+
+def mxfp4_dequant(codes: np.ndarray, scales: np.ndarray, L: int) -> np.ndarray:
+    """MXFP4 codes [rows][ceil32(L)/2] + row-major scales [rows][ceil32(L)/32] -> fp64 [rows][L]."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows = codes.shape[0]
+    assert codes.shape == (rows, ceil32(L) // 2) and scales.shape == (rows, ceil32(L) // BLOCK)
+    out = np.zeros((rows, L), np.float64)
+    lib().oracle_mxfp4_dequant(_p(codes), _p(scales), rows, L, _p(out))
+    return out
+
+
+def gemm_fp4(A, sA, B, sB):
+    """MXFP4 operands (codes [M][K/2], row-major scales [M][K/32]):
+    C[m][n] = sum_k deq(A)[m][k]*deq(B)[n][k]; returns (C, sum|products|) in fp64."""
+    A, sA, B, sB = (np.ascontiguousarray(t, dtype=np.uint8) for t in (A, sA, B, sB))
+    M, K = A.shape[0], A.shape[1] * 2
+    N = B.shape[0]
+    assert sA.shape == (M, K // BLOCK) and B.shape == (N, K // 2) and sB.shape == (N, K // BLOCK)
+    C = np.zeros((M, N), np.float64)
+    Cabs = np.zeros((M, N), np.float64)
+    _check(lib().oracle_gemm_fp4(_p(A), _p(sA), _p(B), _p(sB), M, N, K, _p(C), _p(Cabs)), "gemm_fp4")
+    return C, Cabs
+
+
+def gemm_fp4_sampled(A, sA, B, sB, mi, ni):
+    A, sA, B, sB = (np.ascontiguousarray(t, dtype=np.uint8) for t in (A, sA, B, sB))
+    M, K = A.shape[0], A.shape[1] * 2
+    N = B.shape[0]
+    mi = np.ascontiguousarray(mi, dtype=np.int64)
+    ni = np.ascontiguousarray(ni, dtype=np.int64)
+    C = np.zeros(len(mi), np.float64)
+    Cabs = np.zeros(len(mi), np.float64)
+    _check(lib().oracle_gemm_fp4_sampled(_p(A), _p(sA), _p(B), _p(sB), M, N, K, _p(mi), _p(ni), len(mi),
+                                         _p(C), _p(Cabs)), "gemm_fp4_sampled")
+    return C, Cabs
 
 
 # ---------------------------------------------------------------- GEMMs

@@ -396,6 +396,92 @@ void oracle_mxfp4_ste_backward(const float* grad_y, const uint8_t* sat_mask, flo
 }
 
 /* ---------------------------------------------------------------------- */
+/* MXFP4 operands: dequantisation and the block-scaled FP4 GEMM.            */
+
+/* OCP E2M1 element: bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa;
+ * exponent 0 is subnormal (0.5 * mantissa).  The eight magnitudes are the
+ * AMCT article's codebook {0, 0.5, 1, 1.5, 2, 3, 4, 6} (section 2). */
+static double fp4_decode(uint8_t nib)
+{
+    int e = (nib >> 1) & 3, m = nib & 1;
+    double mag = e == 0 ? 0.5 * m : (1.0 + 0.5 * m) * ldexp(1.0, e - 1);
+    return (nib & 8) ? -mag : mag;
+}
+
+/* codes [rows][Lp/2] (element 2j in the low nibble of byte j), scales
+ * [rows][Lp/32] E8M0 row-major, as written by oracle_mxfp4_qdq_ex ->
+ * out [rows][L] = decode(nibble) * 2^(scale - 127). */
+void oracle_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t L, double* out)
+{
+    int64_t Lp = ceil32(L);
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t c = 0; c < L; c++) {
+            uint8_t byte = codes[r * (Lp / 2) + c / 2];
+            uint8_t nib = (c % 2 == 0) ? (uint8_t)(byte & 0xF) : (uint8_t)(byte >> 4);
+            int s = scales[r * (Lp / MX_BLOCK) + c / MX_BLOCK];
+            out[r * L + c] = fp4_decode(nib) * ldexp(1.0, s - 127);
+        }
+}
+
+/* C[m][n] = sum_k deq(A)[m][k] * deq(B)[n][k] over MXFP4 operands: A codes
+ * [M][K/2] + scales [M][K/32], B codes [N][K/2] + scales [N][K/32] (the
+ * layout above), K % 32 == 0; fp64, with sum |products| beside it. */
+int oracle_gemm_fp4(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
+                    int64_t M, int64_t N, int64_t K, double* C, double* Cabs)
+{
+    if (M < 0 || N < 0 || K < 0 || K % MX_BLOCK) return 1;
+    double* Xa = (double*)malloc(sizeof(double) * (size_t)(M * K + 1));
+    double* Xb = (double*)malloc(sizeof(double) * (size_t)(N * K + 1));
+    if (!Xa || !Xb) { free(Xa); free(Xb); return 4; }
+    oracle_mxfp4_dequant(A, sA, M, K, Xa);
+    oracle_mxfp4_dequant(B, sB, N, K, Xb);
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t n = 0; n < N; n++) {
+            double acc = 0.0, accabs = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                double p = Xa[m * K + k] * Xb[n * K + k];
+                acc += p;
+                accabs += fabs(p);
+            }
+            C[m * N + n] = acc;
+            Cabs[m * N + n] = accabs;
+        }
+    free(Xa);
+    free(Xb);
+    return 0;
+}
+
+/* Selected outputs (mi[i], ni[i]) of the FP4 GEMM above. */
+int oracle_gemm_fp4_sampled(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
+                            int64_t M, int64_t N, int64_t K, const int64_t* mi, const int64_t* ni,
+                            int64_t count, double* C, double* Cabs)
+{
+    if (K % MX_BLOCK) return 1;
+    for (int64_t i = 0; i < count; i++)
+        if (mi[i] < 0 || mi[i] >= M || ni[i] < 0 || ni[i] >= N) return 1;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < count; i++) {
+        double a[MX_BLOCK], b[MX_BLOCK], acc = 0.0, accabs = 0.0;
+        for (int64_t k0 = 0; k0 < K; k0 += MX_BLOCK) {
+            /* one 32-block of row mi[i] of A and row ni[i] of B */
+            oracle_mxfp4_dequant(A + mi[i] * (K / 2) + k0 / 2, sA + mi[i] * (K / MX_BLOCK) + k0 / MX_BLOCK, 1,
+                                 MX_BLOCK, a);
+            oracle_mxfp4_dequant(B + ni[i] * (K / 2) + k0 / 2, sB + ni[i] * (K / MX_BLOCK) + k0 / MX_BLOCK, 1,
+                                 MX_BLOCK, b);
+            for (int j = 0; j < MX_BLOCK; j++) {
+                double p = a[j] * b[j];
+                acc += p;
+                accabs += fabs(p);
+            }
+        }
+        C[i] = acc;
+        Cabs[i] = accabs;
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
 /* Block-scaled GEMMs [TT]: C[m][n] = sum_k deq(A)[m][k] * deq(B)[n][k].    */
 /* Alongside each value the oracle returns sum_k |deq(A)*deq(B)|, the scale */
 /* of the tolerance an fp32-accumulating kernel is held to.                 */

@@ -185,6 +185,25 @@ def test_moe_wgrad_ragged_k_full_sampled(moe_full):
         assert int(torch.count_nonzero(dW[g]).item()) == 0, f"empty expert {g} has nonzero dW"
 
 
+def test_moe_gemms_write_every_output_deterministically(moe_full):
+    """Every output tile is written exactly as before when the outputs start as
+    NaN: the persistent tile walks (ragged M, interleaved ragged K) miss no tile
+    and give the same bits on a second run."""
+    m = mxq()
+    G, K, N = moe_full["W"].shape
+    T = moe_full["X"].shape[0]
+    qx, qw, qy, qxt, ge = moe_full["qx"], moe_full["qw"], moe_full["qy"], moe_full["qxt"], moe_full["ge"]
+    Y = torch.full((T, N), float("nan"), device="cuda")
+    m.mxq_grouped_gemm(m.MXQ_GG_RAGGED_M, qx["q_row"], qx["s_row"], qw["q_colT"], qw["s_colT"], Y, ge)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(Y).all()) and torch.equal(Y, moe_full["Y"])
+    del Y
+    dW = torch.full((G, K, N), float("nan"), device="cuda")
+    m.mxq_grouped_gemm(m.MXQ_GG_RAGGED_K, qxt["q_colT"], qxt["s_colT"], qy["q_colT"], qy["s_colT"], dW, ge)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(dW).all()) and torch.equal(dW, moe_full["dW"])
+
+
 def test_moe_batched_expert_quant_equals_per_expert(moe_full):
     """All 32 experts' dual-axis quantisation in one batched launch gives the
     per-expert launches' bytes exactly (those are checked against the oracle

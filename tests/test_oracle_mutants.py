@@ -11,6 +11,7 @@ import oracle
 sys.path.insert(0, os.path.dirname(__file__))
 import test_oracle_gemm as tg      # noqa: E402
 import test_oracle_mxfp4 as t4     # noqa: E402
+import test_oracle_mxfp4_gemm as t4g  # noqa: E402
 import test_oracle_mxfp8 as t8     # noqa: E402
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "mxq_oracle.c")
@@ -32,6 +33,14 @@ MUTANTS = {
     "fp4 ste mask row stride": ("int sat = (sat_mask[r * (Lp / 8) + c / 8] >> (c % 8)) & 1;",
                                 "int sat = (sat_mask[r * (L / 8) + c / 8] >> (c % 8)) & 1;",
                                 [t4.test_ste_backward_zeroes_only_clipped_elements]),
+    "fp4 dequant nibble order": ("uint8_t nib = (c % 2 == 0) ? (uint8_t)(byte & 0xF) : (uint8_t)(byte >> 4);",
+                                 "uint8_t nib = (c % 2 == 1) ? (uint8_t)(byte & 0xF) : (uint8_t)(byte >> 4);",
+                                 [lambda: t4g.test_dequant_reproduces_qdq_output((3, 17), 6.0)]),
+    "fp4 decode exponent bias": ("(1.0 + 0.5 * m) * ldexp(1.0, e - 1);", "(1.0 + 0.5 * m) * ldexp(1.0, e - 2);",
+                                 [t4g.test_dequant_of_every_nibble_is_the_page_codebook]),
+    "fp4 gemm operand rows shifted": ("double p = Xa[m * K + k] * Xb[n * K + k];",
+                                      "double p = Xa[m * K + k] * Xb[((n + 1) % N) * K + k];",
+                                      [t4g.test_gemm_fp4_equals_matmul_of_qdq_outputs]),
     "fp4 min scale 2^-31": ("#define FP4_MIN_SCALE_EXP (-30)", "#define FP4_MIN_SCALE_EXP (-31)",
                             [t4.test_zero_and_tiny_blocks_use_minimum_scale]),
     "fp4 drops sign of zero": ("double out = copysign(fp4_codebook[idx] * scale, v[i]);",
