@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MXFP8 GEMM & grouped-GEMM TFLOP/s (+quantize GB/s), % of MI355X roofline"
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
+PEAK_FP4_TFLOPS = 10100.0    # MI355X dense FP4 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 
 
@@ -335,6 +336,39 @@ def main():
         gbs = ste_bytes[k] / (ms * 1e-3) / 1e9
         fake_quant[k] = {"ms": round(ms, 4), "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
+    # ---------------------------------------------------------------- MXFP4 GEMM
+    # The dense linear's forward shape with E2M1 operands: X [M][K] and W^T
+    # [N][K] in fp32, quantised to MXFP4 GEMM operands, then the FP4 GEMM.
+    xf = X.float()
+    wtf = W.t().contiguous().float()
+    qa, sa = mxq.quantize_fp4(xf)
+    qb, sb = mxq.quantize_fp4(wtf)
+    Y4 = f32(M, N)
+    fp4_runs = []
+    for i in range(8):
+        tl = Timeline(torch)
+        tl("quant_fp4_operands")
+        mxq.mxq_quantize_fp4(xf, qa, sa)
+        mxq.mxq_quantize_fp4(wtf, qb, sb)
+        tl("gemm_fp4")
+        mxq.mxq_gemm(qa, sa, qb, sb, Y4, fmt=mxq.MXQ_FMT_E2M1)
+        tl(None)
+        if i >= 2:
+            fp4_runs.append(tl)
+    torch.cuda.synchronize()
+    d4 = {}
+    for tl in fp4_runs:
+        for k, v in tl.durations().items():
+            d4.setdefault(k, []).extend(v)
+    g_ms = sum(d4["gemm_fp4"]) / len(d4["gemm_fp4"])
+    q_ms = sum(d4["quant_fp4_operands"]) / len(d4["quant_fp4_operands"])
+    g_tf = 2.0 * M * N * K / (g_ms * 1e-3) / 1e12
+    q_gbs = (M + N) * K * (4 + 0.5 + 1 / 32) / (q_ms * 1e-3) / 1e9
+    mxfp4_gemm = {"shape": f"M{M} N{N} K{K}", "gemm_ms": round(g_ms, 4), "gemm_tflops": round(g_tf, 1),
+                  "frac_fp4_peak": round(g_tf / PEAK_FP4_TFLOPS, 4), "quant_ms": round(q_ms, 4),
+                  "quant_gbs": round(q_gbs, 1), "quant_frac_hbm_peak": round(q_gbs / PEAK_HBM_GBS, 4)}
+    del xf, wtf, qa, sa, qb, sb, Y4
+
     # ---------------------------------------------------------------- MoE schedules: time and memory
     schedules = {}
     for sched in ("dual", "fb_split"):
@@ -393,6 +427,7 @@ def main():
         "components": components,
         "dense_schedules": dense_sched,
         "mxfp4_clipped_ste": fake_quant,
+        "mxfp4_gemm": mxfp4_gemm,
         "moe_schedules": schedules,
     }
     print(json.dumps(out))

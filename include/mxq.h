@@ -75,8 +75,10 @@ typedef enum {
  * (both copies from one read of the input). */
 enum { MXQ_AXIS_ROW = 1, MXQ_AXIS_COLT = 2 };
 
-/* element format of a GEMM operand */
-typedef enum { MXQ_FMT_E4M3 = 0 } mxq_fmt;
+/* element format of a GEMM operand: E4M3 codes (one byte each, written by
+ * the MXFP8 quantisers) or E2M1 codes (two per byte, element 2j in the low
+ * nibble of byte j, written by mxq_quantize_fp4) */
+typedef enum { MXQ_FMT_E4M3 = 0, MXQ_FMT_E2M1 = 1 } mxq_fmt;
 
 /* grouped GEMM modes */
 typedef enum {
@@ -205,6 +207,22 @@ mxq_status mxq_ste_backward_fp4(const float* grad_y, const uint8_t* sat_mask, fl
 mxq_status mxq_fp4_scale_threshold(float scale_factor, int32_t* F, uint32_t* T);
 
 /*
+ * MXFP4 GEMM operand quantisation: the same block rule and element rounding
+ * as mxq_qdq_fp4_ex (AMCT FakeQuant article, section 2; scale_factor 6 is the
+ * default) without the dequantised output, with the scales in the layout
+ * the GEMMs read.  x fp32 [rows][L] device, 4-byte aligned; each row zero-
+ * padded to Lp = ceil32(L).  codes: device bytes [rows][Lp/2], 16-byte
+ * aligned, E2M1 nibbles as for mxq_qdq_fp4 (element 2j in the low nibble of
+ * byte j).  scales: E8M0 bytes, 32-row interleaved like the MXFP8 quantisers'
+ * (scale of row r, block b at ((r/32)*(Lp/32) + b)*32 + r%32 of a
+ * ceil32(rows)*(Lp/32)-byte array; bytes of rows past `rows` are not
+ * written).  A GEMM operand with K = Lp.  scale_factor as for
+ * mxq_qdq_fp4_ex.  rows, L >= 1.
+ */
+mxq_status mxq_quantize_fp4(const float* x, int64_t rows, int64_t L, float scale_factor, uint8_t* codes,
+                            uint8_t* scales, hipStream_t st);
+
+/*
  * Block-scaled GEMM C[m][n] = sum_k deq(A)[m][k] * deq(B)[n][k] (the FP8
  * linear GEMMs of the torchtitan-npu guide, "线性层低精度"), fp32
  * accumulation and fp32 output.  A codes [M][K] + scales (M rows);
@@ -212,7 +230,12 @@ mxq_status mxq_fp4_scale_threshold(float scale_factor, int32_t* F, uint32_t* T);
  * Forward Y = X W: A = row copy of X, B = colT copy of W [K][N].
  * Input gradient dX = dY W^T: A = row copy of dY, B = row copy of W.
  * Weight gradient dW = X^T dY: A = colT copy of X, B = colT copy of dY.
- * M, N >= 1; K >= 32, K % 32 == 0; ldc >= N.
+ * fmt MXQ_FMT_E2M1 (MXFP4 operands, the MXFP4 option of the guide's MoE
+ * recipe with the AMCT article's numeric model): A codes [M][K/2], B codes
+ * [N][K/2] as written by mxq_quantize_fp4 (rows of K elements), scales in
+ * the same interleaved layout.
+ * M, N >= 1; K >= 32, K % 32 == 0; ldc >= N.  Unknown fmt:
+ * MXQ_ERR_UNSUPPORTED.
  */
 mxq_status mxq_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
                     float* C, int64_t M, int64_t N, int64_t K, int64_t ldc, mxq_fmt fmt,
@@ -232,6 +255,10 @@ mxq_status mxq_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const
  *     C[g] = sum over group g's padded columns of deq(A) deq(B);
  *     an empty group gets exact zeros.  Expert weight gradient:
  *     A = grouped copy of X (M = hidden), B = grouped copy of dY (N = ffn).
+ * fmt MXQ_FMT_E2M1: MXFP4 operands as for mxq_gemm (codes K/2 bytes per row,
+ * expert g's B codes at byte g * N * K/2), MXQ_GG_RAGGED_M only (there is no
+ * E2M1 token-axis quantiser): MXQ_GG_RAGGED_K with E2M1 gives
+ * MXQ_ERR_UNSUPPORTED.
  * M, N >= 1; 1 <= G <= MXQ_MAX_GROUPS.
  */
 mxq_status mxq_grouped_gemm(mxq_gg_mode mode, const uint8_t* A, const uint8_t* sA,

@@ -49,25 +49,50 @@ constexpr int BM = 256, BN = 256, BK = 64;   // BK: codes (bytes) per MFMA step
 constexpr int BKS = 2 * BK;                   // codes per tile row per stage (two steps)
 constexpr int WM = 128, WN = 64;              // wave tile
 constexpr int TM = WM / 32, TN = WN / 32;     // MFMA blocks per wave
-constexpr int kTileBytes = BM * BKS;          // codes of one operand tile per stage (32 KB)
 constexpr int kScaleRegion = 4 * 4 * BM;      // one dword per (tile row, K-block) of one operand (4 KB)
-constexpr int kStageBytes = 2 * kTileBytes + 2 * kScaleRegion;  // A, B codes, A, B scales (72 KB)
+
+// Layout of one LDS stage per element format.  E4M3 codes take a byte, E2M1
+// codes (two per byte, element 2j in the low nibble) half of one, so a stage
+// of BKS elements per row holds 128 or 64 code bytes per row.
+template <bool FP4>
+struct Fmt {
+  static constexpr int kRowBytes = FP4 ? BKS / 2 : BKS;                  // code bytes per tile row
+  static constexpr int kChunks = kRowBytes / 16;                         // 16-byte chunks per row (8 / 4)
+  static constexpr int kElemsPerChunk = BKS / kChunks;                   // 16 / 32
+  static constexpr int kTileBytes = BM * kRowBytes;                      // per operand (32 KB / 16 KB)
+  static constexpr int kStageBytes = 2 * kTileBytes + 2 * kScaleRegion;  // A, B codes, A, B scales
+  static constexpr int kLoads = kTileBytes / (kThreads / 64) / 1024;     // dwordx4 loads per wave and operand
+  static constexpr int kLanesPerRow = kRowBytes / 16;                    // lanes of one load on one row
+};
 constexpr int kXcds = 8;                      // XCDs per MI355X; workgroups are dealt round robin
 constexpr int kGroupM = 8;                    // m-tiles per raster group
 
 enum Mode { kDense = 0, kRaggedM = 1, kRaggedK = 2 };
 
+// format codes of the f8f6f4 MFMA operands: 0 = E4M3, 4 = E2M1
+template <bool FP4>
 __device__ __forceinline__ v16f mfma_scaled(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FP4 ? 4 : 0, FP4 ? 4 : 0, 0, sa, 0, sb);
 }
 
-// LDS position of 16-byte chunk c (0..7) of tile row r (128 bytes per stage),
-// XOR-swizzled with f(r) = (r & 7) ^ ((r >> 3) & 1): a fragment read has its
-// lanes on consecutive rows at one chunk, and f makes any 8 aligned
-// consecutive rows land on 8 distinct 16-byte bank groups of a 128-byte bank
-// row (32 banks) and any 16 on 16 distinct groups of a 256-byte one (64
-// banks), so the read is conflict-free either way.
-__device__ __forceinline__ int swz(int r, int c) { return r * BKS + ((c ^ ((r & 7) ^ ((r >> 3) & 1))) << 4); }
+// LDS position of 16-byte chunk c of tile row r.  A fragment read has its
+// lanes on consecutive rows at one chunk.
+//  E4M3 (8 chunks, 128 bytes per row): XOR swizzle f(r) = (r & 7) ^ ((r >> 3)
+//    & 1) makes any 8 aligned consecutive rows land on 8 distinct 16-byte
+//    bank groups of a 128-byte bank row (32 banks) and any 16 on 16 distinct
+//    groups of a 256-byte one (64 banks);
+//  E2M1 (4 chunks, 64 bytes per row): rows r .. r+3 fill one 256-byte bank
+//    row and f(r) = (r >> 2) & 3 moves the chunk within each row's quarter
+//    for every group of four rows, so any 16 consecutive rows hit 16 distinct
+//    bank groups.
+// Either way the read is conflict-free.
+template <bool FP4>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (FP4)
+    return r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
+  else
+    return r * BKS + ((c ^ ((r & 7) ^ ((r >> 3) & 1))) << 4);
+}
 
 // One operand of one workgroup tile: tile rows [0, rows_valid), which are rows
 // row0 .. row0 + rows_valid - 1 of a matrix with codes at base + (r - row0)*ld
@@ -78,7 +103,8 @@ struct Operand {
   const uint8_t* base;   // codes of tile row 0
   const uint8_t* sbase;  // scale array of the whole matrix
   int64_t row0;
-  int64_t ld;
+  int64_t ld;    // code row pitch (bytes)
+  int64_t nblk;  // scale blocks per row (K / 32)
   int rows_valid;
 };
 
@@ -111,16 +137,27 @@ struct OperandAddr {
   uint32_t soff[2];      // per load: offset of the lane's scale row inside the groups
 };
 
-__device__ __forceinline__ int dma_chunk(int j, int lane) { return (lane & 7) ^ (lane >> 3) ^ (j & 1); }
+// E4M3: load j of wave w covers rows 8q .. 8q+7 (q = 4w + j), 8 lanes a row;
+// E2M1: rows 16q .. 16q+15 (q = 2w + j), 4 lanes a row.  Lane l fills slot
+// l % lanes-per-row of its row, which holds chunk slot ^ f(row).
+template <bool FP4>
+__device__ __forceinline__ int dma_chunk(int j, int lane) {
+  if constexpr (FP4)
+    return (lane & 3) ^ (lane >> 4);
+  else
+    return (lane & 7) ^ (lane >> 3) ^ (j & 1);
+}
 
+template <bool FP4>
 __device__ __forceinline__ OperandAddr make_addr(const Operand& op, int wave, int lane) {
+  using F = Fmt<FP4>;
   OperandAddr ad;
-  const int64_t nblk = op.ld / 32;
+  const int64_t nblk = op.nblk;
   ad.cbase = op.base;
   ad.sbase = op.sbase + (op.row0 >> 5) * nblk * 32;
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int row = min((wave * 4 + j) * 8 + (lane >> 3), op.rows_valid - 1);
+  for (int j = 0; j < F::kLoads; j++) {
+    const int row = min((wave * F::kLoads + j) * (64 / F::kLanesPerRow) + lane / F::kLanesPerRow, op.rows_valid - 1);
     ad.coff[j] = (uint32_t)((int64_t)row * op.ld);
   }
 #pragma unroll
@@ -132,24 +169,29 @@ __device__ __forceinline__ OperandAddr make_addr(const Operand& op, int wave, in
   return ad;
 }
 
-__device__ __forceinline__ void issue_codes(const OperandAddr& ad, uint8_t* tile, int wave, int lane, int64_t k,
+// kb: byte offset of the stage along the row
+template <bool FP4>
+__device__ __forceinline__ void issue_codes(const OperandAddr& ad, uint8_t* tile, int wave, int lane, int64_t kb,
                                             int valid_chunks) {
-  const uint8_t* base = ad.cbase + k;
-  const uint32_t c0 = (uint32_t)min(dma_chunk(0, lane), valid_chunks - 1) * 16;
-  const uint32_t c1 = (uint32_t)min(dma_chunk(1, lane), valid_chunks - 1) * 16;
+  using F = Fmt<FP4>;
+  const uint8_t* base = ad.cbase + kb;
+  const uint32_t c0 = (uint32_t)min(dma_chunk<FP4>(0, lane), valid_chunks - 1) * 16;
+  const uint32_t c1 = (uint32_t)min(dma_chunk<FP4>(1, lane), valid_chunks - 1) * 16;
 #pragma unroll
-  for (int j = 0; j < 4; j++)
+  for (int j = 0; j < F::kLoads; j++)
     __builtin_amdgcn_global_load_lds(base + (ad.coff[j] + ((j & 1) ? c1 : c0)),
-                                     (lds_ptr)(tile + (wave * 4 + j) * 1024), 16, 0, 0);
+                                     (lds_ptr)(tile + (wave * F::kLoads + j) * 1024), 16, 0, 0);
 }
 
 // Zero the code chunks at or past valid_chunks (0 zeroes the whole stage) in
 // the bytes this wave's own loads wrote; called after those loads landed.
+template <bool FP4>
 __device__ __forceinline__ void zero_codes(uint8_t* tile, int wave, int lane, int valid_chunks) {
+  using F = Fmt<FP4>;
 #pragma unroll
-  for (int j = 0; j < 4; j++)
-    if (dma_chunk(j, lane) >= valid_chunks)
-      *reinterpret_cast<uint4*>(tile + (wave * 4 + j) * 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
+  for (int j = 0; j < F::kLoads; j++)
+    if (dma_chunk<FP4>(j, lane) >= valid_chunks)
+      *reinterpret_cast<uint4*>(tile + (wave * F::kLoads + j) * 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
 }
 
 __device__ __forceinline__ void issue_scales(const OperandAddr& ad, uint8_t* region, int wave, int64_t k,
@@ -170,41 +212,54 @@ struct Frags {
   uint2 sb;
 };
 
-// fragment of the MFMA row block starting at tile row r0, step s of the stage
+// fragment of the MFMA row block starting at tile row r0, step s of the
+// stage.  E4M3: bytes 0-15 of lane l are K 16g .. 16g+15 of the step, bytes
+// 16-31 K 32+16g .. (g = l/32).  E2M1: bytes 0-15 are the 32 nibbles of K
+// 32g .. 32g+31, the upper half is not read by the MFMA.
+template <bool FP4>
 __device__ __forceinline__ v8i load_frag(const uint8_t* codes, int r0, int s, int lane) {
   const int r = r0 + (lane & 31);
   const int g = lane >> 5;
-  const uint4 lo = *reinterpret_cast<const uint4*>(codes + swz(r, 4 * s + g));
-  const uint4 hi = *reinterpret_cast<const uint4*>(codes + swz(r, 4 * s + 2 + g));
   v8i f;
-  f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
-  f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
+  if constexpr (FP4) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(codes + swz<true>(r, 2 * s + g));
+    f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
+    f[4] = 0; f[5] = 0; f[6] = 0; f[7] = 0;
+  } else {
+    const uint4 lo = *reinterpret_cast<const uint4*>(codes + swz<false>(r, 4 * s + g));
+    const uint4 hi = *reinterpret_cast<const uint4*>(codes + swz<false>(r, 4 * s + 2 + g));
+    f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
+    f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
+  }
   return f;
 }
 
 // B rows wn*64 .. wn*64+63 are 32-row blocks 2*(wn%2) and 2*(wn%2)+1 of half
 // wn/2: their two scale dwords sit 8*(wn%2) bytes into the lane's 16.
+template <bool FP4>
 __device__ __forceinline__ void read_frags(const uint8_t* st, int s, int wm, int wn, int lane, Frags& f) {
+  constexpr int kTileBytes = Fmt<FP4>::kTileBytes;
   const int so = ((lane >> 5) * 32 + (lane & 31)) * 16;
   f.sa = *reinterpret_cast<const uint4*>(st + 2 * kTileBytes + (s * 2 + wm) * 1024 + so);
   f.sb = *reinterpret_cast<const uint2*>(st + 2 * kTileBytes + kScaleRegion + (s * 2 + (wn >> 1)) * 1024 + so +
                                          (wn & 1) * 8);
 #pragma unroll
-  for (int i = 0; i < TM; i++) f.a[i] = load_frag(st, wm * WM + i * 32, s, lane);
+  for (int i = 0; i < TM; i++) f.a[i] = load_frag<FP4>(st, wm * WM + i * 32, s, lane);
 #pragma unroll
-  for (int j = 0; j < TN; j++) f.b[j] = load_frag(st + kTileBytes, wn * WN + j * 32, s, lane);
+  for (int j = 0; j < TN; j++) f.b[j] = load_frag<FP4>(st + kTileBytes, wn * WN + j * 32, s, lane);
 }
 
 __device__ __forceinline__ int u4_get(const uint4& v, int i) {
   return (int)(i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w);
 }
 
+template <bool FP4>
 __device__ __forceinline__ void mfma_step(v16f (&acc)[TM][TN], const Frags& f) {
 #pragma unroll
   for (int i = 0; i < TM; i++)
 #pragma unroll
     for (int j = 0; j < TN; j++)
-      acc[i][j] = mfma_scaled(f.a[i], f.b[j], acc[i][j], u4_get(f.sa, i), (int)(j == 0 ? f.sb.x : f.sb.y));
+      acc[i][j] = mfma_scaled<FP4>(f.a[i], f.b[j], acc[i][j], u4_get(f.sa, i), (int)(j == 0 ? f.sb.x : f.sb.y));
 }
 
 // s_waitcnt with vmcnt(n) only (expcnt / lgkmcnt left at their maximum), gfx9 encoding
@@ -244,7 +299,7 @@ struct GroupScratch {
   int32_t scan_tmp[kThreads];
   int32_t order[kMaxGroups];
 };
-static_assert(sizeof(GroupScratch) <= kStageBytes, "group scratch must fit in one stage");
+static_assert(sizeof(GroupScratch) <= Fmt<true>::kStageBytes, "group scratch must fit in one stage");
 
 // One output tile: where its operands and output live and which K range it
 // reduces over.  All fields are workgroup-uniform.
@@ -293,19 +348,21 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[TM][TN], const Tile
 // pipeline does not drain between tiles and the output stores of one tile
 // drain while the next one computes.  Dense is launched with one workgroup
 // per tile (measured faster).
-template <int MODE>
-__global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
+template <int MODE, bool FP4>
+__global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ sB, float* __restrict__ C, int64_t M, int64_t N, int64_t K,
     int64_t ldc, const int32_t* __restrict__ group_end, int32_t G, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
+  using F = Fmt<FP4>;
+  constexpr int kTileBytes = F::kTileBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[F::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[F::kStageBytes];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   const int bid = blockIdx.x;
-  const int64_t lda = K;
+  const int64_t lda = FP4 ? K / 2 : K;  // code bytes per row of A and B
   const int64_t ldo = MODE == kRaggedK ? N : ldc;
 
   // ---- the tile list
@@ -384,7 +441,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
       const int local = mt - __builtin_amdgcn_readfirstlane(gtp->bstart[g]);
       tl.m0 = (int64_t)__builtin_amdgcn_readfirstlane(gtp->start[g]) + (int64_t)local * BM;
       tl.rows_a = min(BM, __builtin_amdgcn_readfirstlane(gtp->size[g]) - local * BM);
-      tl.b_base = B + (int64_t)g * N * K;
+      tl.b_base = B + (int64_t)g * N * lda;
       tl.sb_base = sB + (int64_t)g * ((N + 31) / 32 * 32) * (K / 32);  // expert scale arrays hold ceil32(N) rows
     } else {
       const int per_g = tiles_m * tiles_n;
@@ -404,15 +461,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
     const int ns = (int)((tl.klen + BKS - 1) / BKS);
     tl.nst = (ns + 1) & ~1;
     tl.last = ns - 1;
-    tl.tail_chunks = ns > 0 ? (int)(tl.klen - (int64_t)tl.last * BKS) / 16 : 8;
+    tl.tail_chunks = ns > 0 ? (int)(tl.klen - (int64_t)tl.last * BKS) / F::kElemsPerChunk : F::kChunks;
     return tl;
   };
   OperandAddr ada, adb;
   auto addr_of = [&](const Tile& tl) {
-    const Operand opa{A + tl.m0 * lda, sA, tl.m0, lda, tl.rows_a};
-    const Operand opb{tl.b_base + tl.n0 * lda, tl.sb_base, tl.n0, lda, tl.rows_b};
-    ada = make_addr(opa, wave, lane);
-    adb = make_addr(opb, wave, lane);
+    const Operand opa{A + tl.m0 * lda, sA, tl.m0, lda, K / 32, tl.rows_a};
+    const Operand opb{tl.b_base + tl.n0 * lda, tl.sb_base, tl.n0, lda, K / 32, tl.rows_b};
+    ada = make_addr<FP4>(opa, wave, lane);
+    adb = make_addr<FP4>(opb, wave, lane);
   };
   const int id0 = tile_id(0);
   auto tile_of = [&](int id) { return make_tile(id); };
@@ -431,21 +488,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
   // re-load the last one (every stage issues the same loads)
   auto issue = [&](int slot, const Tile& tl, int s) {
     const int sc = min(s, tl.last);
-    const int64_t k = tl.k_begin + (int64_t)sc * BKS;
-    const int vc = sc == tl.last ? tl.tail_chunks : 8;
+    const int64_t k = tl.k_begin + (int64_t)sc * BKS;  // elements
+    const int64_t kb = FP4 ? k / 2 : k;                // code bytes
+    const int vc = sc == tl.last ? tl.tail_chunks : F::kChunks;
+    const int vb = (int)((unsigned)vc * F::kElemsPerChunk / 32u);  // valid scale blocks
     uint8_t* st = stages[slot];
-    issue_codes(ada, st, wave, lane, k, vc);
-    issue_codes(adb, st + kTileBytes, wave, lane, k, vc);
-    issue_scales(ada, st + 2 * kTileBytes, wave, k, vc / 2);
-    issue_scales(adb, st + 2 * kTileBytes + kScaleRegion, wave, k, vc / 2);
+    issue_codes<FP4>(ada, st, wave, lane, kb, vc);
+    issue_codes<FP4>(adb, st + kTileBytes, wave, lane, kb, vc);
+    issue_scales(ada, st + 2 * kTileBytes, wave, k, vb);
+    issue_scales(adb, st + 2 * kTileBytes + kScaleRegion, wave, k, vb);
   };
   // once stage s of `tl` has landed in `slot` (this wave's part): zero the
   // chunks past the end of K, or all of it if it only pads the loop
   auto fix = [&](int slot, const Tile& tl, int s) {
-    const int vc = s > tl.last ? 0 : s == tl.last ? tl.tail_chunks : 8;
-    if (vc < 8) {
-      zero_codes(stages[slot], wave, lane, vc);
-      zero_codes(stages[slot] + kTileBytes, wave, lane, vc);
+    const int vc = s > tl.last ? 0 : s == tl.last ? tl.tail_chunks : F::kChunks;
+    if (vc < F::kChunks) {
+      zero_codes<FP4>(stages[slot], wave, lane, vc);
+      zero_codes<FP4>(stages[slot] + kTileBytes, wave, lane, vc);
     }
   };
   auto pin = [&]() {
@@ -464,14 +523,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
   // the last barrier), and have the two steps to land.
   auto stage_steps = [&](int cur, const Tile& nt, int ns) {
     // step 0
-    read_frags(stages[cur], 0, wm, wn, lane, f);
+    read_frags<FP4>(stages[cur], 0, wm, wn, lane, f);
     issue(cur ^ 1, nt, ns);
-    mfma_step(acc, f);
+    mfma_step<FP4>(acc, f);
     pin();
     __builtin_amdgcn_sched_barrier(0);
     // step 1
-    read_frags(stages[cur], 1, wm, wn, lane, f);
-    mfma_step(acc, f);
+    read_frags<FP4>(stages[cur], 1, wm, wn, lane, f);
+    mfma_step<FP4>(acc, f);
     pin();
     __builtin_amdgcn_sched_barrier(0);
     // publish the following stage; after the barrier every wave is done reading `cur`
@@ -541,11 +600,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp8_kernel(
 
 }  // namespace
 
-hipError_t launch_gemm(int mode, const uint8_t* A, const uint8_t* sA, const uint8_t* B,
-                       const uint8_t* sB, float* C, int64_t M, int64_t N, int64_t K, int64_t ldc,
-                       const int32_t* group_end, int32_t G, hipStream_t st) {
+template <bool FP4>
+hipError_t launch_gemm_fmt(int mode, const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
+                           float* C, int64_t M, int64_t N, int64_t K, int64_t ldc, const int32_t* group_end,
+                           int32_t G, hipStream_t st) {
   // 32-bit per-lane load offsets: 256 rows of codes of one tile
-  if ((int64_t)BM * K >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  if ((int64_t)BM * (FP4 ? K / 2 : K) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const int64_t tiles_n = (N + BN - 1) / BN;
   const int64_t tiles_m = (M + BM - 1) / BM;
   const int64_t cus = device_cu_count();
@@ -553,23 +613,31 @@ hipError_t launch_gemm(int mode, const uint8_t* A, const uint8_t* sA, const uint
     const int64_t total = tiles_m * tiles_n;  // one workgroup per tile
     if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
     const int64_t grid = total;
-    gemm_mxfp8_kernel<kDense><<<(unsigned)grid, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, ldc, nullptr, 1,
-                                                                    (int)tiles_m, (int)tiles_n);
+    gemm_mx_kernel<kDense, FP4><<<(unsigned)grid, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, ldc, nullptr, 1,
+                                                                      (int)tiles_m, (int)tiles_n);
   } else if (mode == kRaggedM) {
     // every group adds at most one partial m-tile: an upper bound of the tiles
     const int64_t total = (tiles_m + G) * tiles_n;
     if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
     const int64_t grid = total < cus ? total : cus;
-    gemm_mxfp8_kernel<kRaggedM><<<(unsigned)grid, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, ldc,
-                                                                      group_end, G, (int)tiles_m, (int)tiles_n);
+    gemm_mx_kernel<kRaggedM, FP4><<<(unsigned)grid, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, ldc,
+                                                                        group_end, G, (int)tiles_m, (int)tiles_n);
   } else {
+    if (FP4) return hipErrorInvalidValue;  // no E2M1 token-axis operands
     const int64_t total = (int64_t)G * tiles_m * tiles_n;
     if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
     const int64_t grid = total < cus ? total : cus;
-    gemm_mxfp8_kernel<kRaggedK><<<(unsigned)grid, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, N,
-                                                                      group_end, G, (int)tiles_m, (int)tiles_n);
+    gemm_mx_kernel<kRaggedK, false><<<(unsigned)grid, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, N,
+                                                                          group_end, G, (int)tiles_m, (int)tiles_n);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemm(int mode, bool fp4, const uint8_t* A, const uint8_t* sA, const uint8_t* B,
+                       const uint8_t* sB, float* C, int64_t M, int64_t N, int64_t K, int64_t ldc,
+                       const int32_t* group_end, int32_t G, hipStream_t st) {
+  return fp4 ? launch_gemm_fmt<true>(mode, A, sA, B, sB, C, M, N, K, ldc, group_end, G, st)
+             : launch_gemm_fmt<false>(mode, A, sA, B, sB, C, M, N, K, ldc, group_end, G, st);
 }
 
 }  // namespace mxq

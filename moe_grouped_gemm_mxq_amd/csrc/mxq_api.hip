@@ -218,6 +218,21 @@ mxq_status mxq_qdq_fp4_ex(const float* x, float* y, int64_t rows, int64_t L, flo
   return launched(launch_qdq_fp4(x, y, rows, L, F, T, codes, scales, sat_mask, st), "mxq_qdq_fp4_ex");
 }
 
+mxq_status mxq_quantize_fp4(const float* x, int64_t rows, int64_t L, float scale_factor, uint8_t* codes,
+                            uint8_t* scales, hipStream_t st) {
+  MXQ_REQUIRE(x && codes && scales, "mxq_quantize_fp4: NULL operand");
+  MXQ_REQUIRE(rows >= 1 && L >= 1, "mxq_quantize_fp4: rows and L must be >= 1");
+  MXQ_REQUIRE(((uintptr_t)x & 3u) == 0, "mxq_quantize_fp4: x must be 4-byte aligned");
+  MXQ_REQUIRE(aligned16(codes), "mxq_quantize_fp4: codes must be 16-byte aligned");
+  int F;
+  uint32_t T;
+  MXQ_REQUIRE(fp4_scale_params(scale_factor, &F, &T),
+              "mxq_quantize_fp4: scale_factor must be a normal fp32 value in [2^-64, 2^64) (got %g)",
+              (double)scale_factor);
+  MXQ_REQUIRE_DEVICE();
+  return launched(launch_qdq_fp4(x, nullptr, rows, L, F, T, codes, scales, nullptr, st, true), "mxq_quantize_fp4");
+}
+
 mxq_status mxq_ste_backward_fp4(const float* grad_y, const uint8_t* sat_mask, float* grad_x,
                                 int64_t rows, int64_t L, hipStream_t st) {
   MXQ_REQUIRE(grad_y && sat_mask && grad_x, "mxq_ste_backward_fp4: NULL operand");
@@ -247,9 +262,10 @@ mxq_status mxq_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const
   MXQ_REQUIRE(K >= 32 && K % 32 == 0, "mxq_gemm: K must be a positive multiple of 32 (got %lld)", (long long)K);
   MXQ_REQUIRE(ldc >= N, "mxq_gemm: ldc < N");
   MXQ_REQUIRE(aligned16(A) && aligned16(B) && ((uintptr_t)C & 3u) == 0, "mxq_gemm: A, B must be 16-byte aligned");
-  if (fmt != MXQ_FMT_E4M3) return fail(MXQ_ERR_UNSUPPORTED, "mxq_gemm: only MXQ_FMT_E4M3 operands are implemented");
+  if (fmt != MXQ_FMT_E4M3 && fmt != MXQ_FMT_E2M1)
+    return fail(MXQ_ERR_UNSUPPORTED, "mxq_gemm: unknown operand format %d", (int)fmt);
   MXQ_REQUIRE_DEVICE();
-  return launched(launch_gemm(0, A, sA, B, sB, C, M, N, K, ldc, nullptr, 1, st), "mxq_gemm");
+  return launched(launch_gemm(0, fmt == MXQ_FMT_E2M1, A, sA, B, sB, C, M, N, K, ldc, nullptr, 1, st), "mxq_gemm");
 }
 
 mxq_status mxq_grouped_gemm(mxq_gg_mode mode, const uint8_t* A, const uint8_t* sA,
@@ -262,9 +278,13 @@ mxq_status mxq_grouped_gemm(mxq_gg_mode mode, const uint8_t* A, const uint8_t* s
   MXQ_REQUIRE(K >= 32 && K % 32 == 0, "mxq_grouped_gemm: K must be a positive multiple of 32");
   MXQ_REQUIRE(G >= 1 && G <= MXQ_MAX_GROUPS, "mxq_grouped_gemm: G must be in [1, %d]", MXQ_MAX_GROUPS);
   MXQ_REQUIRE(aligned16(A) && aligned16(B) && ((uintptr_t)C & 3u) == 0, "mxq_grouped_gemm: A, B must be 16-byte aligned");
-  if (fmt != MXQ_FMT_E4M3) return fail(MXQ_ERR_UNSUPPORTED, "mxq_grouped_gemm: only MXQ_FMT_E4M3 operands are implemented");
+  if (fmt != MXQ_FMT_E4M3 && fmt != MXQ_FMT_E2M1)
+    return fail(MXQ_ERR_UNSUPPORTED, "mxq_grouped_gemm: unknown operand format %d", (int)fmt);
+  if (fmt == MXQ_FMT_E2M1 && mode == MXQ_GG_RAGGED_K)
+    return fail(MXQ_ERR_UNSUPPORTED, "mxq_grouped_gemm: MXQ_FMT_E2M1 operands are implemented for MXQ_GG_RAGGED_M only");
   MXQ_REQUIRE_DEVICE();
-  return launched(launch_gemm(mode == MXQ_GG_RAGGED_M ? 1 : 2, A, sA, B, sB, C, M, N, K, N, group_end, G, st),
+  return launched(launch_gemm(mode == MXQ_GG_RAGGED_M ? 1 : 2, fmt == MXQ_FMT_E2M1, A, sA, B, sB, C, M, N, K, N,
+                              group_end, G, st),
                   "mxq_grouped_gemm");
 }
 

@@ -30,13 +30,17 @@ hipError_t launch_quant_tile(const uint16_t* x, int64_t R, int64_t C, int64_t ld
 // MXFP4 quant-dequant.  (F, T) encode the scale factor's exponent threshold;
 // fp4_scale_params computes them and rejects factors outside [2^-64, 2^64).
 bool fp4_scale_params(float scale_factor, int* F, uint32_t* T);
+// y may be null (quantise only); interleave: scales in the GEMM operand layout
+// (32-row interleaved) instead of row-major.
 hipError_t launch_qdq_fp4(const float* x, float* y, int64_t rows, int64_t L, int F, uint32_t T,
-                          uint8_t* codes, uint8_t* scales, uint8_t* sat_mask, hipStream_t st);
+                          uint8_t* codes, uint8_t* scales, uint8_t* sat_mask, hipStream_t st,
+                          bool interleave = false);
 hipError_t launch_ste_backward_fp4(const float* grad_y, const uint8_t* sat_mask, float* grad_x,
                                    int64_t rows, int64_t L, hipStream_t st);
 
-// Block-scaled GEMMs.  mode 0: dense (G = 1, no group_end); 1: ragged M; 2: ragged K.
-hipError_t launch_gemm(int mode, const uint8_t* A, const uint8_t* sA, const uint8_t* B,
+// Block-scaled GEMMs.  mode 0: dense (G = 1, no group_end); 1: ragged M; 2: ragged K
+// (E4M3 only).  fp4: E2M1 codes (two per byte) instead of E4M3.
+hipError_t launch_gemm(int mode, bool fp4, const uint8_t* A, const uint8_t* sA, const uint8_t* B,
                        const uint8_t* sB, float* C, int64_t M, int64_t N, int64_t K, int64_t ldc,
                        const int32_t* group_end, int32_t G, hipStream_t st);
 

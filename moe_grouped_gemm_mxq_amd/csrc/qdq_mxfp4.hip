@@ -64,11 +64,13 @@ __device__ __forceinline__ uint32_t oct_or(uint32_t v) {
 
 // L % 32 == 0 and 16-byte aligned x / y: the tensor is a flat run of blocks,
 // chunk i = elements 4i..4i+3, block i / 8.
+// y null: quantise only.  nbr > 0: scales in the 32-row interleaved GEMM
+// operand layout for rows of nbr blocks; 0: row-major.
 __global__ __launch_bounds__(kThreads) void qdq_flat_kernel(const float* __restrict__ x,
                                                            float* __restrict__ y, int64_t n_chunks,
                                                            Fp4Scale p, uint8_t* __restrict__ codes,
                                                            uint8_t* __restrict__ scales,
-                                                           uint32_t* __restrict__ sat_mask) {
+                                                           uint32_t* __restrict__ sat_mask, int64_t nbr) {
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_chunks;
        i += (int64_t)gridDim.x * kThreads) {
     const uint4 v = reinterpret_cast<const uint4*>(x)[i];
@@ -76,9 +78,13 @@ __global__ __launch_bounds__(kThreads) void qdq_flat_kernel(const float* __restr
     const uint32_t amax = oct_max(absmax4(xb));
     const int e = mxfp4_scale_exp(amax, p);
     const Qdq4 r = qdq4(xb, e);
-    reinterpret_cast<uint4*>(y)[i] = make_uint4(r.out[0], r.out[1], r.out[2], r.out[3]);
+    if (y) reinterpret_cast<uint4*>(y)[i] = make_uint4(r.out[0], r.out[1], r.out[2], r.out[3]);
     if (codes) reinterpret_cast<uint16_t*>(codes)[i] = (uint16_t)r.nibbles;
-    if (scales && (i & 7) == 0) scales[i >> 3] = (uint8_t)(e + 127);
+    if (scales && (i & 7) == 0) {
+      const int64_t blk = i >> 3;
+      const int64_t row = nbr > 0 ? blk / nbr : 0;
+      scales[nbr > 0 ? scale_offset(row, blk - row * nbr, nbr) : blk] = (uint8_t)(e + 127);
+    }
     if (sat_mask) {
       const uint32_t word = oct_or(r.sat << (4 * (i & 7)));
       if ((i & 7) == 0) sat_mask[i >> 3] = word;
@@ -92,7 +98,7 @@ __global__ __launch_bounds__(kThreads) void qdq_rows_kernel(const float* __restr
                                                            int64_t L, Fp4Scale p,
                                                            uint8_t* __restrict__ codes,
                                                            uint8_t* __restrict__ scales,
-                                                           uint32_t* __restrict__ sat_mask) {
+                                                           uint32_t* __restrict__ sat_mask, bool interleave) {
   const int64_t nbr = (L + 31) / 32;  // blocks per row
   const int64_t n_chunks = rows * nbr * 8;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_chunks;
@@ -106,11 +112,14 @@ __global__ __launch_bounds__(kThreads) void qdq_rows_kernel(const float* __restr
     const uint32_t amax = oct_max(absmax4(xb));
     const int e = mxfp4_scale_exp(amax, p);
     const Qdq4 r = qdq4(xb, e);
+    if (y) {
 #pragma unroll
-    for (int j = 0; j < 4; j++)
-      if (col + j < L) y[row * L + col + j] = __uint_as_float(r.out[j]);
+      for (int j = 0; j < 4; j++)
+        if (col + j < L) y[row * L + col + j] = __uint_as_float(r.out[j]);
+    }
     if (codes) *reinterpret_cast<uint16_t*>(codes + row * (nbr * 16) + col / 2) = (uint16_t)r.nibbles;
-    if (scales && (i & 7) == 0) scales[blk] = (uint8_t)(e + 127);
+    if (scales && (i & 7) == 0)
+      scales[interleave ? scale_offset(row, blk - row * nbr, nbr) : blk] = (uint8_t)(e + 127);
     if (sat_mask) {
       // padding elements are 0 and never saturate, so their bits stay clear
       const uint32_t word = oct_or(r.sat << (4 * (i & 7)));
@@ -185,15 +194,16 @@ bool fp4_scale_params(float scale_factor, int* F, uint32_t* T) {
 }
 
 hipError_t launch_qdq_fp4(const float* x, float* y, int64_t rows, int64_t L, int F, uint32_t T,
-                          uint8_t* codes, uint8_t* scales, uint8_t* sat_mask, hipStream_t st) {
+                          uint8_t* codes, uint8_t* scales, uint8_t* sat_mask, hipStream_t st, bool interleave) {
   const Fp4Scale p{F, T};
   const bool flat = L % 32 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)y % 16 == 0;
   const int64_t n_chunks = flat ? rows * L / 4 : rows * ((L + 31) / 32) * 8;
   uint32_t* mask = reinterpret_cast<uint32_t*>(sat_mask);
   if (flat)
-    qdq_flat_kernel<<<grid_for(n_chunks), kThreads, 0, st>>>(x, y, n_chunks, p, codes, scales, mask);
+    qdq_flat_kernel<<<grid_for(n_chunks), kThreads, 0, st>>>(x, y, n_chunks, p, codes, scales, mask,
+                                                             interleave ? L / 32 : 0);
   else
-    qdq_rows_kernel<<<grid_for(n_chunks), kThreads, 0, st>>>(x, y, rows, L, p, codes, scales, mask);
+    qdq_rows_kernel<<<grid_for(n_chunks), kThreads, 0, st>>>(x, y, rows, L, p, codes, scales, mask, interleave);
   return hipGetLastError();
 }
 

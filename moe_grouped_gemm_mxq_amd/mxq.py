@@ -35,6 +35,7 @@ STATUS_NAMES = {0: "MXQ_OK", 1: "MXQ_ERR_INVALID_ARGUMENT", 2: "MXQ_ERR_UNSUPPOR
 MXQ_AXIS_ROW = 1
 MXQ_AXIS_COLT = 2
 MXQ_FMT_E4M3 = 0
+MXQ_FMT_E2M1 = 1
 MXQ_GG_RAGGED_M = 0
 MXQ_GG_RAGGED_K = 1
 BLOCK = 32
@@ -43,7 +44,7 @@ MAX_GROUPS = 1024
 EXPORTED = [
     "mxq_abi_version", "mxq_last_error", "mxq_device_check", "mxq_grouped_cols_max",
     "mxq_quantize", "mxq_quantize_batched", "mxq_quantize_grouped", "mxq_qdq_fp4", "mxq_qdq_fp4_ex",
-    "mxq_ste_backward_fp4", "mxq_fp4_scale_threshold", "mxq_gemm", "mxq_grouped_gemm",
+    "mxq_ste_backward_fp4", "mxq_fp4_scale_threshold", "mxq_quantize_fp4", "mxq_gemm", "mxq_grouped_gemm",
     "mxq_validate_group_end",
 ]
 
@@ -67,6 +68,7 @@ def _load(path: str = LIB_PATH):
         "mxq_qdq_fp4_ex": ([P, P, I64, I64, ctypes.c_float, P, P, P, P], I),
         "mxq_ste_backward_fp4": ([P, P, P, I64, I64, P], I),
         "mxq_fp4_scale_threshold": ([ctypes.c_float, P, P], I),
+        "mxq_quantize_fp4": ([P, I64, I64, ctypes.c_float, P, P, P], I),
         "mxq_gemm": ([P, P, P, P, P, I64, I64, I64, I64, I, P], I),
         "mxq_grouped_gemm": ([I, P, P, P, P, P, I64, I64, I64, P, I32, I, P], I),
         "mxq_validate_group_end": ([P, I32, I64, P, P], I),
@@ -254,14 +256,21 @@ def mxq_fp4_scale_threshold(scale_factor):
     return F.value, T.value
 
 
-def mxq_gemm(A, sA, B, sB, C, stream=None):
-    """A uint8 [M][K] + scales scale_shape(M, K/32), B [N][K] + scale_shape(N, K/32) -> C fp32 [M][ldc >= N]."""
+def _elems(nbytes: int, fmt: int) -> int:
+    """K (elements) of an operand row of `nbytes` code bytes."""
+    return nbytes * 2 if fmt == MXQ_FMT_E2M1 else nbytes
+
+
+def mxq_gemm(A, sA, B, sB, C, stream=None, fmt=MXQ_FMT_E4M3):
+    """A uint8 [M][K] + scales scale_shape(M, K/32), B [N][K] + scale_shape(N, K/32) -> C fp32 [M][ldc >= N].
+    fmt MXQ_FMT_E2M1: A [M][K/2], B [N][K/2] (two E2M1 codes per byte)."""
     for t, n in ((A, "A"), (sA, "sA"), (B, "B"), (sB, "sB")):
         _need(t, torch.uint8, n)
     _need(C, torch.float32, "C", 2)
-    M, K = A.shape
+    M, Kb = A.shape
+    K = _elems(Kb, fmt)
     N = B.shape[0]
-    if (B.dim() != 2 or B.shape[1] != K or tuple(sA.shape) != scale_shape(M, K // BLOCK)
+    if (B.dim() != 2 or B.shape[1] != Kb or tuple(sA.shape) != scale_shape(M, K // BLOCK)
             or tuple(sB.shape) != scale_shape(N, K // BLOCK)):
         raise ValueError("operand shapes disagree")
     if not all(t.is_contiguous() for t in (A, sA, B, sB)):
@@ -269,34 +278,49 @@ def mxq_gemm(A, sA, B, sB, C, stream=None):
     if C.shape[0] != M or C.shape[1] < N or C.stride(1) != 1:
         raise ValueError("C must be [M][>=N] with unit column stride")
     _check(_lib.mxq_gemm(_ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(C), M, N, K, C.stride(0),
-                         MXQ_FMT_E4M3, _stream(stream, A.device)), "mxq_gemm")
+                         fmt, _stream(stream, A.device)), "mxq_gemm")
 
 
-def mxq_grouped_gemm(mode, A, sA, B, sB, C, group_end, stream=None):
+def mxq_grouped_gemm(mode, A, sA, B, sB, C, group_end, stream=None, fmt=MXQ_FMT_E4M3):
     """RAGGED_M: A [M][K], B [G][N][K], C [M][N].  RAGGED_K: A [M][K], B [N][K], C [G][M][N].
 
-    Scales: sA scale_shape(M, K/32); sB (G,) + scale_shape(N, K/32) (ragged M) or scale_shape(N, K/32)."""
+    Scales: sA scale_shape(M, K/32); sB (G,) + scale_shape(N, K/32) (ragged M) or scale_shape(N, K/32).
+    fmt MXQ_FMT_E2M1 (ragged M only): code rows of K/2 bytes."""
     for t, n in ((A, "A"), (sA, "sA"), (B, "B"), (sB, "sB")):
         _need(t, torch.uint8, n)
     _need(C, torch.float32, "C")
     _need(group_end, torch.int32, "group_end", 1)
     G = group_end.numel()
-    M, K = A.shape
+    M, Kb = A.shape
+    K = _elems(Kb, fmt)
     N = B.shape[-2]
     if mode == MXQ_GG_RAGGED_M:
-        ok = (tuple(B.shape) == (G, N, K) and tuple(sB.shape) == (G,) + scale_shape(N, K // BLOCK)
+        ok = (tuple(B.shape) == (G, N, Kb) and tuple(sB.shape) == (G,) + scale_shape(N, K // BLOCK)
               and tuple(C.shape) == (M, N))
     else:
         N = B.shape[0]
-        ok = (tuple(B.shape) == (N, K) and tuple(sB.shape) == scale_shape(N, K // BLOCK)
+        ok = (tuple(B.shape) == (N, Kb) and tuple(sB.shape) == scale_shape(N, K // BLOCK)
               and tuple(C.shape) == (G, M, N))
     if not ok or tuple(sA.shape) != scale_shape(M, K // BLOCK):
         raise ValueError("grouped GEMM operand shapes disagree")
     if not all(t.is_contiguous() for t in (A, sA, B, sB, C)):
         raise ValueError("operands must be contiguous")
     _check(_lib.mxq_grouped_gemm(mode, _ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(C), M, N, K,
-                                 _ptr(group_end), G, MXQ_FMT_E4M3, _stream(stream, A.device)),
+                                 _ptr(group_end), G, fmt, _stream(stream, A.device)),
            "mxq_grouped_gemm")
+
+
+def mxq_quantize_fp4(x, codes, scales, scale_factor=6.0, stream=None):
+    """MXFP4 GEMM operand: x fp32 [rows][L] -> codes uint8 [rows][ceil32(L)/2],
+    scales scale_shape(rows, ceil32(L)/32) (interleaved)."""
+    _need(x, torch.float32, "x")
+    if not x.is_contiguous() or x.dim() != 2:
+        raise ValueError("x must be a contiguous 2-D tensor")
+    rows, L = x.shape
+    _need_u8(codes, "codes", (rows, ceil32(L) // 2))
+    _need_u8(scales, "scales", scale_shape(rows, ceil32(L) // BLOCK))
+    _check(_lib.mxq_quantize_fp4(_ptr(x), rows, L, float(scale_factor), _ptr(codes), _ptr(scales),
+                                 _stream(stream, x.device)), "mxq_quantize_fp4")
 
 
 def mxq_validate_group_end(group_end, T, flag, stream=None):
@@ -369,6 +393,15 @@ def qdq_fp4(x, want_codes=False, stream=None):
     return (y, codes, scales) if want_codes else y
 
 
+def quantize_fp4(x, scale_factor=6.0, stream=None):
+    """MXFP4 GEMM operand of a 2-D fp32 tensor: (codes, interleaved scales)."""
+    rows, L = x.shape
+    codes = _u8((rows, ceil32(L) // 2), x.device)
+    scales = _u8(scale_shape(rows, ceil32(L) // BLOCK), x.device)
+    mxq_quantize_fp4(x, codes, scales, scale_factor, stream)
+    return codes, scales
+
+
 def qdq_fp4_ste(x, scale_factor=6.0, want_codes=False, stream=None):
     """Forward of the clipped-STE fake quantiser: returns (y, sat_mask) or,
     with want_codes, (y, sat_mask, codes, scales)."""
@@ -389,16 +422,16 @@ def ste_backward_fp4(grad_y, sat_mask, stream=None):
     return grad_x
 
 
-def gemm(A, sA, B, sB, stream=None):
+def gemm(A, sA, B, sB, stream=None, fmt=MXQ_FMT_E4M3):
     C = torch.empty((A.shape[0], B.shape[0]), dtype=torch.float32, device=A.device)
-    mxq_gemm(A, sA, B, sB, C, stream)
+    mxq_gemm(A, sA, B, sB, C, stream, fmt)
     return C
 
 
-def grouped_gemm(mode, A, sA, B, sB, group_end, stream=None):
+def grouped_gemm(mode, A, sA, B, sB, group_end, stream=None, fmt=MXQ_FMT_E4M3):
     if mode == MXQ_GG_RAGGED_M:
         C = torch.empty((A.shape[0], B.shape[1]), dtype=torch.float32, device=A.device)
     else:
         C = torch.empty((group_end.numel(), A.shape[0], B.shape[0]), dtype=torch.float32, device=A.device)
-    mxq_grouped_gemm(mode, A, sA, B, sB, C, group_end, stream)
+    mxq_grouped_gemm(mode, A, sA, B, sB, C, group_end, stream, fmt)
     return C

@@ -116,6 +116,11 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
         assert call(lib, "mxq_qdq_fp4_ex", FAKE, FAKE, I64(2), I64(64), F32(sf), P(0), P(0), P(0), P(0)) == 1
     assert "scale_factor" in err(lib)
     assert call(lib, "mxq_qdq_fp4_ex", FAKE, FAKE, I64(2), I64(64), F32(6.0), P(0), P(0), P(0x1002), P(0)) == 1
+    # E2M1 operands: ragged K is not offered
+    assert call(lib, "mxq_grouped_gemm", 1, FAKE, FAKE, FAKE, FAKE, FAKE, I64(4), I64(4), I64(64), FAKE,
+                ctypes.c_int32(2), 1, P(0)) == 2
+    assert "RAGGED_M only" in err(lib)
+    assert call(lib, "mxq_quantize_fp4", FAKE, I64(2), I64(64), F32(6.0), P(0x1008), FAKE, P(0)) == 1
     # STE backward: NULL mask, partial overlap of grad_x and grad_y
     assert call(lib, "mxq_ste_backward_fp4", FAKE, P(0), FAKE, I64(2), I64(64), P(0)) == 1
     assert call(lib, "mxq_ste_backward_fp4", P(0x1000), FAKE, P(0x1010), I64(2), I64(64), P(0)) == 1
