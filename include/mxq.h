@@ -230,8 +230,9 @@ mxq_status mxq_quantize_fp4(const float* x, int64_t rows, int64_t L, float scale
  * Forward Y = X W: A = row copy of X, B = colT copy of W [K][N].
  * Input gradient dX = dY W^T: A = row copy of dY, B = row copy of W.
  * Weight gradient dW = X^T dY: A = colT copy of X, B = colT copy of dY.
- * fmt MXQ_FMT_E2M1 (MXFP4 operands, the MXFP4 option of the guide's MoE
- * recipe with the AMCT article's numeric model): A codes [M][K/2], B codes
+ * fmt MXQ_FMT_E2M1 (MXFP4 operands: the optional MXFP4 of routed experts in
+ * the torchao_npu RFC's "mix" recipe, section 3.4, with the AMCT article's
+ * numeric model, taken as a GEMM on the codes): A codes [M][K/2], B codes
  * [N][K/2] as written by mxq_quantize_fp4 (rows of K elements), scales in
  * the same interleaved layout.
  * M, N >= 1; K >= 32, K % 32 == 0; ldc >= N.  Unknown fmt:
