@@ -1,7 +1,8 @@
-// Block-scaled MXFP8 GEMMs for gfx950: C[m][n] = sum_k deq(A)[m][k] deq(B)[n][k]
-// with E4M3 codes, one E8M0 scale per 32 values along K, fp32 accumulation and
-// fp32 output (the FP8 linear and expert GEMMs of the torchtitan-npu guide,
-// "线性层低精度" and "MoE 专家层低精度").
+// Block-scaled MX GEMMs for gfx950: C[m][n] = sum_k deq(A)[m][k] deq(B)[n][k]
+// with E4M3 codes (or E2M1 codes, two per byte), one E8M0 scale per 32 values
+// along K, fp32 accumulation and fp32 output (the FP8 linear and expert GEMMs
+// of the torchtitan-npu guide, "线性层低精度" and "MoE 专家层低精度"; the
+// optional MXFP4 of routed experts in the torchao_npu RFC's recipes).
 //
 // One main loop serves three problem shapes:
 //   dense    -- one A [M][K], one B [N][K];
@@ -16,6 +17,10 @@
 // and step).  Two waves per SIMD let one wave's MFMAs run while the other
 // waits on its LDS reads, and keep enough LDS requests in flight for the LDS
 // to serve both the fragment reads and the direct loads writing into it.
+//
+// Element formats (Fmt): E4M3 and a wide E2M1 stage hold 128 code bytes per
+// tile row (128 or 256 elements, 2 or 4 MFMA steps); the narrow E2M1 stage
+// holds 64 (128 elements), leaving LDS for the grouped modes' tables.
 //
 // Pipeline: codes (global_load_lds_dwordx4) and scale bytes
 // (global_load_lds_ubyte) go from global memory straight into LDS.  LDS holds
@@ -46,23 +51,32 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr int kThreads = 512;
 constexpr int BM = 256, BN = 256, BK = 64;   // BK: codes (bytes) per MFMA step
-constexpr int BKS = 2 * BK;                   // codes per tile row per stage (two steps)
 constexpr int WM = 128, WN = 64;              // wave tile
 constexpr int TM = WM / 32, TN = WN / 32;     // MFMA blocks per wave
-constexpr int kScaleRegion = 4 * 4 * BM;      // one dword per (tile row, K-block) of one operand (4 KB)
 
-// Layout of one LDS stage per element format.  E4M3 codes take a byte, E2M1
-// codes (two per byte, element 2j in the low nibble) half of one, so a stage
-// of BKS elements per row holds 128 or 64 code bytes per row.
-template <bool FP4>
+// Layout of one LDS stage per operand kind.  E4M3 codes take a byte, E2M1
+// codes (two per byte, element 2j in the low nibble) half of one.
+//   kE4M3:   128 elements (2 MFMA steps) per tile row = 128 code bytes;
+//   kE2M1:   128 elements (2 steps) = 64 code bytes (a 40 KB stage, which
+//            leaves LDS room for the grouped modes' tables);
+//   kE2M1W:  256 elements (4 steps) = 128 code bytes, the E4M3 byte layout,
+//            twice the scales (an 80 KB stage: two fill the 160 KB of LDS;
+//            dense only).  Every load then reads whole 128-byte lines.
+enum Kind { kE4M3 = 0, kE2M1 = 1, kE2M1W = 2 };
+template <int KIND>
 struct Fmt {
-  static constexpr int kRowBytes = FP4 ? BKS / 2 : BKS;                  // code bytes per tile row
-  static constexpr int kChunks = kRowBytes / 16;                         // 16-byte chunks per row (8 / 4)
-  static constexpr int kElemsPerChunk = BKS / kChunks;                   // 16 / 32
+  static constexpr bool kFp4 = KIND != kE4M3;
+  static constexpr int kSteps = KIND == kE2M1W ? 4 : 2;                  // MFMA steps per stage
+  static constexpr int kStageElems = kSteps * BK;                        // elements per tile row and stage
+  static constexpr int kRowBytes = KIND == kE2M1 ? 64 : 128;             // code bytes per tile row
+  static constexpr int kChunks = kRowBytes / 16;                         // 16-byte chunks per row
+  static constexpr int kElemsPerChunk = kStageElems / kChunks;           // 16 / 32
   static constexpr int kTileBytes = BM * kRowBytes;                      // per operand (32 KB / 16 KB)
+  static constexpr int kScaleRegion = kSteps * 2 * 4 * BM;               // one dword per (tile row, K-block)
   static constexpr int kStageBytes = 2 * kTileBytes + 2 * kScaleRegion;  // A, B codes, A, B scales
   static constexpr int kLoads = kTileBytes / (kThreads / 64) / 1024;     // dwordx4 loads per wave and operand
   static constexpr int kLanesPerRow = kRowBytes / 16;                    // lanes of one load on one row
+  static constexpr int kScaleLoads = kScaleRegion / 256 / (kThreads / 64);  // ubyte loads per wave and operand
 };
 constexpr int kXcds = 8;                      // XCDs per MI355X; workgroups are dealt round robin
 constexpr int kGroupM = 8;                    // m-tiles per raster group
@@ -70,9 +84,10 @@ constexpr int kGroupM = 8;                    // m-tiles per raster group
 enum Mode { kDense = 0, kRaggedM = 1, kRaggedK = 2 };
 
 // format codes of the f8f6f4 MFMA operands: 0 = E4M3, 4 = E2M1
-template <bool FP4>
+template <int KIND>
 __device__ __forceinline__ v16f mfma_scaled(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FP4 ? 4 : 0, FP4 ? 4 : 0, 0, sa, 0, sb);
+  constexpr int f = KIND == kE4M3 ? 0 : 4;
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, f, f, 0, sa, 0, sb);
 }
 
 // LDS position of 16-byte chunk c of tile row r.  A fragment read has its
@@ -81,17 +96,17 @@ __device__ __forceinline__ v16f mfma_scaled(const v8i& a, const v8i& b, const v1
 //    & 1) makes any 8 aligned consecutive rows land on 8 distinct 16-byte
 //    bank groups of a 128-byte bank row (32 banks) and any 16 on 16 distinct
 //    groups of a 256-byte one (64 banks);
-//  E2M1 (4 chunks, 64 bytes per row): rows r .. r+3 fill one 256-byte bank
+//  narrow E2M1 (4 chunks, 64 bytes per row): rows r .. r+3 fill one 256-byte bank
 //    row and f(r) = (r >> 2) & 3 moves the chunk within each row's quarter
 //    for every group of four rows, so any 16 consecutive rows hit 16 distinct
 //    bank groups.
-// Either way the read is conflict-free.
-template <bool FP4>
+// Either way the read is conflict-free.  (Wide E2M1 uses the E4M3 layout.)
+template <int KIND>
 __device__ __forceinline__ int swz(int r, int c) {
-  if constexpr (FP4)
+  if constexpr (KIND == kE2M1)
     return r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
   else
-    return r * BKS + ((c ^ ((r & 7) ^ ((r >> 3) & 1))) << 4);
+    return r * 128 + ((c ^ ((r & 7) ^ ((r >> 3) & 1))) << 4);
 }
 
 // One operand of one workgroup tile: tile rows [0, rows_valid), which are rows
@@ -137,20 +152,29 @@ struct OperandAddr {
   uint32_t soff[2];      // per load: offset of the lane's scale row inside the groups
 };
 
-// E4M3: load j of wave w covers rows 8q .. 8q+7 (q = 4w + j), 8 lanes a row;
-// E2M1: rows 16q .. 16q+15 (q = 2w + j), 4 lanes a row.  Lane l fills slot
-// l % lanes-per-row of its row, which holds chunk slot ^ f(row).
-template <bool FP4>
+// 128-byte rows: load j of wave w covers rows 8q .. 8q+7 (q = 4w + j), 8
+// lanes a row; narrow E2M1: rows 16q .. 16q+15 (q = 2w + j), 4 lanes a row.
+// Lane l fills slot l % lanes-per-row of its row, which holds chunk
+// slot ^ f(row).
+template <int KIND>
 __device__ __forceinline__ int dma_chunk(int j, int lane) {
-  if constexpr (FP4)
+  if constexpr (KIND == kE2M1)
     return (lane & 3) ^ (lane >> 4);
   else
     return (lane & 7) ^ (lane >> 3) ^ (j & 1);
 }
 
-template <bool FP4>
+// scale loads: unit u = w * L + j (L loads per wave) fills slots
+// [64u, 64u + 64): r / 16 = u % 2, g = (u / 2) % 2, h = (u / 4) % 2, step
+// s = u / 8; half h is fixed per wave
+template <int KIND>
+__device__ __forceinline__ int scale_half(int wave) {
+  return Fmt<KIND>::kScaleLoads == 4 ? (wave & 1) : ((wave >> 1) & 1);
+}
+
+template <int KIND>
 __device__ __forceinline__ OperandAddr make_addr(const Operand& op, int wave, int lane) {
-  using F = Fmt<FP4>;
+  using F = Fmt<KIND>;
   OperandAddr ad;
   const int64_t nblk = op.nblk;
   ad.cbase = op.base;
@@ -162,7 +186,7 @@ __device__ __forceinline__ OperandAddr make_addr(const Operand& op, int wave, in
   }
 #pragma unroll
   for (int j = 0; j < 2; j++) {
-    const int i = lane & 3, r = (j * 16 + (lane >> 2)) & 31, h = (wave >> 1) & 1;
+    const int i = lane & 3, r = (j * 16 + (lane >> 2)) & 31, h = scale_half<KIND>(wave);
     const int64_t R = op.row0 + min(h * 128 + i * 32 + r, op.rows_valid - 1);
     ad.soff[j] = (uint32_t)(((R >> 5) - (op.row0 >> 5)) * nblk * 32 + (R & 31));
   }
@@ -170,13 +194,13 @@ __device__ __forceinline__ OperandAddr make_addr(const Operand& op, int wave, in
 }
 
 // kb: byte offset of the stage along the row
-template <bool FP4>
+template <int KIND>
 __device__ __forceinline__ void issue_codes(const OperandAddr& ad, uint8_t* tile, int wave, int lane, int64_t kb,
                                             int valid_chunks) {
-  using F = Fmt<FP4>;
+  using F = Fmt<KIND>;
   const uint8_t* base = ad.cbase + kb;
-  const uint32_t c0 = (uint32_t)min(dma_chunk<FP4>(0, lane), valid_chunks - 1) * 16;
-  const uint32_t c1 = (uint32_t)min(dma_chunk<FP4>(1, lane), valid_chunks - 1) * 16;
+  const uint32_t c0 = (uint32_t)min(dma_chunk<KIND>(0, lane), valid_chunks - 1) * 16;
+  const uint32_t c1 = (uint32_t)min(dma_chunk<KIND>(1, lane), valid_chunks - 1) * 16;
 #pragma unroll
   for (int j = 0; j < F::kLoads; j++)
     __builtin_amdgcn_global_load_lds(base + (ad.coff[j] + ((j & 1) ? c1 : c0)),
@@ -185,22 +209,25 @@ __device__ __forceinline__ void issue_codes(const OperandAddr& ad, uint8_t* tile
 
 // Zero the code chunks at or past valid_chunks (0 zeroes the whole stage) in
 // the bytes this wave's own loads wrote; called after those loads landed.
-template <bool FP4>
+template <int KIND>
 __device__ __forceinline__ void zero_codes(uint8_t* tile, int wave, int lane, int valid_chunks) {
-  using F = Fmt<FP4>;
+  using F = Fmt<KIND>;
 #pragma unroll
   for (int j = 0; j < F::kLoads; j++)
-    if (dma_chunk<FP4>(j, lane) >= valid_chunks)
+    if (dma_chunk<KIND>(j, lane) >= valid_chunks)
       *reinterpret_cast<uint4*>(tile + (wave * F::kLoads + j) * 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
 }
 
+template <int KIND>
 __device__ __forceinline__ void issue_scales(const OperandAddr& ad, uint8_t* region, int wave, int64_t k,
                                              int valid_blocks) {
+  constexpr int L = Fmt<KIND>::kScaleLoads;
 #pragma unroll
-  for (int j = 0; j < 2; j++) {
-    const int blk = min((wave >> 2) * 2 + (wave & 1), valid_blocks - 1);  // uniform
-    __builtin_amdgcn_global_load_lds(ad.sbase + (k + blk * 32) + ad.soff[j],
-                                     (lds_ptr)(region + (wave * 2 + j) * 256), 1, 0, 0);
+  for (int j = 0; j < L; j++) {
+    const int u = wave * L + j;                                          // (uniform)
+    const int blk = min((u >> 3) * 2 + ((u >> 1) & 1), valid_blocks - 1);  // 2 * step + g
+    __builtin_amdgcn_global_load_lds(ad.sbase + (k + blk * 32) + ad.soff[u & 1], (lds_ptr)(region + u * 256), 1,
+                                     0, 0);
   }
 }
 
@@ -216,18 +243,18 @@ struct Frags {
 // stage.  E4M3: bytes 0-15 of lane l are K 16g .. 16g+15 of the step, bytes
 // 16-31 K 32+16g .. (g = l/32).  E2M1: bytes 0-15 are the 32 nibbles of K
 // 32g .. 32g+31, the upper half is not read by the MFMA.
-template <bool FP4>
+template <int KIND>
 __device__ __forceinline__ v8i load_frag(const uint8_t* codes, int r0, int s, int lane) {
   const int r = r0 + (lane & 31);
   const int g = lane >> 5;
   v8i f;
-  if constexpr (FP4) {
-    const uint4 lo = *reinterpret_cast<const uint4*>(codes + swz<true>(r, 2 * s + g));
+  if constexpr (KIND != kE4M3) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(codes + swz<KIND>(r, 2 * s + g));
     f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
     f[4] = 0; f[5] = 0; f[6] = 0; f[7] = 0;
   } else {
-    const uint4 lo = *reinterpret_cast<const uint4*>(codes + swz<false>(r, 4 * s + g));
-    const uint4 hi = *reinterpret_cast<const uint4*>(codes + swz<false>(r, 4 * s + 2 + g));
+    const uint4 lo = *reinterpret_cast<const uint4*>(codes + swz<KIND>(r, 4 * s + g));
+    const uint4 hi = *reinterpret_cast<const uint4*>(codes + swz<KIND>(r, 4 * s + 2 + g));
     f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
     f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
   }
@@ -236,30 +263,30 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* codes, int r0, int s, in
 
 // B rows wn*64 .. wn*64+63 are 32-row blocks 2*(wn%2) and 2*(wn%2)+1 of half
 // wn/2: their two scale dwords sit 8*(wn%2) bytes into the lane's 16.
-template <bool FP4>
+template <int KIND>
 __device__ __forceinline__ void read_frags(const uint8_t* st, int s, int wm, int wn, int lane, Frags& f) {
-  constexpr int kTileBytes = Fmt<FP4>::kTileBytes;
+  constexpr int kTileBytes = Fmt<KIND>::kTileBytes, kScaleRegion = Fmt<KIND>::kScaleRegion;
   const int so = ((lane >> 5) * 32 + (lane & 31)) * 16;
   f.sa = *reinterpret_cast<const uint4*>(st + 2 * kTileBytes + (s * 2 + wm) * 1024 + so);
   f.sb = *reinterpret_cast<const uint2*>(st + 2 * kTileBytes + kScaleRegion + (s * 2 + (wn >> 1)) * 1024 + so +
                                          (wn & 1) * 8);
 #pragma unroll
-  for (int i = 0; i < TM; i++) f.a[i] = load_frag<FP4>(st, wm * WM + i * 32, s, lane);
+  for (int i = 0; i < TM; i++) f.a[i] = load_frag<KIND>(st, wm * WM + i * 32, s, lane);
 #pragma unroll
-  for (int j = 0; j < TN; j++) f.b[j] = load_frag<FP4>(st + kTileBytes, wn * WN + j * 32, s, lane);
+  for (int j = 0; j < TN; j++) f.b[j] = load_frag<KIND>(st + kTileBytes, wn * WN + j * 32, s, lane);
 }
 
 __device__ __forceinline__ int u4_get(const uint4& v, int i) {
   return (int)(i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w);
 }
 
-template <bool FP4>
+template <int KIND>
 __device__ __forceinline__ void mfma_step(v16f (&acc)[TM][TN], const Frags& f) {
 #pragma unroll
   for (int i = 0; i < TM; i++)
 #pragma unroll
     for (int j = 0; j < TN; j++)
-      acc[i][j] = mfma_scaled<FP4>(f.a[i], f.b[j], acc[i][j], u4_get(f.sa, i), (int)(j == 0 ? f.sb.x : f.sb.y));
+      acc[i][j] = mfma_scaled<KIND>(f.a[i], f.b[j], acc[i][j], u4_get(f.sa, i), (int)(j == 0 ? f.sb.x : f.sb.y));
 }
 
 // s_waitcnt with vmcnt(n) only (expcnt / lgkmcnt left at their maximum), gfx9 encoding
@@ -299,7 +326,7 @@ struct GroupScratch {
   int32_t scan_tmp[kThreads];
   int32_t order[kMaxGroups];
 };
-static_assert(sizeof(GroupScratch) <= Fmt<true>::kStageBytes, "group scratch must fit in one stage");
+static_assert(sizeof(GroupScratch) <= Fmt<kE2M1>::kStageBytes, "group scratch must fit in one stage");
 
 // One output tile: where its operands and output live and which K range it
 // reduces over.  All fields are workgroup-uniform.
@@ -348,13 +375,14 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[TM][TN], const Tile
 // pipeline does not drain between tiles and the output stores of one tile
 // drain while the next one computes.  Dense is launched with one workgroup
 // per tile (measured faster).
-template <int MODE, bool FP4>
+template <int MODE, int KIND>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ sB, float* __restrict__ C, int64_t M, int64_t N, int64_t K,
     int64_t ldc, const int32_t* __restrict__ group_end, int32_t G, int tiles_m, int tiles_n) {
-  using F = Fmt<FP4>;
-  constexpr int kTileBytes = F::kTileBytes;
+  using F = Fmt<KIND>;
+  constexpr bool FP4 = F::kFp4;
+  constexpr int kTileBytes = F::kTileBytes, kScaleRegion = F::kScaleRegion, BKS = F::kStageElems;
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[F::kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[F::kStageBytes];
   const int t = threadIdx.x;
@@ -468,8 +496,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
   auto addr_of = [&](const Tile& tl) {
     const Operand opa{A + tl.m0 * lda, sA, tl.m0, lda, K / 32, tl.rows_a};
     const Operand opb{tl.b_base + tl.n0 * lda, tl.sb_base, tl.n0, lda, K / 32, tl.rows_b};
-    ada = make_addr<FP4>(opa, wave, lane);
-    adb = make_addr<FP4>(opb, wave, lane);
+    ada = make_addr<KIND>(opa, wave, lane);
+    adb = make_addr<KIND>(opb, wave, lane);
   };
   const int id0 = tile_id(0);
   auto tile_of = [&](int id) { return make_tile(id); };
@@ -493,18 +521,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
     const int vc = sc == tl.last ? tl.tail_chunks : F::kChunks;
     const int vb = (int)((unsigned)vc * F::kElemsPerChunk / 32u);  // valid scale blocks
     uint8_t* st = stages[slot];
-    issue_codes<FP4>(ada, st, wave, lane, kb, vc);
-    issue_codes<FP4>(adb, st + kTileBytes, wave, lane, kb, vc);
-    issue_scales(ada, st + 2 * kTileBytes, wave, k, vb);
-    issue_scales(adb, st + 2 * kTileBytes + kScaleRegion, wave, k, vb);
+    issue_codes<KIND>(ada, st, wave, lane, kb, vc);
+    issue_codes<KIND>(adb, st + kTileBytes, wave, lane, kb, vc);
+    issue_scales<KIND>(ada, st + 2 * kTileBytes, wave, k, vb);
+    issue_scales<KIND>(adb, st + 2 * kTileBytes + kScaleRegion, wave, k, vb);
   };
   // once stage s of `tl` has landed in `slot` (this wave's part): zero the
   // chunks past the end of K, or all of it if it only pads the loop
   auto fix = [&](int slot, const Tile& tl, int s) {
     const int vc = s > tl.last ? 0 : s == tl.last ? tl.tail_chunks : F::kChunks;
     if (vc < F::kChunks) {
-      zero_codes<FP4>(stages[slot], wave, lane, vc);
-      zero_codes<FP4>(stages[slot] + kTileBytes, wave, lane, vc);
+      zero_codes<KIND>(stages[slot], wave, lane, vc);
+      zero_codes<KIND>(stages[slot] + kTileBytes, wave, lane, vc);
     }
   };
   auto pin = [&]() {
@@ -523,16 +551,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
   // the last barrier), and have the two steps to land.
   auto stage_steps = [&](int cur, const Tile& nt, int ns) {
     // step 0
-    read_frags<FP4>(stages[cur], 0, wm, wn, lane, f);
+    read_frags<KIND>(stages[cur], 0, wm, wn, lane, f);
     issue(cur ^ 1, nt, ns);
-    mfma_step<FP4>(acc, f);
+    mfma_step<KIND>(acc, f);
     pin();
     __builtin_amdgcn_sched_barrier(0);
-    // step 1
-    read_frags<FP4>(stages[cur], 1, wm, wn, lane, f);
-    mfma_step<FP4>(acc, f);
-    pin();
-    __builtin_amdgcn_sched_barrier(0);
+    // steps 1 ..
+#pragma unroll
+    for (int st = 1; st < F::kSteps; st++) {
+      read_frags<KIND>(stages[cur], st, wm, wn, lane, f);
+      mfma_step<KIND>(acc, f);
+      pin();
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // publish the following stage; after the barrier every wave is done reading `cur`
     wait_vmcnt<0>();  // this wave's loads of the following stage landed
     fix(cur ^ 1, nt, ns);
@@ -600,12 +631,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
 
 }  // namespace
 
-template <bool FP4>
-hipError_t launch_gemm_fmt(int mode, const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
-                           float* C, int64_t M, int64_t N, int64_t K, int64_t ldc, const int32_t* group_end,
-                           int32_t G, hipStream_t st) {
+template <int KIND>
+hipError_t launch_gemm_kind(int mode, const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
+                            float* C, int64_t M, int64_t N, int64_t K, int64_t ldc, const int32_t* group_end,
+                            int32_t G, hipStream_t st) {
   // 32-bit per-lane load offsets: 256 rows of codes of one tile
-  if ((int64_t)BM * (FP4 ? K / 2 : K) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  if ((int64_t)BM * (KIND != kE4M3 ? K / 2 : K) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const int64_t tiles_n = (N + BN - 1) / BN;
   const int64_t tiles_m = (M + BM - 1) / BM;
   const int64_t cus = device_cu_count();
@@ -613,22 +644,29 @@ hipError_t launch_gemm_fmt(int mode, const uint8_t* A, const uint8_t* sA, const 
     const int64_t total = tiles_m * tiles_n;  // one workgroup per tile
     if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
     const int64_t grid = total;
-    gemm_mx_kernel<kDense, FP4><<<(unsigned)grid, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, ldc, nullptr, 1,
-                                                                      (int)tiles_m, (int)tiles_n);
+    gemm_mx_kernel<kDense, KIND><<<(unsigned)grid, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, ldc, nullptr, 1,
+                                                                       (int)tiles_m, (int)tiles_n);
   } else if (mode == kRaggedM) {
-    // every group adds at most one partial m-tile: an upper bound of the tiles
-    const int64_t total = (tiles_m + G) * tiles_n;
-    if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const int64_t grid = total < cus ? total : cus;
-    gemm_mx_kernel<kRaggedM, FP4><<<(unsigned)grid, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, ldc,
-                                                                        group_end, G, (int)tiles_m, (int)tiles_n);
+    if constexpr (KIND == kE2M1W) {
+      return hipErrorInvalidValue;  // the wide stage leaves no LDS for the group table
+    } else {
+      // every group adds at most one partial m-tile: an upper bound of the tiles
+      const int64_t total = (tiles_m + G) * tiles_n;
+      if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
+      const int64_t grid = total < cus ? total : cus;
+      gemm_mx_kernel<kRaggedM, KIND><<<(unsigned)grid, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, ldc,
+                                                                           group_end, G, (int)tiles_m, (int)tiles_n);
+    }
   } else {
-    if (FP4) return hipErrorInvalidValue;  // no E2M1 token-axis operands
-    const int64_t total = (int64_t)G * tiles_m * tiles_n;
-    if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const int64_t grid = total < cus ? total : cus;
-    gemm_mx_kernel<kRaggedK, false><<<(unsigned)grid, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, N,
-                                                                          group_end, G, (int)tiles_m, (int)tiles_n);
+    if constexpr (KIND != kE4M3) {
+      return hipErrorInvalidValue;  // no E2M1 token-axis operands
+    } else {
+      const int64_t total = (int64_t)G * tiles_m * tiles_n;
+      if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
+      const int64_t grid = total < cus ? total : cus;
+      gemm_mx_kernel<kRaggedK, KIND><<<(unsigned)grid, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, N,
+                                                                           group_end, G, (int)tiles_m, (int)tiles_n);
+    }
   }
   return hipGetLastError();
 }
@@ -636,8 +674,12 @@ hipError_t launch_gemm_fmt(int mode, const uint8_t* A, const uint8_t* sA, const 
 hipError_t launch_gemm(int mode, bool fp4, const uint8_t* A, const uint8_t* sA, const uint8_t* B,
                        const uint8_t* sB, float* C, int64_t M, int64_t N, int64_t K, int64_t ldc,
                        const int32_t* group_end, int32_t G, hipStream_t st) {
-  return fp4 ? launch_gemm_fmt<true>(mode, A, sA, B, sB, C, M, N, K, ldc, group_end, G, st)
-             : launch_gemm_fmt<false>(mode, A, sA, B, sB, C, M, N, K, ldc, group_end, G, st);
+  if (!fp4) return launch_gemm_kind<kE4M3>(mode, A, sA, B, sB, C, M, N, K, ldc, group_end, G, st);
+  if (mode == kRaggedK) return hipErrorInvalidValue;  // no E2M1 token-axis operands
+  // dense E2M1 runs the wide stage (two of them fill the LDS); the grouped
+  // modes need LDS for their tables and run the narrow one
+  if (mode == kDense) return launch_gemm_kind<kE2M1W>(mode, A, sA, B, sB, C, M, N, K, ldc, group_end, G, st);
+  return launch_gemm_kind<kE2M1>(mode, A, sA, B, sB, C, M, N, K, ldc, group_end, G, st);
 }
 
 }  // namespace mxq
