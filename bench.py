@@ -64,8 +64,8 @@ def measured_traffic(kernel_label):
     vals = {}
     with open(path) as f:
         for line in f:
-            if line.startswith("- ") and ":" in line:
-                k, v = line[2:].split(":", 1)
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].split(": ", 1)
                 vals[k.strip()] = v.strip().strip("`")
     if vals.get("kernel source sha256[:16]") != source_digest(GEMM_SRC):
         return None
