@@ -235,3 +235,56 @@ def test_moe_fb_split_equals_dual(moe_full):
                         fwd_only["q_row"].view(G, K, N), fwd_only["s_row"].view(G, K // 32, N // 32, 32), ge)
     torch.cuda.synchronize()
     assert torch.equal(dX, moe_full["dX"])
+
+
+# ------------------------------------------------------------------ many groups
+def many_group_sizes(G, seed):
+    """Mostly empty groups, some of 1-40 rows, three of 257: exercises group
+    tables larger than a workgroup, long runs of empty experts and partial
+    tiles."""
+    rng = np.random.default_rng(seed)
+    sizes = np.where(rng.random(G) < 0.85, 0, rng.integers(1, 41, G))
+    sizes[rng.choice(G, 3, replace=False)] = 257
+    return sizes.astype(np.int64)
+
+
+@pytest.mark.parametrize("G", [600, 1024])
+def test_ragged_m_many_groups(G):
+    m = mxq()
+    sizes = many_group_sizes(G, G)
+    T, K, N = int(sizes.sum()), 64, 40
+    X = scaled_randn((T, K), G, lo=-6, hi=6)
+    W = scaled_randn((G * K, N), G + 1, lo=-6, hi=6, axis=1).reshape(G, K, N)
+    ge = np.cumsum(sizes).astype(np.int32)
+    qx = m.quantize(X.cuda(), 1)
+    qw = m.quantize_batched(W.cuda(), 2)                     # B[g] = column copy of W[g]
+    C = m.grouped_gemm(m.MXQ_GG_RAGGED_M, qx["q_row"], qx["s_row"], qw["q_colT"], qw["s_colT"],
+                       torch.from_numpy(ge).cuda())
+    torch.cuda.synchronize()
+    A, sA = oracle.mxfp8_quant_row(bits(X))
+    refB = [oracle.mxfp8_quant_colT(bits(W[g])) for g in range(G)]
+    Bq = np.stack([b[0] for b in refB])
+    Bs = np.stack([b[1] for b in refB])
+    Cr, Ca = oracle.grouped_gemm_ragged_m(A, sA, Bq, Bs, ge)
+    assert_gemm_close(host(C), Cr, Ca, f"ragged M, {G} groups", hw_bound=ragged_m_bound(A, sA, Bq, Bs, ge))
+
+
+@pytest.mark.parametrize("G", [600, 1024])
+def test_ragged_k_many_groups(G):
+    m = mxq()
+    sizes = many_group_sizes(G, G + 7)
+    T, Mh, N = int(sizes.sum()), 40, 48
+    X = scaled_randn((T, Mh), G + 2, lo=-6, hi=6, axis=1)
+    dY = scaled_randn((T, N), G + 3, lo=-6, hi=6, axis=1)
+    ge_np = np.cumsum(sizes).astype(np.int32)
+    ge = torch.from_numpy(ge_np).cuda()
+    qx = m.quantize_grouped(X.cuda(), ge, 2)
+    qy = m.quantize_grouped(dY.cuda(), ge, 2, ldq=qx["ldq"])
+    C = m.grouped_gemm(m.MXQ_GG_RAGGED_K, qx["q_colT"], qx["s_colT"], qy["q_colT"], qy["s_colT"], ge)
+    torch.cuda.synchronize()
+    A, sA = oracle.mxfp8_quant_grouped_colT(bits(X), ge_np, qx["ldq"])
+    B, sB = oracle.mxfp8_quant_grouped_colT(bits(dY), ge_np, qx["ldq"])
+    Cr, Ca = oracle.grouped_gemm_ragged_k(A, sA, B, sB, ge_np)
+    got = host(C)
+    assert_gemm_close(got, Cr, Ca, f"ragged K, {G} groups", hw_bound=ragged_k_bound(A, sA, B, sB, ge_np))
+    assert not got[sizes == 0].any(), "empty experts must get exact zeros"

@@ -256,7 +256,10 @@ def test_quantize_batched_bitexact(R, C, pad, axis):
 
 
 GROUPS = [[70], [0, 1, 31, 32, 33, 0], [0, 0, 5], [64, 0], [17, 40, 1, 0, 96],
-          [0, 0, 0, 200, 0, 0], [129, 1, 255, 0, 2, 64, 33]]
+          [0, 0, 0, 200, 0, 0], [129, 1, 255, 0, 2, 64, 33],
+          # 1024 groups (the maximum), mostly empty: tables larger than a workgroup
+          np.where(np.random.default_rng(1).random(1024) < 0.85, 0,
+                   np.random.default_rng(2).integers(1, 41, 1024)).tolist()]
 
 
 @pytest.mark.parametrize("sizes", GROUPS)
