@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 2
+#define MXQ_ABI_VERSION 3
 #define MXQ_BLOCK 32          /* elements per MX block; fixed */
 #define MXQ_MAX_GROUPS 1024   /* largest G the grouped entry points accept */
 

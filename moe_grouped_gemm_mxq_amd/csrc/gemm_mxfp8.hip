@@ -24,13 +24,14 @@
 //
 // Pipeline: codes (global_load_lds_dwordx4) and scale bytes
 // (global_load_lds_ubyte) go from global memory straight into LDS.  LDS holds
-// two stages of two steps each (128 codes per tile row, so every 16-byte lane
-// load belongs to a fully used 128-byte line); the loads of a stage are issued
-// two steps before its first use.  One s_barrier per two steps (raw, with
-// explicit vmcnt / lgkmcnt waits: a full __syncthreads would drain the loads
-// in flight) publishes the next stage and retires the current one.  The two stages are separate LDS arrays and the
-// loop is unrolled over both, so the compiler can tell the stage being read
-// from the stage being filled and never waits on the latter.
+// two stages (with 128 code bytes per tile row every 16-byte lane load belongs
+// to a fully used 128-byte line); the loads of a stage are issued one stage
+// before its first use.  One s_barrier per stage (raw, with explicit vmcnt /
+// lgkmcnt waits: a full __syncthreads would drain the loads in flight)
+// publishes the next stage and retires the current one.  The two stages are
+// separate LDS arrays and the loop is unrolled over both, so the compiler can
+// tell the stage being read from the stage being filled and never waits on
+// the latter.
 //
 // Operand layout of v_mfma_scale_f32_32x32x64_f8f6f4 for FP8 (found by
 // probing): lane l holds row l%32; its bytes 0-15 are K = 16g..16g+15 and
@@ -337,7 +338,7 @@ struct Tile {
   const uint8_t* b_base;   // B codes of the tile's expert (ragged M) or B
   const uint8_t* sb_base;  // B scales of the tile's expert
   float* c_base;           // output matrix of the tile (ragged K: the expert's)
-  int nst;                 // stages of two steps, rounded up to even (0 if klen == 0)
+  int nst;                 // K stages, rounded up to even (0 if klen == 0)
   int last, tail_chunks;   // last real stage and its valid 16-byte chunks per row
 };
 
@@ -542,13 +543,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
       for (int j = 0; j < TN; j++) asm volatile("" : "+a"(acc[i][j]));
   };
   Frags f;
-  // The two steps of a stage in LDS stage `cur` (published by the last
+  // The MFMA steps of a stage in LDS stage `cur` (published by the last
   // barrier).  Each wave reads a step's fragments and runs its 8 MFMAs as
   // soon as they arrive (the compiler waits per fragment); the other wave on
   // the SIMD keeps the matrix pipe busy meanwhile.  The loads of the stage
   // that follows (tile nt, stage ns) go out right after step 0's fragment
   // reads, into the other LDS stage (every wave finished reading it before
-  // the last barrier), and have the two steps to land.
+  // the last barrier), and have the stage's steps to land.
   auto stage_steps = [&](int cur, const Tile& nt, int ns) {
     // step 0
     read_frags<KIND>(stages[cur], 0, wm, wn, lane, f);

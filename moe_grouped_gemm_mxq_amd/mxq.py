@@ -80,7 +80,12 @@ def _load(path: str = LIB_PATH):
     return lib
 
 
+ABI_VERSION = 3  # MXQ_ABI_VERSION of include/mxq.h this binding is written against
+
 _lib = _load()
+if _lib.mxq_abi_version() != ABI_VERSION:
+    raise RuntimeError(f"libmxq.so at {LIB_PATH} implements ABI {_lib.mxq_abi_version()}, this binding needs "
+                       f"{ABI_VERSION}: rebuild it with `python -m moe_grouped_gemm_mxq_amd.build`")
 
 
 class MxqError(RuntimeError):

@@ -54,6 +54,8 @@ def test_abi_version_and_pure_host_helpers(lib):
     header = open(os.path.join(ROOT, "include", "mxq.h")).read()
     declared = int(re.search(r"#define MXQ_ABI_VERSION (\d+)", header).group(1))
     assert lib.mxq_abi_version() == declared
+    from moe_grouped_gemm_mxq_amd import mxq
+    assert mxq.ABI_VERSION == declared
     f = lib.mxq_grouped_cols_max
     f.restype = ctypes.c_int64
     f.argtypes = [ctypes.c_int64, ctypes.c_int32]
