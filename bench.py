@@ -134,7 +134,7 @@ def main():
     sizes = workloads.moe_group_sizes()
 
     # ---------------------------------------------------------------- outputs (allocated once)
-    sc = lambda rows, nblk: u8(*mxq.scale_shape(rows, nblk))   # interleaved scale array
+    sc = lambda rows, nblk: u8(*mxq.scale_shape(rows, nblk))   # GEMM-operand scale array
     qx = dict(q_row=u8(M, K), s_row=sc(M, K // 32), q_colT=u8(K, M), s_colT=sc(K, M // 32))
     qw = dict(q_row=u8(K, N), s_row=sc(K, N // 32), q_colT=u8(N, K), s_colT=sc(N, K // 32))
     qy = dict(q_row=u8(M, N), s_row=sc(M, N // 32), q_colT=u8(N, M), s_colT=sc(N, M // 32))
@@ -153,7 +153,7 @@ def main():
         # [g*H, (g+1)*H) of the stacked buffers (H is a multiple of 32)
         mxq.mxq_quantize_batched(Wm, mask,
                                  mw["q_row"].view(G, H, F) if mask & R else None,
-                                 mw["s_row"].view(G, H // 32, F // 32, 32) if mask & R else None,
+                                 mw["s_row"].view(G, H // 128, F // 32, 32, 4) if mask & R else None,
                                  mw["q_colT"] if mask & C else None, mw["s_colT"] if mask & C else None)
 
     def moe_fwd(tl, schedule):
@@ -174,7 +174,7 @@ def main():
             quant_w_experts(R)
         tl("moe_gemm_dgrad_raggedM")
         mxq.mxq_grouped_gemm(mxq.MXQ_GG_RAGGED_M, mdy["q_row"], mdy["s_row"], mw["q_row"].view(G, H, F),
-                             mw["s_row"].view(G, H // 32, F // 32, 32), mdX, ge)
+                             mw["s_row"].view(G, H // 128, F // 32, 32, 4), mdX, ge)
         tl("moe_gemm_wgrad_raggedK")
         mxq.mxq_grouped_gemm(mxq.MXQ_GG_RAGGED_K, mxt["q_colT"], mxt["s_colT"], mdy["q_colT"], mdy["s_colT"], mdW, ge)
 

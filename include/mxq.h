@@ -30,13 +30,14 @@
  *  - A quantised MXFP8 operand is `codes[rows][Kp]` (one E4M3 byte per
  *    element, the reduction axis K contiguous, Kp = ceil32(K), padding codes
  *    0x00) plus its scales: one E8M0 byte (value 2^(byte-127)) per row and
- *    block of 32, stored 32-row interleaved -- the scale of row r, block b is
- *    byte ((r/32) * (Kp/32) + b) * 32 + r%32 of an array of
- *    ceil32(rows) * (Kp/32) bytes ("scales[ceil32(rows)/32][Kp/32][32]").
- *    The scales of 32 consecutive rows for one block are adjacent, which is
- *    how a GEMM tile fetches them.  Bytes of rows past `rows` are not
- *    written.  A row range whose first row is a multiple of 32 is itself a
- *    valid operand (its scale array starts at byte first_row * (Kp/32)).
+ *    block of 32, in 128-row groups -- the scale of row r, block b is byte
+ *    (((r/128) * (Kp/32) + b) * 32 + r%32) * 4 + (r/32)%4 of an array of
+ *    ceil128(rows) * (Kp/32) bytes ("scales[ceil128(rows)/128][Kp/32][32][4]").
+ *    A dword holds the scales of rows r, r+32, r+64, r+96 of a group for one
+ *    block, and a group's blocks are 128 bytes apart, which is how a GEMM
+ *    tile fetches them.  Bytes of rows past `rows` are not written.  A row
+ *    range whose first row is a multiple of 128 is itself a valid operand
+ *    (its scale array starts at byte first_row * (Kp/32)).
  *  - "row" copy: blocks along the contiguous dim of the input.  "colT" copy:
  *    the quantised transpose, blocks running down the columns of the input.
  *  - Errors: every entry point validates its host-visible arguments first
@@ -59,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 3
+#define MXQ_ABI_VERSION 4
 #define MXQ_BLOCK 32          /* elements per MX block; fixed */
 #define MXQ_MAX_GROUPS 1024   /* largest G the grouped entry points accept */
 
@@ -105,9 +106,9 @@ int64_t mxq_grouped_cols_max(int64_t T, int32_t G);
  * quantisation of activations and weights of the torchtitan-npu guide
  * ("线性层低精度"), with the axis choice of MindSpeed PR 3852 ("主要改动").
  *   axis_mask & MXQ_AXIS_ROW : q_row [R][Cp], s_row (R rows, Cp/32 blocks,
- *                              interleaved), Cp = ceil32(C)
+ *                              operand layout), Cp = ceil32(C)
  *   axis_mask & MXQ_AXIS_COLT: q_colT [C][Rp], s_colT (C rows, Rp/32 blocks,
- *                              interleaved), Rp = ceil32(R)
+ *                              operand layout), Rp = ceil32(R)
  * Pointers for an axis not requested may be NULL.  Both axes together read
  * x once (dual-axis quantisation).  R, C >= 1; ldx >= C.
  */
@@ -135,13 +136,13 @@ mxq_status mxq_quantize_batched(const uint16_t* x, int64_t batch, int64_t R, int
  * group g owns rows [end_{g-1}, end_g) with end_g = group_end[g] (device
  * int32 [G], cumulative, end_{-1} = 0).
  *   MXQ_AXIS_COLT: q_colT [C][ldq], s_colT (C rows, ldq/32 blocks,
- *     interleaved).  Blocks restart at
+ *     operand layout).  Blocks restart at
  *     each group start; group g occupies columns [P_g, P_g + ceil32(m_g)),
  *     P_g = sum_{j<g} ceil32(m_j), its tail zero-padded.  Columns at and past
  *     P_G are not written.  ldq % 32 == 0; ldq >= sum_g ceil32(m_g) is a
  *     precondition (mxq_grouped_cols_max(T, G) always suffices); blocks that
  *     would fall past ldq are dropped.
- *   MXQ_AXIS_ROW: q_row [T][Cp], s_row (T rows, interleaved), identical to
+ *   MXQ_AXIS_ROW: q_row [T][Cp], s_row (T rows, operand layout), identical to
  *     mxq_quantize's row copy; with COLT the input is read once.
  * 1 <= G <= MXQ_MAX_GROUPS; T, C >= 1.
  */
@@ -213,10 +214,10 @@ mxq_status mxq_fp4_scale_threshold(float scale_factor, int32_t* F, uint32_t* T);
  * the GEMMs read.  x fp32 [rows][L] device, 4-byte aligned; each row zero-
  * padded to Lp = ceil32(L).  codes: device bytes [rows][Lp/2], 16-byte
  * aligned, E2M1 nibbles as for mxq_qdq_fp4 (element 2j in the low nibble of
- * byte j).  scales: E8M0 bytes, 32-row interleaved like the MXFP8 quantisers'
- * (scale of row r, block b at ((r/32)*(Lp/32) + b)*32 + r%32 of a
- * ceil32(rows)*(Lp/32)-byte array; bytes of rows past `rows` are not
- * written).  A GEMM operand with K = Lp.  scale_factor as for
+ * byte j).  scales: E8M0 bytes in the GEMM operand layout of the MXFP8
+ * quantisers (row r, block b at byte (((r/128)*(Lp/32) + b)*32 + r%32)*4 +
+ * (r/32)%4 of a ceil128(rows)*(Lp/32)-byte array; bytes of rows past `rows`
+ * are not written).  A GEMM operand with K = Lp.  scale_factor as for
  * mxq_qdq_fp4_ex.  rows, L >= 1.
  */
 mxq_status mxq_quantize_fp4(const float* x, int64_t rows, int64_t L, float scale_factor, uint8_t* codes,
@@ -226,7 +227,7 @@ mxq_status mxq_quantize_fp4(const float* x, int64_t rows, int64_t L, float scale
  * Block-scaled GEMM C[m][n] = sum_k deq(A)[m][k] * deq(B)[n][k] (the FP8
  * linear GEMMs of the torchtitan-npu guide, "线性层低精度"), fp32
  * accumulation and fp32 output.  A codes [M][K] + scales (M rows);
- * B codes [N][K] + scales (N rows), scales interleaved; C fp32 [M][ldc].
+ * B codes [N][K] + scales (N rows), scales in the operand layout; C fp32 [M][ldc].
  * Forward Y = X W: A = row copy of X, B = colT copy of W [K][N].
  * Input gradient dX = dY W^T: A = row copy of dY, B = row copy of W.
  * Weight gradient dW = X^T dY: A = colT copy of X, B = colT copy of dY.
@@ -234,7 +235,7 @@ mxq_status mxq_quantize_fp4(const float* x, int64_t rows, int64_t L, float scale
  * the torchao_npu RFC's "mix" recipe, section 3.4, with the AMCT article's
  * numeric model, taken as a GEMM on the codes): A codes [M][K/2], B codes
  * [N][K/2] as written by mxq_quantize_fp4 (rows of K elements), scales in
- * the same interleaved layout.
+ * the same operand layout.
  * M, N >= 1; K >= 32, K % 32 == 0; ldc >= N.  Unknown fmt:
  * MXQ_ERR_UNSUPPORTED.
  */
@@ -246,7 +247,7 @@ mxq_status mxq_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const
  * Grouped block-scaled GEMM over ragged expert groups (torchtitan-npu guide,
  * "MoE 专家层低精度"); group_end device int32 [G] as for mxq_quantize_grouped.
  *   MXQ_GG_RAGGED_M: A [M][K] (+ scales of M rows); B [G][N][K] with G
- *     scale arrays of N rows each, expert g's at byte g * ceil32(N) * (K/32);
+ *     scale arrays of N rows each, expert g's at byte g * ceil128(N) * (K/32);
  *     C fp32 [M][N].  Rows of group g use expert B[g]; rows at or past
  *     group_end[G-1] are not written.  K >= 32, K % 32 == 0.
  *     Expert forward: A = row copy of X, B[g] = colT copy of W[g] [K][N].

@@ -73,22 +73,24 @@ struct Fmt {
   static constexpr int kChunks = kRowBytes / 16;                         // 16-byte chunks per row
   static constexpr int kElemsPerChunk = kStageElems / kChunks;           // 16 / 32
   static constexpr int kTileBytes = BM * kRowBytes;                      // per operand (32 KB / 16 KB)
-  static constexpr int kScaleRegion = kSteps * 2 * 4 * BM;               // one dword per (tile row, K-block)
+  static constexpr int kBlocks = 2 * kSteps;                             // K-blocks per stage
+  static constexpr int kScaleRegion = 2 * kBlocks * 32 * 4;              // one dword per (half, block, row % 32)
   static constexpr int kStageBytes = 2 * kTileBytes + 2 * kScaleRegion;  // A, B codes, A, B scales
   static constexpr int kLoads = kTileBytes / (kThreads / 64) / 1024;     // dwordx4 loads per wave and operand
   static constexpr int kLanesPerRow = kRowBytes / 16;                    // lanes of one load on one row
-  static constexpr int kScaleLoads = kScaleRegion / 256 / (kThreads / 64);  // ubyte loads per wave and operand
+  static constexpr int kScaleLoads = kScaleRegion / 256 / 4;             // dword loads per wave (4 waves an operand)
 };
 constexpr int kXcds = 8;                      // XCDs per MI355X; workgroups are dealt round robin
 constexpr int kGroupM = 8;                    // m-tiles per raster group
 
 enum Mode { kDense = 0, kRaggedM = 1, kRaggedK = 2 };
 
-// format codes of the f8f6f4 MFMA operands: 0 = E4M3, 4 = E2M1
-template <int KIND>
+// format codes of the f8f6f4 MFMA operands: 0 = E4M3, 4 = E2M1; op_sel
+// picks byte I of the A scale dword and byte J of the B one
+template <int KIND, int I, int J>
 __device__ __forceinline__ v16f mfma_scaled(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
   constexpr int f = KIND == kE4M3 ? 0 : 4;
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, f, f, 0, sa, 0, sb);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, f, f, I, sa, J, sb);
 }
 
 // LDS position of 16-byte chunk c of tile row r.  A fragment read has its
@@ -112,9 +114,11 @@ __device__ __forceinline__ int swz(int r, int c) {
 
 // One operand of one workgroup tile: tile rows [0, rows_valid), which are rows
 // row0 .. row0 + rows_valid - 1 of a matrix with codes at base + (r - row0)*ld
-// and scales at sbase + scale_offset(r, block, ld/32) (the 32-row interleaved
-// layout the quantisers write).  Rows at or past rows_valid are read from row
-// rows_valid-1 (their results are never stored).
+// and scales at sbase + scale_offset(r, block, nblk) (the layout the
+// quantisers write).  row0 is a multiple of 128, so the tile's two halves are
+// whole 128-row groups of the scale array.  Code rows at or past rows_valid
+// are read from row rows_valid-1, and a half with no valid row reads the
+// scales of the first half (their results are never stored).
 struct Operand {
   const uint8_t* base;   // codes of tile row 0
   const uint8_t* sbase;  // scale array of the whole matrix
@@ -136,21 +140,21 @@ struct Operand {
 // fetched from the last valid chunk (always in bounds) and zeroed by
 // zero_codes() once they have landed.
 //
-// Scales: slot d (0..1023) of one operand and stage, one dword each (the scale
-// in its low byte): d = (((s*2 + h)*2 + g)*32 + r)*4 + i holds the scale of
-// tile row h*128 + i*32 + r over K-block g of step s (0, 1) of the stage.  A
-// lane of wave half h reading the 16 bytes at slot (((s*2 + h)*2 + l/32)*32 +
-// l%32)*4 gets the scales of the four 32-row blocks of half h for step s.
-// Wave w fills slots [128w, 128w+128) with two ubyte loads; load j has
-// s = w/4, h = (w/2)%2 and g = w%2 (uniform), so its lanes differ only in the
-// row: in the interleaved scale layout they read 4 runs of 16 consecutive
-// bytes.  A K-block past the end of
-// K re-reads the last valid one (its codes are zeroed).
+// Scales: dword d = (h * NB + b) * 32 + r of one operand and stage (NB
+// K-blocks per stage) holds the scales of tile rows h*128 + i*32 + r, i =
+// 0..3 (byte i), over K-block b: exactly the dword of the global layout for
+// that 128-row group, block and r, so one 64-lane dword load moves two
+// blocks of a half (256 consecutive bytes) into place.  The waves of one
+// operand (0-3 for A, 4-7 for B) share its NB loads.  A lane reads the dword
+// of its row r and K-block of the step, and the MFMA's op_sel picks the row
+// block.  A K-block past the end of K re-reads the last valid one (its codes
+// are zeroed).
 struct OperandAddr {
   const uint8_t* cbase;  // codes of tile row 0
-  const uint8_t* sbase;  // scale bytes of the tile's first 32-row group, block 0
+  const uint8_t* sbase;  // scale bytes of the tile's first 128-row group, block 0
   uint32_t coff[4];      // per load: row offset of the lane's row
-  uint32_t soff[2];      // per load: offset of the lane's scale row inside the groups
+  uint32_t sgroup;       // scale bytes per 128-row group (128 * blocks per row)
+  int halves;            // 128-row halves of the tile with a valid row (1 or 2)
 };
 
 // 128-byte rows: load j of wave w covers rows 8q .. 8q+7 (q = 4w + j), 8
@@ -169,27 +173,18 @@ __device__ __forceinline__ int dma_chunk(int j, int lane) {
 // [64u, 64u + 64): r / 16 = u % 2, g = (u / 2) % 2, h = (u / 4) % 2, step
 // s = u / 8; half h is fixed per wave
 template <int KIND>
-__device__ __forceinline__ int scale_half(int wave) {
-  return Fmt<KIND>::kScaleLoads == 4 ? (wave & 1) : ((wave >> 1) & 1);
-}
-
-template <int KIND>
 __device__ __forceinline__ OperandAddr make_addr(const Operand& op, int wave, int lane) {
   using F = Fmt<KIND>;
   OperandAddr ad;
   const int64_t nblk = op.nblk;
   ad.cbase = op.base;
-  ad.sbase = op.sbase + (op.row0 >> 5) * nblk * 32;
+  ad.sbase = op.sbase + (op.row0 >> 7) * nblk * 128;
+  ad.sgroup = (uint32_t)(nblk * 128);
+  ad.halves = op.rows_valid > 128 ? 2 : 1;
 #pragma unroll
   for (int j = 0; j < F::kLoads; j++) {
     const int row = min((wave * F::kLoads + j) * (64 / F::kLanesPerRow) + lane / F::kLanesPerRow, op.rows_valid - 1);
     ad.coff[j] = (uint32_t)((int64_t)row * op.ld);
-  }
-#pragma unroll
-  for (int j = 0; j < 2; j++) {
-    const int i = lane & 3, r = (j * 16 + (lane >> 2)) & 31, h = scale_half<KIND>(wave);
-    const int64_t R = op.row0 + min(h * 128 + i * 32 + r, op.rows_valid - 1);
-    ad.soff[j] = (uint32_t)(((R >> 5) - (op.row0 >> 5)) * nblk * 32 + (R & 31));
   }
   return ad;
 }
@@ -219,16 +214,22 @@ __device__ __forceinline__ void zero_codes(uint8_t* tile, int wave, int lane, in
       *reinterpret_cast<uint4*>(tile + (wave * F::kLoads + j) * 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
 }
 
+// this wave's share of one operand's scale loads for the stage at element k
+// (waves 0-3 load A's, 4-7 B's; unit u covers half u / (NB/2), blocks
+// 2 (u % (NB/2)) and one more)
 template <int KIND>
-__device__ __forceinline__ void issue_scales(const OperandAddr& ad, uint8_t* region, int wave, int64_t k,
+__device__ __forceinline__ void issue_scales(const OperandAddr& ad, uint8_t* region, int wave, int lane, int64_t k,
                                              int valid_blocks) {
-  constexpr int L = Fmt<KIND>::kScaleLoads;
+  using F = Fmt<KIND>;
+  constexpr int UPH = F::kBlocks / 2;  // loads per half
 #pragma unroll
-  for (int j = 0; j < L; j++) {
-    const int u = wave * L + j;                                          // (uniform)
-    const int blk = min((u >> 3) * 2 + ((u >> 1) & 1), valid_blocks - 1);  // 2 * step + g
-    __builtin_amdgcn_global_load_lds(ad.sbase + (k + blk * 32) + ad.soff[u & 1], (lds_ptr)(region + u * 256), 1,
-                                     0, 0);
+  for (int j = 0; j < F::kScaleLoads; j++) {
+    const int u = (wave & 3) * F::kScaleLoads + j;  // (uniform)
+    const int h = u / UPH, bp = u % UPH;
+    const int blk = min(2 * bp + (lane >> 5), valid_blocks - 1);
+    const int hs = h < ad.halves ? h : 0;  // a half without valid rows reads the first half's scales
+    __builtin_amdgcn_global_load_lds(ad.sbase + (hs * ad.sgroup + ((k >> 5) + blk) * 128 + (lane & 31) * 4),
+                                     (lds_ptr)(region + (h * F::kBlocks + 2 * bp) * 128), 4, 0, 0);
   }
 }
 
@@ -236,8 +237,7 @@ __device__ __forceinline__ void issue_scales(const OperandAddr& ad, uint8_t* reg
 // per lane each), and the lane's 4 + 2 block scales.
 struct Frags {
   v8i a[TM], b[TN];
-  uint4 sa;
-  uint2 sb;
+  uint32_t sa, sb;  // byte i: row block i of A / B column block (bytes 0, 1 used)
 };
 
 // fragment of the MFMA row block starting at tile row r0, step s of the
@@ -266,28 +266,32 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* codes, int r0, int s, in
 // wn/2: their two scale dwords sit 8*(wn%2) bytes into the lane's 16.
 template <int KIND>
 __device__ __forceinline__ void read_frags(const uint8_t* st, int s, int wm, int wn, int lane, Frags& f) {
-  constexpr int kTileBytes = Fmt<KIND>::kTileBytes, kScaleRegion = Fmt<KIND>::kScaleRegion;
-  const int so = ((lane >> 5) * 32 + (lane & 31)) * 16;
-  f.sa = *reinterpret_cast<const uint4*>(st + 2 * kTileBytes + (s * 2 + wm) * 1024 + so);
-  f.sb = *reinterpret_cast<const uint2*>(st + 2 * kTileBytes + kScaleRegion + (s * 2 + (wn >> 1)) * 1024 + so +
-                                         (wn & 1) * 8);
+  using F = Fmt<KIND>;
+  constexpr int kTileBytes = F::kTileBytes, kScaleRegion = F::kScaleRegion;
+  const int so = (2 * s * 32 + lane) * 4;  // block 2s + lane/32, row lane % 32
+  f.sa = *reinterpret_cast<const uint32_t*>(st + 2 * kTileBytes + wm * (F::kBlocks * 128) + so);
+  // B: the wave's column blocks are row blocks 2 (wn % 2) and 2 (wn % 2) + 1 of half wn / 2
+  f.sb = *reinterpret_cast<const uint32_t*>(st + 2 * kTileBytes + kScaleRegion + (wn >> 1) * (F::kBlocks * 128) +
+                                            so) >> (16 * (wn & 1));
 #pragma unroll
   for (int i = 0; i < TM; i++) f.a[i] = load_frag<KIND>(st, wm * WM + i * 32, s, lane);
 #pragma unroll
   for (int j = 0; j < TN; j++) f.b[j] = load_frag<KIND>(st + kTileBytes, wn * WN + j * 32, s, lane);
 }
 
-__device__ __forceinline__ int u4_get(const uint4& v, int i) {
-  return (int)(i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w);
-}
 
 template <int KIND>
 __device__ __forceinline__ void mfma_step(v16f (&acc)[TM][TN], const Frags& f) {
-#pragma unroll
-  for (int i = 0; i < TM; i++)
-#pragma unroll
-    for (int j = 0; j < TN; j++)
-      acc[i][j] = mfma_scaled<KIND>(f.a[i], f.b[j], acc[i][j], u4_get(f.sa, i), (int)(j == 0 ? f.sb.x : f.sb.y));
+  static_assert(TM == 4 && TN == 2, "the op_sel byte of each block is spelled out");
+  const int sa = (int)f.sa, sb = (int)f.sb;
+  acc[0][0] = mfma_scaled<KIND, 0, 0>(f.a[0], f.b[0], acc[0][0], sa, sb);
+  acc[0][1] = mfma_scaled<KIND, 0, 1>(f.a[0], f.b[1], acc[0][1], sa, sb);
+  acc[1][0] = mfma_scaled<KIND, 1, 0>(f.a[1], f.b[0], acc[1][0], sa, sb);
+  acc[1][1] = mfma_scaled<KIND, 1, 1>(f.a[1], f.b[1], acc[1][1], sa, sb);
+  acc[2][0] = mfma_scaled<KIND, 2, 0>(f.a[2], f.b[0], acc[2][0], sa, sb);
+  acc[2][1] = mfma_scaled<KIND, 2, 1>(f.a[2], f.b[1], acc[2][1], sa, sb);
+  acc[3][0] = mfma_scaled<KIND, 3, 0>(f.a[3], f.b[0], acc[3][0], sa, sb);
+  acc[3][1] = mfma_scaled<KIND, 3, 1>(f.a[3], f.b[1], acc[3][1], sa, sb);
 }
 
 // s_waitcnt with vmcnt(n) only (expcnt / lgkmcnt left at their maximum), gfx9 encoding
@@ -332,8 +336,10 @@ static_assert(sizeof(GroupScratch) <= Fmt<kE2M1>::kStageBytes, "group scratch mu
 // One output tile: where its operands and output live and which K range it
 // reduces over.  All fields are workgroup-uniform.
 struct Tile {
-  int64_t m0, n0;          // first output row / column
-  int rows_a, rows_b;      // valid rows of the A and B tiles (<= 256)
+  int64_t m0, n0;          // first output row / column (multiples of 128)
+  int rows_a, rows_b;      // output rows / columns of the tile end here (<= 256)
+  int row_lo;              // ... and its output rows start here (ragged M: group start - m0)
+  int rows_load;           // A rows of the tile that exist in the matrix (>= rows_a)
   int64_t k_begin, klen;   // reduction range; klen == 0: an empty expert (zeros)
   const uint8_t* b_base;   // B codes of the tile's expert (ragged M) or B
   const uint8_t* sb_base;  // B scales of the tile's expert
@@ -359,7 +365,7 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[TM][TN], const Tile
 #pragma unroll
       for (int r = 0; r < 4; r++) {
         const int row = row0 + i * 32 + 8 * q + r;
-        if (row < tl.rows_a) {
+        if (row >= tl.row_lo && row < tl.rows_a) {
           if (c_ok0) p[0] = acc[i][0][q * 4 + r];
           if (c_ok1) p[32] = acc[i][1][q * 4 + r];
         }
@@ -403,7 +409,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
     n_tiles = tiles_m * tiles_n;
   } else if constexpr (MODE == kRaggedM) {
     __shared__ GroupTable gt;  // read by every tile of the workgroup
-    build_group_table<kThreads>(group_end, G, M, BM, gt, reinterpret_cast<GroupScratch*>(stage1)->scan_tmp);
+    build_group_table<kThreads>(group_end, G, M, BM, gt, reinterpret_cast<GroupScratch*>(stage1)->scan_tmp, 128);
     n_tiles = gt.bstart[G] * tiles_n;  // real m-tiles x n-tiles
     gtp = &gt;
   } else {
@@ -454,6 +460,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
   };
   auto make_tile = [&](int id) {
     Tile tl;
+    tl.row_lo = 0;
     tl.k_begin = 0;
     tl.klen = K;
     tl.b_base = B;
@@ -464,14 +471,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
       raster(id, tiles_m, tiles_n, mt, nt);
       tl.m0 = (int64_t)mt * BM;
       tl.rows_a = (int)min<int64_t>(BM, M - tl.m0);
+      tl.rows_load = tl.rows_a;
     } else if constexpr (MODE == kRaggedM) {
+      // A group's tiles start at the multiple of 128 at or below its first
+      // row (the scale array's 128-row groups); rows of the tile outside the
+      // group are computed with this expert but not stored.
       raster(id, n_tiles / tiles_n, tiles_n, mt, nt);
       const int g = __builtin_amdgcn_readfirstlane(find_group(*gtp, G, mt));
       const int local = mt - __builtin_amdgcn_readfirstlane(gtp->bstart[g]);
-      tl.m0 = (int64_t)__builtin_amdgcn_readfirstlane(gtp->start[g]) + (int64_t)local * BM;
-      tl.rows_a = min(BM, __builtin_amdgcn_readfirstlane(gtp->size[g]) - local * BM);
+      const int start = __builtin_amdgcn_readfirstlane(gtp->start[g]);
+      const int64_t m_al = start & ~127;
+      tl.m0 = m_al + (int64_t)local * BM;
+      tl.row_lo = local == 0 ? start - (int)m_al : 0;
+      tl.rows_a = (int)min<int64_t>(BM, start + __builtin_amdgcn_readfirstlane(gtp->size[g]) - tl.m0);
+      tl.rows_load = (int)min<int64_t>(BM, M - tl.m0);
       tl.b_base = B + (int64_t)g * N * lda;
-      tl.sb_base = sB + (int64_t)g * ((N + 31) / 32 * 32) * (K / 32);  // expert scale arrays hold ceil32(N) rows
+      tl.sb_base = sB + (int64_t)g * ((N + 127) / 128 * 128) * (K / 32);  // expert scale arrays hold ceil128(N) rows
     } else {
       const int per_g = tiles_m * tiles_n;
       const int gi = id / per_g;
@@ -479,6 +494,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
       raster(id - gi * per_g, tiles_m, tiles_n, mt, nt);
       tl.m0 = (int64_t)mt * BM;
       tl.rows_a = (int)min<int64_t>(BM, M - tl.m0);
+      tl.rows_load = tl.rows_a;
       tl.k_begin = (int64_t)__builtin_amdgcn_readfirstlane(kbp[g]) * 32;
       // never past the row length
       const int64_t k_end = min<int64_t>((int64_t)__builtin_amdgcn_readfirstlane(kbp[g + 1]) * 32, K);
@@ -495,7 +511,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
   };
   OperandAddr ada, adb;
   auto addr_of = [&](const Tile& tl) {
-    const Operand opa{A + tl.m0 * lda, sA, tl.m0, lda, K / 32, tl.rows_a};
+    const Operand opa{A + tl.m0 * lda, sA, tl.m0, lda, K / 32, tl.rows_load};
     const Operand opb{tl.b_base + tl.n0 * lda, tl.sb_base, tl.n0, lda, K / 32, tl.rows_b};
     ada = make_addr<KIND>(opa, wave, lane);
     adb = make_addr<KIND>(opb, wave, lane);
@@ -524,8 +540,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
     uint8_t* st = stages[slot];
     issue_codes<KIND>(ada, st, wave, lane, kb, vc);
     issue_codes<KIND>(adb, st + kTileBytes, wave, lane, kb, vc);
-    issue_scales<KIND>(ada, st + 2 * kTileBytes, wave, k, vb);
-    issue_scales<KIND>(adb, st + 2 * kTileBytes + kScaleRegion, wave, k, vb);
+    if (wave < 4)  // (uniform) waves 0-3 load A's scales, 4-7 B's
+      issue_scales<KIND>(ada, st + 2 * kTileBytes, wave, lane, k, vb);
+    else
+      issue_scales<KIND>(adb, st + 2 * kTileBytes + kScaleRegion, wave, lane, k, vb);
   };
   // once stage s of `tl` has landed in `slot` (this wave's part): zero the
   // chunks past the end of K, or all of it if it only pads the loop
@@ -651,8 +669,9 @@ hipError_t launch_gemm_kind(int mode, const uint8_t* A, const uint8_t* sA, const
     if constexpr (KIND == kE2M1W) {
       return hipErrorInvalidValue;  // the wide stage leaves no LDS for the group table
     } else {
-      // every group adds at most one partial m-tile: an upper bound of the tiles
-      const int64_t total = (tiles_m + G) * tiles_n;
+        // a group's tiles start up to 127 rows before it and it may end in a
+      // partial tile: at most two extra m-tiles per group
+      const int64_t total = (tiles_m + 2 * (int64_t)G) * tiles_n;
       if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
       const int64_t grid = total < cus ? total : cus;
       gemm_mx_kernel<kRaggedM, KIND><<<(unsigned)grid, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, ldc,

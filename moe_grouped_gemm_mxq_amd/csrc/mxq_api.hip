@@ -157,7 +157,8 @@ mxq_status mxq_quantize_batched(const uint16_t* x, int64_t batch, int64_t R, int
   MXQ_REQUIRE_DEVICE();
   const int64_t Cp = (C + 31) / 32 * 32, Rp = (R + 31) / 32 * 32;
   // each matrix's outputs exactly as mxq_quantize lays them out, back to back
-  const BatchStrides bs{x_stride, R * Cp, Rp * (Cp / 32), C * Rp, (C + 31) / 32 * 32 * (Rp / 32)};
+  // scale arrays hold ceil128(rows) rows (the GEMM operand scale layout)
+  const BatchStrides bs{x_stride, R * Cp, (R + 127) / 128 * 128 * (Cp / 32), C * Rp, (C + 127) / 128 * 128 * (Rp / 32)};
   if (!col)
     return launched(launch_quant_row(x, R, C, ldx, q_row, s_row, st, (int)batch, bs), "mxq_quantize_batched(row)");
   return launched(launch_quant_tile(x, R, C, ldx, nullptr, 1, Rp, row ? q_row : nullptr, row ? s_row : nullptr,

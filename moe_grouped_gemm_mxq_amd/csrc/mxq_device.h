@@ -75,12 +75,15 @@ __device__ __forceinline__ uint32_t e4m3_encode4(uint32_t lo, uint32_t hi, float
 
 __device__ __forceinline__ float e8m0_as_scale(uint32_t byte) { return __uint_as_float(byte << 23); }
 
-// Byte offset of the scale of row r, block b in an MXFP8 operand's scale array
-// (nblk blocks per row), 32-row interleaved: the scales of rows 32q .. 32q+31
-// for one block are 32 consecutive bytes, so a GEMM tile fetches the scales of
-// many rows for one K-block in a few cache lines.
+// Byte offset of the scale of row r, block b in a GEMM operand's scale array
+// (nblk blocks per row): 128-row groups, then blocks, then r % 32, then
+// (r / 32) % 4.  The four bytes of a dword are the scales of rows r, r+32,
+// r+64, r+96 of one group for one block -- the four MFMA row blocks a GEMM
+// lane multiplies -- so a GEMM stage fetches a 128-row group's scales for
+// two K-blocks with one 64-lane dword load (256 consecutive bytes).  Array
+// size ceil128(rows) * nblk bytes; bytes of rows past the last are padding.
 __device__ __forceinline__ int64_t scale_offset(int64_t r, int64_t b, int64_t nblk) {
-  return ((r >> 5) * nblk + b) * 32 + (r & 31);
+  return (((r >> 7) * nblk + b) * 32 + (r & 31)) * 4 + ((r >> 5) & 3);
 }
 
 // ---------------------------------------------------------------- MXFP4 (E2M1)

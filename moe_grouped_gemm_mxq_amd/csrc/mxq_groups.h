@@ -32,11 +32,13 @@ __device__ __forceinline__ void group_span(const int32_t* __restrict__ group_end
 }
 
 // All THREADS threads of the workgroup must call this; G <= 4 * THREADS.
-// start / size may be null (only the block starts are written then).
+// start / size may be null (only the block starts are written then).  With
+// align > 1 a non-empty group's units start at the multiple of `align` at or
+// below its first row: it counts ceil((size + start % align) / unit) units.
 template <int THREADS>
 __device__ void build_block_starts(const int32_t* __restrict__ group_end, int32_t G, int64_t R,
                                    int32_t unit, int32_t* start, int32_t* size, int32_t* bstart /* [G + 1] */,
-                                   int32_t* scan_tmp /* [THREADS] */) {
+                                   int32_t* scan_tmp /* [THREADS] */, int32_t align = 1) {
   static_assert(4 * THREADS >= kMaxGroups, "each thread owns at most four groups");
   const int t = threadIdx.x;
   int local = 0;
@@ -50,7 +52,7 @@ __device__ void build_block_starts(const int32_t* __restrict__ group_end, int32_
       group_span(group_end, g, R, b, m);
       if (start) start[g] = b;
       if (size) size[g] = m;
-      nb[j] = (m + unit - 1) / unit;
+      nb[j] = m > 0 ? (m + b % align + unit - 1) / unit : 0;
       local += nb[j];
     }
   }
@@ -78,8 +80,9 @@ __device__ void build_block_starts(const int32_t* __restrict__ group_end, int32_
 
 template <int THREADS>
 __device__ void build_group_table(const int32_t* __restrict__ group_end, int32_t G, int64_t R,
-                                  int32_t unit, GroupTable& gt, int32_t* scan_tmp /* [THREADS] */) {
-  build_block_starts<THREADS>(group_end, G, R, unit, gt.start, gt.size, gt.bstart, scan_tmp);
+                                  int32_t unit, GroupTable& gt, int32_t* scan_tmp /* [THREADS] */,
+                                  int32_t align = 1) {
+  build_block_starts<THREADS>(group_end, G, R, unit, gt.start, gt.size, gt.bstart, scan_tmp, align);
 }
 
 // largest g with bstart[g] <= u (u < bstart[G] assumed)

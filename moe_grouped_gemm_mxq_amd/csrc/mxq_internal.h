@@ -31,7 +31,7 @@ hipError_t launch_quant_tile(const uint16_t* x, int64_t R, int64_t C, int64_t ld
 // fp4_scale_params computes them and rejects factors outside [2^-64, 2^64).
 bool fp4_scale_params(float scale_factor, int* F, uint32_t* T);
 // y may be null (quantise only); interleave: scales in the GEMM operand layout
-// (32-row interleaved) instead of row-major.
+// (scale_offset) instead of row-major.
 hipError_t launch_qdq_fp4(const float* x, float* y, int64_t rows, int64_t L, int F, uint32_t T,
                           uint8_t* codes, uint8_t* scales, uint8_t* sat_mask, hipStream_t st,
                           bool interleave = false);

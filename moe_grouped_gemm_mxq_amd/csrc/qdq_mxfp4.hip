@@ -64,8 +64,8 @@ __device__ __forceinline__ uint32_t oct_or(uint32_t v) {
 
 // L % 32 == 0 and 16-byte aligned x / y: the tensor is a flat run of blocks,
 // chunk i = elements 4i..4i+3, block i / 8.
-// y null: quantise only.  nbr > 0: scales in the 32-row interleaved GEMM
-// operand layout for rows of nbr blocks; 0: row-major.
+// y null: quantise only.  nbr > 0: scales in the GEMM operand layout
+// (scale_offset) for rows of nbr blocks; 0: row-major.
 __global__ __launch_bounds__(kThreads) void qdq_flat_kernel(const float* __restrict__ x,
                                                            float* __restrict__ y, int64_t n_chunks,
                                                            Fp4Scale p, uint8_t* __restrict__ codes,

@@ -8,7 +8,7 @@
 // The element conversion is the hardware scaled conversion plus a saturation
 // fix-up (see mxq_device.h); it was checked exhaustively over every bf16 value
 // and every scale byte against the CPU oracle.  Scales are written in the
-// 32-row interleaved layout of scale_offset().
+// GEMM operand layout of scale_offset().
 #include "mxq_device.h"
 #include "mxq_groups.h"
 #include "mxq_internal.h"

@@ -9,10 +9,11 @@ Functions named like the C entry points take every buffer from the caller;
 the lower-case helpers (``quantize``, ``gemm`` ...) allocate the outputs with
 ``torch.empty`` and call them.
 
-MXFP8 scale arrays are uint8 tensors of shape ``scale_shape(rows, nblk)`` =
-``(ceil32(rows) // 32, nblk, 32)``: element ``[r // 32, b, r % 32]`` is the
-E8M0 scale of row ``r``, block ``b`` (the 32-row interleaved layout of
-include/mxq.h).
+GEMM operand scale arrays are uint8 tensors of shape ``scale_shape(rows,
+nblk)`` = ``(ceil128(rows) // 128, nblk, 32, 4)``: element
+``[r // 128, b, r % 32, (r // 32) % 4]`` is the E8M0 scale of row ``r``,
+block ``b`` (the layout of include/mxq.h: each dword holds the scales of
+rows r, r+32, r+64, r+96 of a 128-row group for one block).
 """
 from __future__ import annotations
 
@@ -80,7 +81,7 @@ def _load(path: str = LIB_PATH):
     return lib
 
 
-ABI_VERSION = 3  # MXQ_ABI_VERSION of include/mxq.h this binding is written against
+ABI_VERSION = 4  # MXQ_ABI_VERSION of include/mxq.h this binding is written against
 
 _lib = _load()
 if _lib.mxq_abi_version() != ABI_VERSION:
@@ -126,8 +127,8 @@ def ceil32(v: int) -> int:
 
 
 def scale_shape(rows: int, nblk: int) -> tuple:
-    """Shape of the interleaved scale array of an operand with `rows` rows and `nblk` blocks per row."""
-    return (ceil32(rows) // BLOCK, nblk, BLOCK)
+    """Shape of the GEMM-operand scale array of `rows` rows and `nblk` blocks per row."""
+    return ((rows + 127) // 128, nblk, BLOCK, 4)
 
 
 def _need_out(t, name, shape):
@@ -317,7 +318,7 @@ def mxq_grouped_gemm(mode, A, sA, B, sB, C, group_end, stream=None, fmt=MXQ_FMT_
 
 def mxq_quantize_fp4(x, codes, scales, scale_factor=6.0, stream=None):
     """MXFP4 GEMM operand: x fp32 [rows][L] -> codes uint8 [rows][ceil32(L)/2],
-    scales scale_shape(rows, ceil32(L)/32) (interleaved)."""
+    scales scale_shape(rows, ceil32(L)/32) (the GEMM operand layout)."""
     _need(x, torch.float32, "x")
     if not x.is_contiguous() or x.dim() != 2:
         raise ValueError("x must be a contiguous 2-D tensor")
@@ -399,7 +400,7 @@ def qdq_fp4(x, want_codes=False, stream=None):
 
 
 def quantize_fp4(x, scale_factor=6.0, stream=None):
-    """MXFP4 GEMM operand of a 2-D fp32 tensor: (codes, interleaved scales)."""
+    """MXFP4 GEMM operand of a 2-D fp32 tensor: (codes, scales in the operand layout)."""
     rows, L = x.shape
     codes = _u8((rows, ceil32(L) // 2), x.device)
     scales = _u8(scale_shape(rows, ceil32(L) // BLOCK), x.device)

@@ -19,18 +19,18 @@ def host(t: torch.Tensor) -> np.ndarray:
 
 
 def unpack_scales(s: torch.Tensor, rows: int) -> np.ndarray:
-    """Interleaved MXFP8 scale array of shape (ceil32(rows)/32, nblk, 32)
-    (element [r//32, b, r%32] = scale of row r, block b) -> row-major
-    [rows][nblk] on the host."""
-    q, nblk, b = s.shape
-    assert b == 32 and q * 32 >= rows > q * 32 - 32, (tuple(s.shape), rows)
-    return host(s.permute(0, 2, 1).reshape(q * 32, nblk)[:rows])
+    """GEMM-operand scale array of shape (ceil128(rows)/128, nblk, 32, 4)
+    (element [r//128, b, r%32, (r//32)%4] = scale of row r, block b) ->
+    row-major [rows][nblk] on the host."""
+    q, nblk, b, i = s.shape
+    assert b == 32 and i == 4 and q * 128 >= rows > q * 128 - 128, (tuple(s.shape), rows)
+    return host(s.permute(0, 3, 2, 1).reshape(q * 128, nblk)[:rows])
 
 
 def scale_rows(s: torch.Tensor, idx) -> np.ndarray:
-    """Rows `idx` of an interleaved scale array, row-major [len(idx)][nblk] on the host."""
+    """Rows `idx` of a GEMM-operand scale array, row-major [len(idx)][nblk] on the host."""
     i = torch.as_tensor(np.asarray(idx), device=s.device)
-    return host(s[i // 32, :, i % 32])
+    return host(s[i // 128, :, i % 32, (i // 32) % 4])
 
 
 def out_host(got: dict, key: str, rows: int) -> np.ndarray:

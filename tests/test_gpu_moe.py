@@ -84,14 +84,14 @@ def moe_full():
           "q_colT": torch.empty((G, N, K), dtype=torch.uint8, device="cuda"),
           "s_colT": torch.empty((G,) + m.scale_shape(N, K // 32), dtype=torch.uint8, device="cuda")}
     for g in range(G):   # K % 32 == 0: expert g's rows are row groups [g*K/32, (g+1)*K/32)
-        m.mxq_quantize(W[g], 3, qw["q_row"][g * K:(g + 1) * K], qw["s_row"][g * K // 32:(g + 1) * K // 32],
+        m.mxq_quantize(W[g], 3, qw["q_row"][g * K:(g + 1) * K], qw["s_row"][g * K // 128:(g + 1) * K // 128],
                        qw["q_colT"][g], qw["s_colT"][g])
     Y = m.grouped_gemm(m.MXQ_GG_RAGGED_M, qx["q_row"], qx["s_row"], qw["q_colT"], qw["s_colT"], ge)
     # backward: dY by rows and grouped token axis in one read; X grouped token axis
     qy = m.quantize_grouped(dY, ge, 3)
     qxt = m.quantize_grouped(X, ge, 2, ldq=qy["ldq"])
     dX = m.grouped_gemm(m.MXQ_GG_RAGGED_M, qy["q_row"], qy["s_row"],
-                        qw["q_row"].view(G, K, N), qw["s_row"].view(G, K // 32, N // 32, 32), ge)
+                        qw["q_row"].view(G, K, N), qw["s_row"].view(G, K // 128, N // 32, 32, 4), ge)
     dW = m.grouped_gemm(m.MXQ_GG_RAGGED_K, qxt["q_colT"], qxt["s_colT"], qy["q_colT"], qy["s_colT"], ge)
     torch.cuda.synchronize()
     return dict(X=X, W=W, dY=dY, ge=ge, ge_np=host(ge), qx=qx, qw=qw, qy=qy, qxt=qxt, Y=Y, dX=dX, dW=dW,
@@ -232,7 +232,7 @@ def test_moe_fb_split_equals_dual(moe_full):
     assert torch.equal(fwd_only["s_row"], moe_full["qw"]["s_row"])
     qy = moe_full["qy"]
     dX = m.grouped_gemm(m.MXQ_GG_RAGGED_M, qy["q_row"], qy["s_row"],
-                        fwd_only["q_row"].view(G, K, N), fwd_only["s_row"].view(G, K // 32, N // 32, 32), ge)
+                        fwd_only["q_row"].view(G, K, N), fwd_only["s_row"].view(G, K // 128, N // 32, 32, 4), ge)
     torch.cuda.synchronize()
     assert torch.equal(dX, moe_full["dX"])
 
