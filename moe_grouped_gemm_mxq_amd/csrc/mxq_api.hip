@@ -128,6 +128,7 @@ mxq_status mxq_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, in
   MXQ_REQUIRE((!row || aligned16(q_row)) && (!col || aligned16(q_colT)),
               "mxq_quantize: code outputs must be 16-byte aligned");
   MXQ_REQUIRE(((uintptr_t)x & 1u) == 0, "mxq_quantize: x must be 2-byte aligned");
+  MXQ_REQUIRE(!row || ((uintptr_t)s_row & 3u) == 0, "mxq_quantize: s_row must be 4-byte aligned");
   MXQ_REQUIRE_DEVICE();
   if (!col) return launched(launch_quant_row(x, R, C, ldx, q_row, s_row, st), "mxq_quantize(row)");
   const int64_t Rp = (R + 31) / 32 * 32;
@@ -154,6 +155,7 @@ mxq_status mxq_quantize_batched(const uint16_t* x, int64_t batch, int64_t R, int
   MXQ_REQUIRE((!row || aligned16(q_row)) && (!col || aligned16(q_colT)),
               "mxq_quantize_batched: code outputs must be 16-byte aligned");
   MXQ_REQUIRE(((uintptr_t)x & 1u) == 0, "mxq_quantize_batched: x must be 2-byte aligned");
+  MXQ_REQUIRE(!row || ((uintptr_t)s_row & 3u) == 0, "mxq_quantize_batched: s_row must be 4-byte aligned");
   MXQ_REQUIRE_DEVICE();
   const int64_t Cp = (C + 31) / 32 * 32, Rp = (R + 31) / 32 * 32;
   // each matrix's outputs exactly as mxq_quantize lays them out, back to back
@@ -183,6 +185,7 @@ mxq_status mxq_quantize_grouped(const uint16_t* x, int64_t T, int64_t C, int64_t
   MXQ_REQUIRE((!row || aligned16(q_row)) && (!col || aligned16(q_colT)),
               "mxq_quantize_grouped: code outputs must be 16-byte aligned");
   MXQ_REQUIRE(((uintptr_t)x & 1u) == 0, "mxq_quantize_grouped: x must be 2-byte aligned");
+  MXQ_REQUIRE(!row || ((uintptr_t)s_row & 3u) == 0, "mxq_quantize_grouped: s_row must be 4-byte aligned");
   MXQ_REQUIRE_DEVICE();
   if (!col) return launched(launch_quant_row(x, T, C, ldx, q_row, s_row, st), "mxq_quantize_grouped(row)");
   return launched(launch_quant_tile(x, T, C, ldx, group_end, G, ldq, row ? q_row : nullptr,

@@ -21,12 +21,20 @@ constexpr int kThreads = 256;
 
 // ------------------------------------------------------------------ row copy
 // A row is Cp/8 chunks of 8 bf16 (16 bytes); four consecutive lanes hold one
-// block.  `tpr` (threads per row, a power of two >= 4) lanes share a row and
-// 256/tpr rows are processed per step, so no division is needed.  A lane
-// takes up to kRowUnroll chunks of its row at once and issues all their loads
-// before any arithmetic, so enough bytes are in flight to cover the HBM
-// latency.
+// block.  `tpr` (threads per row, a power of two in [8, 256]) lanes share a
+// row.  A lane takes up to kRowUnroll chunks of its row at once and issues all
+// their loads before any arithmetic, so enough bytes are in flight to cover
+// the HBM latency.
+//
+// The scale bytes of one block of rows r, r+32, r+64, r+96 of a 128-row group
+// share a dword, and the dwords of consecutive r%32 are adjacent, so a byte
+// store per row and block touches one cache line each, which costs as much as
+// the row's loads.  A workgroup therefore takes four 256-thread sub-groups,
+// sub-group j on rows 32j + q .. 32j + q + rps - 1 of a group (rps = 256/tpr),
+// gathers their scale bytes in LDS and writes them as dwords: one line per
+// block for 4 * rps rows.
 constexpr int kRowUnroll = 4;
+constexpr int kRowSub = 256, kRowThreads = 4 * kRowSub;
 
 template <bool VEC>
 __device__ __forceinline__ void load_chunk(const uint16_t* xr, int64_t col, int64_t C, uint32_t (&w)[4]) {
@@ -44,25 +52,38 @@ __device__ __forceinline__ void load_chunk(const uint16_t* xr, int64_t col, int6
 }
 
 template <bool VEC>
-__global__ __launch_bounds__(kThreads) void quant_row_kernel(const uint16_t* __restrict__ x, int64_t R,
-                                                            int64_t C, int64_t ldx, int tpr_log2,
-                                                            uint8_t* __restrict__ q,
-                                                            uint8_t* __restrict__ s, BatchStrides bs) {
+__global__ __launch_bounds__(kRowThreads) void quant_row_kernel(const uint16_t* __restrict__ x, int64_t R,
+                                                               int64_t C, int64_t ldx, int tpr_log2,
+                                                               uint8_t* __restrict__ q,
+                                                               uint8_t* __restrict__ s, BatchStrides bs) {
   // matrix blockIdx.y of a batch
   x += blockIdx.y * bs.x;
   q += blockIdx.y * bs.q_row;
   s += blockIdx.y * bs.s_row;
+  // scale dwords of one column step, double-buffered across steps
+  __shared__ uint32_t sc_lds[2][kRowSub];
   const int64_t Cp = (C + 31) / 32 * 32;
+  const int64_t nblk = Cp / 32;
   const int cpr = (int)(Cp / 8);  // chunks per row (a multiple of 4)
   const int tpr = 1 << tpr_log2;
-  const int rps = kThreads >> tpr_log2;  // rows per step
+  const int rps_log2 = 8 - tpr_log2;  // rows per sub-group, <= 32
   const int t = threadIdx.x;
-  for (int64_t row0 = (int64_t)blockIdx.x * rps; row0 < R; row0 += (int64_t)gridDim.x * rps) {
-    const int64_t row = row0 + (t >> tpr_log2);
+  const int j = t >> 8;                       // sub-group: 32-row block of the group
+  const int i = (t & (kRowSub - 1)) >> tpr_log2;  // row within the sub-group's run
+  const int lc = t & (tpr - 1);               // lane within the row
+  const int per_group = 32 >> rps_log2;       // workgroups per 128-row group
+  const int64_t n_units = (R + 127) / 128 * per_group;
+  const int n_steps = (cpr + kRowUnroll * tpr - 1) / (kRowUnroll * tpr);  // uniform
+  int parity = 0;
+  for (int64_t unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
+    const int64_t g = unit / per_group;
+    const int qb = (int)(unit - g * per_group) << rps_log2;
+    const int64_t row = g * 128 + 32 * j + qb + i;
     const bool row_ok = row < R;  // uniform per quad
     const uint16_t* xr = x + (row_ok ? row : 0) * ldx;
-    for (int c0 = t & (tpr - 1); c0 < cpr; c0 += kRowUnroll * tpr) {
-      // (c < cpr is uniform per quad: cpr and tpr are multiples of 4)
+    for (int step = 0; step < n_steps; step++, parity ^= 1) {
+      uint8_t* lds_bytes = reinterpret_cast<uint8_t*>(sc_lds[parity]);
+      const int c0 = step * kRowUnroll * tpr + lc;
       uint32_t w[kRowUnroll][4];
       if (VEC && C % 8 == 0) {
         // unconditional 16-byte loads from clamped columns (chunks past C are
@@ -87,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(const uint16_t* __r
 #pragma unroll
       for (int u = 0; u < kRowUnroll; u++) {
         const int c8 = c0 + u * tpr;
-        if (c8 >= cpr) break;
+        if (c8 >= cpr) break;  // (uniform per quad: cpr and tpr are multiples of 4)
         const int64_t col = (int64_t)c8 * 8;
         uint32_t m = hmax_u16x2(pkmax_u16(absmax_bf16x2(w[u][0], w[u][1]), absmax_bf16x2(w[u][2], w[u][3])));
         m = quad_max_u32(m);
@@ -96,9 +117,30 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(const uint16_t* __r
         uint2 codes;
         codes.x = e4m3_encode4(w[u][0], w[u][1], sc);
         codes.y = e4m3_encode4(w[u][2], w[u][3], sc);
-        if (row_ok) {
-          *reinterpret_cast<uint2*>(q + row * Cp + col) = codes;
-          if ((c8 & 3) == 0) s[scale_offset(row, c8 / 4, Cp / 32)] = (uint8_t)byte;
+        if (row_ok) *reinterpret_cast<uint2*>(q + row * Cp + col) = codes;
+        if ((c8 & 3) == 0) {
+          const int bl = (c8 >> 2) - step * tpr;  // block within the step, < tpr
+          lds_bytes[((bl << rps_log2) + i) * 4 + j] = row_ok ? (uint8_t)byte : (uint8_t)0;
+        }
+      }
+      __syncthreads();
+      // one dword per (block, row of the run): bytes of rows +0, +32, +64, +96;
+      // the next step fills the other buffer, and the one after that waits at
+      // the next step's barrier, which these reads precede
+      if (t < kRowSub) {
+        const int bl = t >> rps_log2, ii = t & ((1 << rps_log2) - 1);
+        const int64_t blk = (int64_t)step * tpr + bl;
+        if (blk < nblk) {
+          uint8_t* dst = s + ((g * nblk + blk) * 32 + qb + ii) * 4;
+          const uint32_t v = sc_lds[parity][t];
+          const int64_t r0 = g * 128 + qb + ii;
+          if (r0 + 96 < R) {
+            *reinterpret_cast<uint32_t*>(dst) = v;
+          } else {  // last, partial group: bytes of rows past R stay untouched
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++)
+              if (r0 + 32 * jj < R) dst[jj] = (uint8_t)(v >> (8 * jj));
+          }
         }
       }
     }
@@ -269,20 +311,20 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
 hipError_t launch_quant_row(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q,
                             uint8_t* s, hipStream_t st, int batch, BatchStrides bs) {
   const int64_t cpr = (C + 31) / 32 * 4;
-  int tpr_log2 = 2;
+  int tpr_log2 = 3;  // at most 32 rows per sub-group
   while ((1 << tpr_log2) < cpr && tpr_log2 < 8) tpr_log2++;
-  const int64_t rps = kThreads >> tpr_log2;
-  const int64_t want = (R + rps - 1) / rps;
-  // one workgroup per row step (many short workgroups stream HBM faster than
-  // a grid-stride loop over a CU-sized grid); capped by the grid-size limit
+  const int64_t per_group = 32 >> (8 - tpr_log2);
+  const int64_t want = (R + 127) / 128 * per_group;
+  // one workgroup per unit of rows (many short workgroups stream HBM faster
+  // than a grid-stride loop over a CU-sized grid); capped by the grid limit
   const int64_t cap = 0x7FFFFFFF;
   const int grid = (int)(want < cap ? want : cap);
   const bool vec = (ldx % 8 == 0) && ((uintptr_t)x % 16 == 0) && (batch == 1 || bs.x % 8 == 0);
   const dim3 g((unsigned)grid, (unsigned)batch);
   if (vec)
-    quant_row_kernel<true><<<g, kThreads, 0, st>>>(x, R, C, ldx, tpr_log2, q, s, bs);
+    quant_row_kernel<true><<<g, kRowThreads, 0, st>>>(x, R, C, ldx, tpr_log2, q, s, bs);
   else
-    quant_row_kernel<false><<<g, kThreads, 0, st>>>(x, R, C, ldx, tpr_log2, q, s, bs);
+    quant_row_kernel<false><<<g, kRowThreads, 0, st>>>(x, R, C, ldx, tpr_log2, q, s, bs);
   return hipGetLastError();
 }
 

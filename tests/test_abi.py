@@ -90,6 +90,14 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     assert call(lib, "mxq_quantize", FAKE, I64(4), I64(32), I64(32), 4, FAKE, FAKE, FAKE, FAKE, P(0)) == 1
     # misaligned code output
     assert call(lib, "mxq_quantize", FAKE, I64(4), I64(32), I64(32), 1, P(0x1001), FAKE, P(0), P(0), P(0)) == 1
+    # misaligned row scales (the row quantiser stores them as dwords)
+    assert call(lib, "mxq_quantize", FAKE, I64(4), I64(32), I64(32), 1, FAKE, P(0x1002), P(0), P(0), P(0)) == 1
+    assert "s_row" in err(lib)
+    assert call(lib, "mxq_quantize_batched", FAKE, I64(1), I64(4), I64(32), I64(32), I64(128), 1, FAKE,
+                P(0x1001), P(0), P(0), P(0)) == 1
+    assert call(lib, "mxq_quantize_grouped", FAKE, I64(64), I64(32), I64(32), FAKE, ctypes.c_int32(2),
+                I64(64), 1, FAKE, P(0x1003), P(0), P(0), P(0)) == 1
+    assert "s_row" in err(lib)
     # GEMM: K not a multiple of 32, ldc < N, bad format
     assert call(lib, "mxq_gemm", FAKE, FAKE, FAKE, FAKE, FAKE, I64(4), I64(4), I64(48), I64(4), 0, P(0)) == 1
     assert "multiple of 32" in err(lib)

@@ -112,8 +112,12 @@ def test_dense_fb_split_equals_dual():
     dual_x, dual_w = m.quantize(Xd, 3), m.quantize(Wd, 3)
     fb_x = {**m.quantize(Xd, 1), **m.quantize(Xd, 2)}   # forward rows, backward columns
     fb_w = {**m.quantize(Wd, 2), **m.quantize(Wd, 1)}
-    for k in ("q_row", "s_row", "q_colT", "s_colT"):
+    # every copy equal (scales: the rows the operand has; padding rows are unspecified)
+    for k in ("q_row", "q_colT"):
         assert torch.equal(dual_x[k], fb_x[k]) and torch.equal(dual_w[k], fb_w[k]), k
+    for k, rx, rw in (("s_row", M, K), ("s_colT", K, N)):
+        assert np.array_equal(unpack_scales(dual_x[k], rx), unpack_scales(fb_x[k], rx)), k
+        assert np.array_equal(unpack_scales(dual_w[k], rw), unpack_scales(fb_w[k], rw)), k
     qy = m.quantize(dYd, 3)
     grads = []
     for qx, qw in ((dual_x, dual_w), (fb_x, fb_w)):

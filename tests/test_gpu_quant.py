@@ -175,6 +175,33 @@ def test_quantize_bitexact(shape, axis):
         assert_bytes_equal(out_host(got, k, v.shape[0]), v, f"{k} {shape}")
 
 
+@pytest.mark.parametrize("R,C", [(300, 257), (97, 8200), (1, 40), (4097, 7168)])
+@pytest.mark.parametrize("axis", [1, 2, 3])
+def test_quantize_leaves_scale_padding_untouched(R, C, axis):
+    """Scale arrays have ceil128(rows) rows; the bytes of rows past `rows` (a
+    sentinel here) are never written, by the row kernel or the tile kernel."""
+    m = mxq()
+    x = scaled_randn((R, C), seed=R + C)
+    Cp, Rp = (C + 31) // 32 * 32, (R + 31) // 32 * 32
+    dev = torch.device("cuda")
+    out = dict(q_row=torch.empty(R, Cp, dtype=torch.uint8, device=dev),
+               s_row=torch.full(m.scale_shape(R, Cp // 32), 0xA5, dtype=torch.uint8, device=dev),
+               q_colT=torch.empty(C, Rp, dtype=torch.uint8, device=dev),
+               s_colT=torch.full(m.scale_shape(C, Rp // 32), 0xA5, dtype=torch.uint8, device=dev))
+    row, col = axis & 1, axis & 2
+    m.mxq_quantize(x.cuda(), axis, out["q_row"] if row else None, out["s_row"] if row else None,
+                   out["q_colT"] if col else None, out["s_colT"] if col else None)
+    torch.cuda.synchronize()
+    for k, v in quant_ref(bits(x), axis).items():
+        if k.startswith("s_"):
+            sc = out[k]
+            full = host(sc.permute(0, 3, 2, 1).reshape(sc.shape[0] * 128, sc.shape[1]))
+            assert np.all(full[v.shape[0]:] == 0xA5), f"{k} padding written {R}x{C}"
+            assert_bytes_equal(full[:v.shape[0]], v, f"{k} {R}x{C}")
+        else:
+            assert_bytes_equal(host(out[k]), v, f"{k} {R}x{C}")
+
+
 @pytest.mark.parametrize("C,pad", [(200, 8), (203, 3)])
 def test_quantize_strided_input(C, pad):
     """x is a column slice of a wider matrix (row stride C+pad)."""
