@@ -18,12 +18,11 @@
 // waits on its LDS reads, and keep enough LDS requests in flight for the LDS
 // to serve both the fragment reads and the direct loads writing into it.
 //
-// Element formats (Fmt): E4M3 and a wide E2M1 stage hold 128 code bytes per
-// tile row (128 or 256 elements, 2 or 4 MFMA steps); the narrow E2M1 stage
-// holds 64 (128 elements), leaving LDS for the grouped modes' tables.
+// Element formats (Fmt): an E4M3 or E2M1 stage holds 128 code bytes per tile
+// row (128 or 256 elements, 2 or 4 MFMA steps).
 //
-// Pipeline: codes (global_load_lds_dwordx4) and scale bytes
-// (global_load_lds_ubyte) go from global memory straight into LDS.  LDS holds
+// Pipeline: codes (global_load_lds_dwordx4) and scale dwords
+// (global_load_lds_dword) go from global memory straight into LDS.  LDS holds
 // two stages (with 128 code bytes per tile row every 16-byte lane load belongs
 // to a fully used 128-byte line); the loads of a stage are issued one stage
 // before its first use.  One s_barrier per stage (raw, with explicit vmcnt /
@@ -55,24 +54,22 @@ constexpr int BM = 256, BN = 256, BK = 64;   // BK: codes (bytes) per MFMA step
 constexpr int WM = 128, WN = 64;              // wave tile
 constexpr int TM = WM / 32, TN = WN / 32;     // MFMA blocks per wave
 
-// Layout of one LDS stage per operand kind.  E4M3 codes take a byte, E2M1
-// codes (two per byte, element 2j in the low nibble) half of one.
-//   kE4M3:   128 elements (2 MFMA steps) per tile row = 128 code bytes;
-//   kE2M1:   128 elements (2 steps) = 64 code bytes (a 40 KB stage, which
-//            leaves LDS room for the grouped modes' tables);
-//   kE2M1W:  256 elements (4 steps) = 128 code bytes, the E4M3 byte layout,
-//            twice the scales (an 80 KB stage: two fill the 160 KB of LDS;
-//            dense only).  Every load then reads whole 128-byte lines.
-enum Kind { kE4M3 = 0, kE2M1 = 1, kE2M1W = 2 };
+// Layout of one LDS stage per operand kind: 128 code bytes per tile row, so
+// every load reads whole 128-byte lines.  E4M3 codes take a byte, E2M1 codes
+// (two per byte, element 2j in the low nibble) half of one.
+//   kE4M3:  128 elements (2 MFMA steps) per tile row, a 66 KB stage;
+//   kE2M1:  256 elements (4 steps) with twice the scales, a 68 KB stage that
+//           carries twice the MFMA work for the same code bytes.
+enum Kind { kE4M3 = 0, kE2M1 = 1 };
 template <int KIND>
 struct Fmt {
   static constexpr bool kFp4 = KIND != kE4M3;
-  static constexpr int kSteps = KIND == kE2M1W ? 4 : 2;                  // MFMA steps per stage
+  static constexpr int kSteps = kFp4 ? 4 : 2;                            // MFMA steps per stage
   static constexpr int kStageElems = kSteps * BK;                        // elements per tile row and stage
-  static constexpr int kRowBytes = KIND == kE2M1 ? 64 : 128;             // code bytes per tile row
+  static constexpr int kRowBytes = 128;                                  // code bytes per tile row
   static constexpr int kChunks = kRowBytes / 16;                         // 16-byte chunks per row
   static constexpr int kElemsPerChunk = kStageElems / kChunks;           // 16 / 32
-  static constexpr int kTileBytes = BM * kRowBytes;                      // per operand (32 KB / 16 KB)
+  static constexpr int kTileBytes = BM * kRowBytes;                      // per operand (32 KB)
   static constexpr int kBlocks = 2 * kSteps;                             // K-blocks per stage
   static constexpr int kScaleRegion = 2 * kBlocks * 32 * 4;              // one dword per (half, block, row % 32)
   static constexpr int kStageBytes = 2 * kTileBytes + 2 * kScaleRegion;  // A, B codes, A, B scales
@@ -93,23 +90,14 @@ __device__ __forceinline__ v16f mfma_scaled(const v8i& a, const v8i& b, const v1
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, f, f, I, sa, J, sb);
 }
 
-// LDS position of 16-byte chunk c of tile row r.  A fragment read has its
-// lanes on consecutive rows at one chunk.
-//  E4M3 (8 chunks, 128 bytes per row): XOR swizzle f(r) = (r & 7) ^ ((r >> 3)
-//    & 1) makes any 8 aligned consecutive rows land on 8 distinct 16-byte
-//    bank groups of a 128-byte bank row (32 banks) and any 16 on 16 distinct
-//    groups of a 256-byte one (64 banks);
-//  narrow E2M1 (4 chunks, 64 bytes per row): rows r .. r+3 fill one 256-byte bank
-//    row and f(r) = (r >> 2) & 3 moves the chunk within each row's quarter
-//    for every group of four rows, so any 16 consecutive rows hit 16 distinct
-//    bank groups.
-// Either way the read is conflict-free.  (Wide E2M1 uses the E4M3 layout.)
-template <int KIND>
+// LDS position of 16-byte chunk c of tile row r (8 chunks, 128 bytes per
+// row).  A fragment read has its lanes on consecutive rows at one chunk; the
+// XOR swizzle f(r) = (r & 7) ^ ((r >> 3) & 1) makes any 8 aligned consecutive
+// rows land on 8 distinct 16-byte bank groups of a 128-byte bank row (32
+// banks) and any 16 on 16 distinct groups of a 256-byte one (64 banks), so
+// the read is conflict-free.
 __device__ __forceinline__ int swz(int r, int c) {
-  if constexpr (KIND == kE2M1)
-    return r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
-  else
-    return r * 128 + ((c ^ ((r & 7) ^ ((r >> 3) & 1))) << 4);
+  return r * 128 + ((c ^ ((r & 7) ^ ((r >> 3) & 1))) << 4);
 }
 
 // One operand of one workgroup tile: tile rows [0, rows_valid), which are rows
@@ -157,21 +145,13 @@ struct OperandAddr {
   int halves;            // 128-row halves of the tile with a valid row (1 or 2)
 };
 
-// 128-byte rows: load j of wave w covers rows 8q .. 8q+7 (q = 4w + j), 8
-// lanes a row; narrow E2M1: rows 16q .. 16q+15 (q = 2w + j), 4 lanes a row.
-// Lane l fills slot l % lanes-per-row of its row, which holds chunk
-// slot ^ f(row).
-template <int KIND>
+// Load j of wave w covers tile rows 8q .. 8q+7 (q = 4w + j), 8 lanes a row.
+// Lane l fills slot l % 8 of its row, which holds chunk slot ^ f(row).
 __device__ __forceinline__ int dma_chunk(int j, int lane) {
-  if constexpr (KIND == kE2M1)
-    return (lane & 3) ^ (lane >> 4);
-  else
-    return (lane & 7) ^ (lane >> 3) ^ (j & 1);
+  return (lane & 7) ^ (lane >> 3) ^ (j & 1);
 }
 
-// scale loads: unit u = w * L + j (L loads per wave) fills slots
-// [64u, 64u + 64): r / 16 = u % 2, g = (u / 2) % 2, h = (u / 4) % 2, step
-// s = u / 8; half h is fixed per wave
+// per-lane code row offsets and the tile's scale base of one operand
 template <int KIND>
 __device__ __forceinline__ OperandAddr make_addr(const Operand& op, int wave, int lane) {
   using F = Fmt<KIND>;
@@ -195,8 +175,8 @@ __device__ __forceinline__ void issue_codes(const OperandAddr& ad, uint8_t* tile
                                             int valid_chunks) {
   using F = Fmt<KIND>;
   const uint8_t* base = ad.cbase + kb;
-  const uint32_t c0 = (uint32_t)min(dma_chunk<KIND>(0, lane), valid_chunks - 1) * 16;
-  const uint32_t c1 = (uint32_t)min(dma_chunk<KIND>(1, lane), valid_chunks - 1) * 16;
+  const uint32_t c0 = (uint32_t)min(dma_chunk(0, lane), valid_chunks - 1) * 16;
+  const uint32_t c1 = (uint32_t)min(dma_chunk(1, lane), valid_chunks - 1) * 16;
 #pragma unroll
   for (int j = 0; j < F::kLoads; j++)
     __builtin_amdgcn_global_load_lds(base + (ad.coff[j] + ((j & 1) ? c1 : c0)),
@@ -210,7 +190,7 @@ __device__ __forceinline__ void zero_codes(uint8_t* tile, int wave, int lane, in
   using F = Fmt<KIND>;
 #pragma unroll
   for (int j = 0; j < F::kLoads; j++)
-    if (dma_chunk<KIND>(j, lane) >= valid_chunks)
+    if (dma_chunk(j, lane) >= valid_chunks)
       *reinterpret_cast<uint4*>(tile + (wave * F::kLoads + j) * 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
 }
 
@@ -250,12 +230,12 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* codes, int r0, int s, in
   const int g = lane >> 5;
   v8i f;
   if constexpr (KIND != kE4M3) {
-    const uint4 lo = *reinterpret_cast<const uint4*>(codes + swz<KIND>(r, 2 * s + g));
+    const uint4 lo = *reinterpret_cast<const uint4*>(codes + swz(r, 2 * s + g));
     f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
     f[4] = 0; f[5] = 0; f[6] = 0; f[7] = 0;
   } else {
-    const uint4 lo = *reinterpret_cast<const uint4*>(codes + swz<KIND>(r, 4 * s + g));
-    const uint4 hi = *reinterpret_cast<const uint4*>(codes + swz<KIND>(r, 4 * s + 2 + g));
+    const uint4 lo = *reinterpret_cast<const uint4*>(codes + swz(r, 4 * s + g));
+    const uint4 hi = *reinterpret_cast<const uint4*>(codes + swz(r, 4 * s + 2 + g));
     f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
     f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
   }
@@ -331,7 +311,8 @@ struct GroupScratch {
   int32_t scan_tmp[kThreads];
   int32_t order[kMaxGroups];
 };
-static_assert(sizeof(GroupScratch) <= Fmt<kE2M1>::kStageBytes, "group scratch must fit in one stage");
+static_assert(sizeof(GroupScratch) <= Fmt<kE4M3>::kStageBytes && sizeof(GroupScratch) <= Fmt<kE2M1>::kStageBytes,
+              "group scratch must fit in one stage");
 
 // One output tile: where its operands and output live and which K range it
 // reduces over.  All fields are workgroup-uniform.
@@ -666,17 +647,13 @@ hipError_t launch_gemm_kind(int mode, const uint8_t* A, const uint8_t* sA, const
     gemm_mx_kernel<kDense, KIND><<<(unsigned)grid, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, ldc, nullptr, 1,
                                                                        (int)tiles_m, (int)tiles_n);
   } else if (mode == kRaggedM) {
-    if constexpr (KIND == kE2M1W) {
-      return hipErrorInvalidValue;  // the wide stage leaves no LDS for the group table
-    } else {
-        // a group's tiles start up to 127 rows before it and it may end in a
-      // partial tile: at most two extra m-tiles per group
-      const int64_t total = (tiles_m + 2 * (int64_t)G) * tiles_n;
-      if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-      const int64_t grid = total < cus ? total : cus;
-      gemm_mx_kernel<kRaggedM, KIND><<<(unsigned)grid, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, ldc,
-                                                                           group_end, G, (int)tiles_m, (int)tiles_n);
-    }
+    // a group's tiles start up to 127 rows before it and it may end in a
+    // partial tile: at most two extra m-tiles per group
+    const int64_t total = (tiles_m + 2 * (int64_t)G) * tiles_n;
+    if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const int64_t grid = total < cus ? total : cus;
+    gemm_mx_kernel<kRaggedM, KIND><<<(unsigned)grid, kThreads, 0, st>>>(A, sA, B, sB, C, M, N, K, ldc,
+                                                                         group_end, G, (int)tiles_m, (int)tiles_n);
   } else {
     if constexpr (KIND != kE4M3) {
       return hipErrorInvalidValue;  // no E2M1 token-axis operands
@@ -696,9 +673,6 @@ hipError_t launch_gemm(int mode, bool fp4, const uint8_t* A, const uint8_t* sA, 
                        const int32_t* group_end, int32_t G, hipStream_t st) {
   if (!fp4) return launch_gemm_kind<kE4M3>(mode, A, sA, B, sB, C, M, N, K, ldc, group_end, G, st);
   if (mode == kRaggedK) return hipErrorInvalidValue;  // no E2M1 token-axis operands
-  // dense E2M1 runs the wide stage (two of them fill the LDS); the grouped
-  // modes need LDS for their tables and run the narrow one
-  if (mode == kDense) return launch_gemm_kind<kE2M1W>(mode, A, sA, B, sB, C, M, N, K, ldc, group_end, G, st);
   return launch_gemm_kind<kE2M1>(mode, A, sA, B, sB, C, M, N, K, ldc, group_end, G, st);
 }
 

@@ -83,9 +83,10 @@ def test_gemm_fp4_full_size_sampled():
 
 
 @pytest.mark.parametrize("sizes", [[5, 0, 300, 33], [256, 1, 0, 0, 513]])
-def test_grouped_gemm_fp4_ragged_m(sizes):
+@pytest.mark.parametrize("K", [192, 608])
+def test_grouped_gemm_fp4_ragged_m(sizes, K):
     m = mxq()
-    T, N, K, G = sum(sizes), 96, 192, len(sizes)
+    T, N, G = sum(sizes), 96, len(sizes)
     x = fp4_inputs((T, K), T + 7)
     w = fp4_inputs((G * N, K), T + 8)
     ge_np = np.cumsum(sizes).astype(np.int32)
