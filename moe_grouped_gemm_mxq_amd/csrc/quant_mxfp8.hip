@@ -151,8 +151,13 @@ __global__ __launch_bounds__(kRowThreads) void quant_row_kernel(const uint16_t* 
 // A 128 x 128 bf16 tile (128 rows of padded position space = 4 blocks, 128
 // columns) is read once with coalesced 16-byte loads, optionally quantised
 // along its rows (four lanes per block), staged in LDS, and quantised down its
-// columns: each thread takes a column pair and one block of 32 rows.
+// columns: each thread takes a column pair and one block of 32 rows.  The
+// column codes go back through LDS as a [column][row] code tile, so that eight
+// lanes store one column's 128 codes together: stored straight from the
+// column-pair lanes, every 16-byte store would touch its own cache line.
 constexpr int kTR = 128, kTC = 128, kLdsStride = kTC * 2 + 16;
+constexpr int kCodePitch = kTR + 16;  // code tile row pitch: 16-byte aligned, 4-pass b128 reads
+static_assert(kTC * kCodePitch <= kTR * kLdsStride, "the code tile reuses the bf16 tile's LDS");
 
 template <bool ROW, bool GROUPED, bool VEC>
 __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
@@ -270,39 +275,60 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
   const int pr = t & 63;  // column pair
   const int rb = t >> 6;  // block of 32 tile rows
   const int64_t col = c0 + 2 * pr;
-  if (rb_valid[rb] <= 0 || col >= C) return;
+  const bool blk_ok = rb_valid[rb] > 0 && col < C;  // (every thread reaches both barriers below)
   const int64_t pb = p0 / 32 + rb;  // padded block = output block column
-  uint32_t d[32];
-#pragma unroll
-  for (int i = 0; i < 32; i++)
-    d[i] = *reinterpret_cast<const uint32_t*>(tile + (rb * 32 + i) * kLdsStride + 4 * pr);
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 32; i += 2) m = pkmax_u16(m, absmax_bf16x2(d[i], d[i + 1]));
-  // absmax_bf16x2 keeps per-half maxima: low half = column col, high half = col + 1
-  const uint32_t byte_lo = mxfp8_scale_byte(m & 0xFFFFu);
-  const uint32_t byte_hi = mxfp8_scale_byte(m >> 16);
-  const float sc_lo = e8m0_as_scale(byte_lo), sc_hi = e8m0_as_scale(byte_hi);
   uint32_t clo[8], chi[8];
+  {
+    uint32_t d[32];
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const uint32_t a0 = __builtin_amdgcn_perm(d[4 * i + 1], d[4 * i], 0x05040100u);
-    const uint32_t a1 = __builtin_amdgcn_perm(d[4 * i + 3], d[4 * i + 2], 0x05040100u);
-    const uint32_t b0 = __builtin_amdgcn_perm(d[4 * i + 1], d[4 * i], 0x07060302u);
-    const uint32_t b1 = __builtin_amdgcn_perm(d[4 * i + 3], d[4 * i + 2], 0x07060302u);
-    clo[i] = e4m3_encode4(a0, a1, sc_lo);
-    chi[i] = e4m3_encode4(b0, b1, sc_hi);
+    for (int i = 0; i < 32; i++)
+      d[i] = *reinterpret_cast<const uint32_t*>(tile + (rb * 32 + i) * kLdsStride + 4 * pr);
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 32; i += 2) m = pkmax_u16(m, absmax_bf16x2(d[i], d[i + 1]));
+    // absmax_bf16x2 keeps per-half maxima: low half = column col, high half = col + 1
+    const uint32_t byte_lo = mxfp8_scale_byte(m & 0xFFFFu);
+    const uint32_t byte_hi = mxfp8_scale_byte(m >> 16);
+    const float sc_lo = e8m0_as_scale(byte_lo), sc_hi = e8m0_as_scale(byte_hi);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const uint32_t a0 = __builtin_amdgcn_perm(d[4 * i + 1], d[4 * i], 0x05040100u);
+      const uint32_t a1 = __builtin_amdgcn_perm(d[4 * i + 3], d[4 * i + 2], 0x05040100u);
+      const uint32_t b0 = __builtin_amdgcn_perm(d[4 * i + 1], d[4 * i], 0x07060302u);
+      const uint32_t b1 = __builtin_amdgcn_perm(d[4 * i + 3], d[4 * i + 2], 0x07060302u);
+      clo[i] = e4m3_encode4(a0, a1, sc_lo);
+      chi[i] = e4m3_encode4(b0, b1, sc_hi);
+    }
+    if (blk_ok) {
+      // one byte per column and block: the 128 columns of a wave share one line
+      const int64_t nsb = ldq / 32;
+      s_colT[scale_offset(col, pb, nsb)] = (uint8_t)byte_lo;
+      if (col + 1 < C) s_colT[scale_offset(col + 1, pb, nsb)] = (uint8_t)byte_hi;
+    }
   }
-  const int64_t nsb = ldq / 32;
-  uint8_t* dst = q_colT + col * ldq + pb * 32;
-  reinterpret_cast<uint4*>(dst)[0] = make_uint4(clo[0], clo[1], clo[2], clo[3]);
-  reinterpret_cast<uint4*>(dst)[1] = make_uint4(clo[4], clo[5], clo[6], clo[7]);
-  s_colT[scale_offset(col, pb, nsb)] = (uint8_t)byte_lo;
-  if (col + 1 < C) {
-    dst += ldq;
-    reinterpret_cast<uint4*>(dst)[0] = make_uint4(chi[0], chi[1], chi[2], chi[3]);
-    reinterpret_cast<uint4*>(dst)[1] = make_uint4(chi[4], chi[5], chi[6], chi[7]);
-    s_colT[scale_offset(col + 1, pb, nsb)] = (uint8_t)byte_hi;
+  __syncthreads();  // every thread has read its column pair: the tile's LDS now holds codes
+  {
+    uint8_t* cl = tile + (2 * pr) * kCodePitch + rb * 32;
+    reinterpret_cast<uint4*>(cl)[0] = make_uint4(clo[0], clo[1], clo[2], clo[3]);
+    reinterpret_cast<uint4*>(cl)[1] = make_uint4(clo[4], clo[5], clo[6], clo[7]);
+    cl += kCodePitch;
+    reinterpret_cast<uint4*>(cl)[0] = make_uint4(chi[0], chi[1], chi[2], chi[3]);
+    reinterpret_cast<uint4*>(cl)[1] = make_uint4(chi[4], chi[5], chi[6], chi[7]);
+  }
+  __syncthreads();
+  // lane l of wave w stores 16 codes (rows 16 (l % 8) ..) of tile column
+  // 8 (4 i + w) + l / 8: eight lanes cover one output row's 128 bytes
+  const int k = t & 7;
+  const int rbk = k >> 1;  // block of those rows
+  if (rb_valid[rbk] > 0) {
+#pragma unroll
+    for (int i = 0; i < kTC / 32; i++) {
+      const int cc = 8 * (4 * i + (t >> 6)) + ((t & 63) >> 3);
+      const int64_t cg = c0 + cc;
+      if (cg < C)
+        *reinterpret_cast<uint4*>(q_colT + cg * ldq + p0 + 16 * k) =
+            *reinterpret_cast<const uint4*>(tile + cc * kCodePitch + 16 * k);
+    }
   }
 }
 
