@@ -111,12 +111,18 @@ __device__ __forceinline__ int mxfp4_scale_exp(uint32_t amax_bits, Fp4Scale p) {
   return e < -30 ? -30 : e;
 }
 
-// codebook index (0..7 for 0,0.5,1,1.5,2,3,4,6) of |x| / 2^e: count the midpoints
-// |x| reaches (ties go up).  yabs = |x| * 2^-e is exact.
+// codebook index (0..7 for 0,0.5,1,1.5,2,3,4,6) of |x| / 2^e: the number of
+// midpoints (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5) that yabs = |x| * 2^-e
+// (exact) reaches, so ties go up.  Every midpoint starts a quarter of its
+// binade, so the index depends only on the exponent and the top two mantissa
+// bits: bits >> 21, clamped to the 21 values from [0.21875, 0.25) (index 0,
+// like everything below) to [7, 8) (index 7, like everything above), picks a
+// 3-bit entry of kFp4IndexTable.  Checked against the midpoint count for every
+// finite non-negative fp32 value.
+constexpr uint64_t kFp4IndexTable = 0x7ff6b646d2449248ull;  // entries 0,1,1,1,1,1,1,2,2,2,3,3,4,4,5,5,6,6,7,7,7
 __device__ __forceinline__ uint32_t mxfp4_index(float yabs) {
-  return (uint32_t)(yabs >= 0.25f) + (uint32_t)(yabs >= 0.75f) + (uint32_t)(yabs >= 1.25f) +
-         (uint32_t)(yabs >= 1.75f) + (uint32_t)(yabs >= 2.5f) + (uint32_t)(yabs >= 3.5f) +
-         (uint32_t)(yabs >= 5.0f);
+  const uint32_t k = min(max(__float_as_uint(yabs) >> 21, 499u), 519u) - 499u;
+  return (uint32_t)(kFp4IndexTable >> (3 * k)) & 7u;
 }
 
 // fp32 bits of codebook[idx] * 2^e with the sign bit `sign` (0 or 0x80000000).
