@@ -12,7 +12,10 @@ One step = one pass of the whole path over resident synthetic inputs:
 The forward/backward-split schedule of the MoE layer (W[g] quantised on its
 reduction axis only in the forward, re-quantised along N in the backward) is
 timed beside the step, with the device memory each schedule holds from
-forward to backward.
+forward to backward; so are the dense linear's two schedules, the MXFP4 QDQ
+with its saturation mask and the masked (clipped-STE) backward, and the MXFP4
+GEMMs (operand quantisation, the dense forward shape, and the ragged-M MoE
+forward shape) with E2M1 operands.
 
 Prints one JSON line.  `value` = GEMM FLOPs of the step / step time.
 """
@@ -369,6 +372,33 @@ def main():
                   "quant_gbs": round(q_gbs, 1), "quant_frac_hbm_peak": round(q_gbs / PEAK_HBM_GBS, 4)}
     del xf, wtf, qa, sa, qb, sb, Y4
 
+    # The MoE forward shape with E2M1 operands: the routed token rows and every
+    # expert's W[g]^T [F][H] in fp32, quantised to MXFP4 GEMM operands, then
+    # the ragged-M FP4 GEMM over the same expert groups.
+    xmf = Xm.float()
+    qxm, sxm = mxq.quantize_fp4(xmf)
+    del xmf
+    wmf = Wm.transpose(1, 2).reshape(G * F, H).float()
+    qwm, swm = mxq.quantize_fp4(wmf)
+    del wmf
+    qwm = qwm.view(G, F, H // 2)
+    swm = swm.view(G, F // 128, H // 32, 32, 4)
+    moe4_runs = []
+    for i in range(6):
+        tl = Timeline(torch)
+        tl("gemm_fp4_raggedM")
+        mxq.mxq_grouped_gemm(mxq.MXQ_GG_RAGGED_M, qxm, sxm, qwm, swm, mY, ge, fmt=mxq.MXQ_FMT_E2M1)
+        tl(None)
+        if i >= 2:
+            moe4_runs.append(tl)
+    torch.cuda.synchronize()
+    m4 = [v for tl in moe4_runs for v in tl.durations()["gemm_fp4_raggedM"]]
+    m4_ms = sum(m4) / len(m4)
+    m4_tf = 2.0 * routed * H * F / (m4_ms * 1e-3) / 1e12
+    mxfp4_moe_gemm = {"shape": f"{routed} routed rows, {G} experts, {H} -> {F}", "gemm_ms": round(m4_ms, 4),
+                      "gemm_tflops": round(m4_tf, 1), "frac_fp4_peak": round(m4_tf / PEAK_FP4_TFLOPS, 4)}
+    del qxm, sxm, qwm, swm
+
     # ---------------------------------------------------------------- MoE schedules: time and memory
     schedules = {}
     for sched in ("dual", "fb_split"):
@@ -428,6 +458,7 @@ def main():
         "dense_schedules": dense_sched,
         "mxfp4_clipped_ste": fake_quant,
         "mxfp4_gemm": mxfp4_gemm,
+        "mxfp4_moe_gemm": mxfp4_moe_gemm,
         "moe_schedules": schedules,
     }
     print(json.dumps(out))
