@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 4
+#define MXQ_ABI_VERSION 5
 #define MXQ_BLOCK 32          /* elements per MX block; fixed */
 #define MXQ_MAX_GROUPS 1024   /* largest G the grouped entry points accept */
 
@@ -100,6 +100,16 @@ mxq_status mxq_device_check(int device);
 /* Columns a grouped token-axis copy of T rows in G groups may need: an upper
  * bound of sum_g ceil32(m_g), rounded up to 32.  Pure host arithmetic. */
 int64_t mxq_grouped_cols_max(int64_t T, int32_t G);
+
+/* Bytes of a quantised GEMM operand of `rows` rows and reduction length K in
+ * format fmt (MXQ_FMT_E4M3 or MXQ_FMT_E2M1), Kp = ceil32(K): *code_bytes =
+ * rows * Kp (E4M3) or rows * Kp / 2 (E2M1); *scale_bytes = ceil128(rows) *
+ * Kp / 32 (the operand scale layout below).  The row copy of an R x C matrix
+ * is (R, C), its colT copy (C, R), a grouped token-axis copy (C, ldq), an
+ * MXFP4 operand (rows, L).  The shape-only counterpart of the quantisers, so
+ * a caller can allocate their outputs.  Pure host arithmetic; rows, K >= 1,
+ * outputs non-NULL, else MXQ_ERR_INVALID_ARGUMENT. */
+mxq_status mxq_operand_sizes(int64_t rows, int64_t K, int fmt, int64_t* code_bytes, int64_t* scale_bytes);
 
 /*
  * MXFP8 quantisation of a bf16 matrix x [R][ldx] (R x C used), the per-block

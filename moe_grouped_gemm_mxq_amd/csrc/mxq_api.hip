@@ -114,6 +114,16 @@ int64_t mxq_grouped_cols_max(int64_t T, int32_t G) {
   return (T + 31 * (int64_t)G + 31) / 32 * 32;
 }
 
+mxq_status mxq_operand_sizes(int64_t rows, int64_t K, int fmt, int64_t* code_bytes, int64_t* scale_bytes) {
+  MXQ_REQUIRE(code_bytes && scale_bytes, "mxq_operand_sizes: NULL output");
+  MXQ_REQUIRE(rows >= 1 && K >= 1, "mxq_operand_sizes: rows and K must be >= 1");
+  MXQ_REQUIRE(fmt == MXQ_FMT_E4M3 || fmt == MXQ_FMT_E2M1, "mxq_operand_sizes: unknown format %d", fmt);
+  const int64_t Kp = (K + 31) / 32 * 32;
+  *code_bytes = fmt == MXQ_FMT_E4M3 ? rows * Kp : rows * (Kp / 2);
+  *scale_bytes = (rows + 127) / 128 * 128 * (Kp / 32);
+  return MXQ_OK;
+}
+
 mxq_status mxq_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int axis_mask,
                         uint8_t* q_row, uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT,
                         hipStream_t st) {

@@ -43,7 +43,7 @@ BLOCK = 32
 MAX_GROUPS = 1024
 
 EXPORTED = [
-    "mxq_abi_version", "mxq_last_error", "mxq_device_check", "mxq_grouped_cols_max",
+    "mxq_abi_version", "mxq_last_error", "mxq_device_check", "mxq_grouped_cols_max", "mxq_operand_sizes",
     "mxq_quantize", "mxq_quantize_batched", "mxq_quantize_grouped", "mxq_qdq_fp4", "mxq_qdq_fp4_ex",
     "mxq_ste_backward_fp4", "mxq_fp4_scale_threshold", "mxq_quantize_fp4", "mxq_gemm", "mxq_grouped_gemm",
     "mxq_validate_group_end",
@@ -62,6 +62,7 @@ def _load(path: str = LIB_PATH):
         "mxq_last_error": ([], ctypes.c_char_p),
         "mxq_device_check": ([I], I),
         "mxq_grouped_cols_max": ([I64, I32], I64),
+        "mxq_operand_sizes": ([I64, I64, I, P, P], I),
         "mxq_quantize": ([P, I64, I64, I64, I, P, P, P, P, P], I),
         "mxq_quantize_batched": ([P, I64, I64, I64, I64, I64, I, P, P, P, P, P], I),
         "mxq_quantize_grouped": ([P, I64, I64, I64, P, I32, I64, I, P, P, P, P, P], I),
@@ -81,7 +82,7 @@ def _load(path: str = LIB_PATH):
     return lib
 
 
-ABI_VERSION = 4  # MXQ_ABI_VERSION of include/mxq.h this binding is written against
+ABI_VERSION = 5  # MXQ_ABI_VERSION of include/mxq.h this binding is written against
 
 _lib = _load()
 if _lib.mxq_abi_version() != ABI_VERSION:
@@ -154,6 +155,13 @@ def mxq_device_check(device: int = 0) -> int:
 
 def mxq_grouped_cols_max(T: int, G: int) -> int:
     return _lib.mxq_grouped_cols_max(T, G)
+
+
+def mxq_operand_sizes(rows: int, K: int, fmt: int = 0) -> tuple:
+    """(code bytes, scale bytes) of a quantised GEMM operand of `rows` rows and reduction length K."""
+    c, sc = ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.mxq_operand_sizes(rows, K, fmt, ctypes.byref(c), ctypes.byref(sc)), "mxq_operand_sizes")
+    return c.value, sc.value
 
 
 def mxq_quantize(x, axis_mask, q_row=None, s_row=None, q_colT=None, s_colT=None, stream=None):

@@ -64,6 +64,28 @@ def test_abi_version_and_pure_host_helpers(lib):
     assert f(70, 6) % 32 == 0 and f(70, 6) >= 70 + 31 * 6
 
 
+def test_operand_sizes(lib):
+    """Shape-only sizes of a quantised operand: codes rows x ceil32(K) bytes (E4M3)
+    or half that (E2M1); scales ceil128(rows) x ceil32(K)/32 bytes, the binding's
+    scale_shape; bad arguments are rejected."""
+    from moe_grouped_gemm_mxq_amd import mxq
+    fn = lib.mxq_operand_sizes
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    c, s = ctypes.c_int64(), ctypes.c_int64()
+    for rows, K in [(1, 1), (33, 2), (128, 32), (129, 33), (131072, 7168), (7168, 131328)]:
+        Kp = (K + 31) // 32 * 32
+        sshape = mxq.scale_shape(rows, Kp // 32)
+        for fmt, code in ((0, rows * Kp), (1, rows * Kp // 2)):
+            assert fn(rows, K, fmt, ctypes.byref(c), ctypes.byref(s)) == 0
+            assert c.value == code and s.value == sshape[0] * sshape[1] * sshape[2] * sshape[3]
+        assert mxq.mxq_operand_sizes(rows, K) == (rows * Kp, s.value)
+    assert fn(0, 32, 0, ctypes.byref(c), ctypes.byref(s)) == 1
+    assert fn(4, 32, 7, ctypes.byref(c), ctypes.byref(s)) == 1
+    assert fn(4, 32, 0, None, ctypes.byref(s)) == 1
+    assert "NULL" in err(lib)
+
+
 def call(lib, name, *args):
     fn = getattr(lib, name)
     fn.restype = ctypes.c_int
