@@ -98,6 +98,44 @@ class Timeline:
         return out
 
 
+def moe_tile_stats(sizes, H, F, cus, BM=256, BN=256, BK=128):
+    """Work the grouped GEMMs' tile walks do beyond the routed rows and tokens,
+    and how evenly the persistent walks spread it over the workgroups (host
+    arithmetic following the kernels' tiling: ragged-M tiles start at the
+    128-row boundary at or below their group's first row; ragged-K tiles of a
+    group reduce over its 32-padded tokens in 128-deep stages, an even number
+    of them, and are dealt round robin, largest group first)."""
+    out = {}
+    # ragged M (forward: N = F; input gradient: N = H), K = H or F
+    start, m_tiles = 0, 0
+    for m in sizes:
+        if m:
+            m_tiles += (start - (start & ~127) + m + BM - 1) // BM
+        start += m
+    routed = sum(sizes)
+    for name, n, k in (("raggedM_fwd", F, H), ("raggedM_dgrad", H, F)):
+        tiles = m_tiles * ((n + BN - 1) // BN)
+        rounds = -(-tiles // cus)
+        out[name] = {"tiles": tiles, "rows_computed": m_tiles * BM, "rows_routed": routed,
+                     "row_waste_frac": round(1 - routed / (m_tiles * BM), 4),
+                     "max_over_mean_tiles_per_workgroup": round(rounds / (tiles / cus), 4)}
+    # ragged K (weight gradient: M = H, N = F), empty groups' tiles store zeros
+    per_g = ((H + BM - 1) // BM) * ((F + BN - 1) // BN)
+    nst = [(-(-((m + 31) // 32 * 32) // BK) + 1) // 2 * 2 for m in sizes]
+    order = sorted(range(len(sizes)), key=lambda g: (-sizes[g], g))
+    work = [0] * cus
+    tile = 0
+    for g in order:
+        for _ in range(per_g):
+            work[tile % cus] += nst[g] + 1  # its stages plus one for the output tile
+            tile += 1
+    k_computed = sum(nst[g] * BK for g in range(len(sizes)))
+    out["raggedK_wgrad"] = {"tiles": tile, "tokens_routed": routed, "tokens_computed": k_computed,
+                            "token_waste_frac": round(1 - routed / k_computed, 4),
+                            "max_over_mean_stages_per_workgroup": round(max(work) / (sum(work) / cus), 4)}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -460,6 +498,7 @@ def main():
         "mxfp4_gemm": mxfp4_gemm,
         "mxfp4_moe_gemm": mxfp4_moe_gemm,
         "moe_schedules": schedules,
+        "moe_tiles": moe_tile_stats(sizes, H, F, torch.cuda.get_device_properties(0).multi_processor_count),
     }
     print(json.dumps(out))
 
