@@ -30,11 +30,11 @@ hipError_t launch_quant_tile(const uint16_t* x, int64_t R, int64_t C, int64_t ld
 // MXFP4 quant-dequant.  (F, T) encode the scale factor's exponent threshold;
 // fp4_scale_params computes them and rejects factors outside [2^-64, 2^64).
 bool fp4_scale_params(float scale_factor, int* F, uint32_t* T);
-// y may be null (quantise only); interleave: scales in the GEMM operand layout
-// (scale_offset) instead of row-major.
+// y may be null (quantise only); operand_layout: scales in the GEMM operand
+// layout (scale_offset) instead of row-major.
 hipError_t launch_qdq_fp4(const float* x, float* y, int64_t rows, int64_t L, int F, uint32_t T,
                           uint8_t* codes, uint8_t* scales, uint8_t* sat_mask, hipStream_t st,
-                          bool interleave = false);
+                          bool operand_layout = false);
 hipError_t launch_ste_backward_fp4(const float* grad_y, const uint8_t* sat_mask, float* grad_x,
                                    int64_t rows, int64_t L, hipStream_t st);
 

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kThreads) void qdq_rows_kernel(const float* __restr
                                                            int64_t L, Fp4Scale p,
                                                            uint8_t* __restrict__ codes,
                                                            uint8_t* __restrict__ scales,
-                                                           uint32_t* __restrict__ sat_mask, bool interleave) {
+                                                           uint32_t* __restrict__ sat_mask, bool operand_layout) {
   const int64_t nbr = (L + 31) / 32;  // blocks per row
   const int64_t n_chunks = rows * nbr * 8;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_chunks;
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void qdq_rows_kernel(const float* __restr
     }
     if (codes) *reinterpret_cast<uint16_t*>(codes + row * (nbr * 16) + col / 2) = (uint16_t)r.nibbles;
     if (scales && (i & 7) == 0)
-      scales[interleave ? scale_offset(row, blk - row * nbr, nbr) : blk] = (uint8_t)(e + 127);
+      scales[operand_layout ? scale_offset(row, blk - row * nbr, nbr) : blk] = (uint8_t)(e + 127);
     if (sat_mask) {
       // padding elements are 0 and never saturate, so their bits stay clear
       const uint32_t word = oct_or(r.sat << (4 * (i & 7)));
@@ -194,16 +194,16 @@ bool fp4_scale_params(float scale_factor, int* F, uint32_t* T) {
 }
 
 hipError_t launch_qdq_fp4(const float* x, float* y, int64_t rows, int64_t L, int F, uint32_t T,
-                          uint8_t* codes, uint8_t* scales, uint8_t* sat_mask, hipStream_t st, bool interleave) {
+                          uint8_t* codes, uint8_t* scales, uint8_t* sat_mask, hipStream_t st, bool operand_layout) {
   const Fp4Scale p{F, T};
   const bool flat = L % 32 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)y % 16 == 0;
   const int64_t n_chunks = flat ? rows * L / 4 : rows * ((L + 31) / 32) * 8;
   uint32_t* mask = reinterpret_cast<uint32_t*>(sat_mask);
   if (flat)
     qdq_flat_kernel<<<grid_for(n_chunks), kThreads, 0, st>>>(x, y, n_chunks, p, codes, scales, mask,
-                                                             interleave ? L / 32 : 0);
+                                                             operand_layout ? L / 32 : 0);
   else
-    qdq_rows_kernel<<<grid_for(n_chunks), kThreads, 0, st>>>(x, y, rows, L, p, codes, scales, mask, interleave);
+    qdq_rows_kernel<<<grid_for(n_chunks), kThreads, 0, st>>>(x, y, rows, L, p, codes, scales, mask, operand_layout);
   return hipGetLastError();
 }
 

@@ -187,7 +187,7 @@ def test_moe_wgrad_ragged_k_full_sampled(moe_full):
 
 def test_moe_gemms_write_every_output_deterministically(moe_full):
     """Every output tile is written exactly as before when the outputs start as
-    NaN: the persistent tile walks (ragged M, interleaved ragged K) miss no tile
+    NaN: the persistent tile walks (ragged M, ragged K largest group first) miss no tile
     and give the same bits on a second run."""
     m = mxq()
     G, K, N = moe_full["W"].shape
