@@ -242,8 +242,10 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* codes, int r0, int s, in
   return f;
 }
 
-// B rows wn*64 .. wn*64+63 are 32-row blocks 2*(wn%2) and 2*(wn%2)+1 of half
-// wn/2: their two scale dwords sit 8*(wn%2) bytes into the lane's 16.
+// A lane's scale registers for step s: A's dword of its row r = lane % 32 in
+// the wave's half wm, whose byte i scales row block i; B's dword of half wn/2,
+// whose bytes 2*(wn%2) and 2*(wn%2)+1 scale the wave's two column blocks
+// (B rows wn*64 .. wn*64+63), shifted down to bytes 0 and 1 for op_sel.
 template <int KIND>
 __device__ __forceinline__ void read_frags(const uint8_t* st, int s, int wm, int wn, int lane, Frags& f) {
   using F = Fmt<KIND>;
