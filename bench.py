@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle leg")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (reference for HBM counter scaling)")
+    ap.add_argument("--quant-traffic", action="store_true",
+                    help="only run each quantiser launch of the step once, in a fixed order, and print their "
+                         "algorithmic bytes (for per-launch HBM counters)")
     return ap.parse_args()
 
 
@@ -256,6 +259,30 @@ def main():
         "moe_quant_x_grouped": T * H * 2 + padded * H * (1 + 1 / 32),
     }
     step_flops = sum(flops.values())
+
+    if args.quant_traffic:
+        # every quantiser launch of the step once; the printed order is the
+        # dispatch order of the quantiser kernels
+        launches = []
+        mxq.mxq_qdq_fp4(x4, y4)
+        launches.append(["qdq_fp4 8192x8192", "qdq_flat_kernel", bytes_["qdq_fp4"]])
+        for name, t, q, r, c in (("X", X, qx, M, K), ("W", W, qw, K, N), ("dY", dY, qy, M, N)):
+            mxq.mxq_quantize(t, R | C, q["q_row"], q["s_row"], q["q_colT"], q["s_colT"])
+            launches.append([f"dense_quant_dual {name} {r}x{c}", "quant_tile_kernel<true, false, true>", qb(r, c, 2)])
+        mxq.mxq_quantize(Xm, R, mx["q_row"], mx["s_row"])
+        launches.append([f"moe_quant_x_row {T}x{H}", "quant_row_kernel<true>", bytes_["moe_quant_x_row"]])
+        quant_w_experts(R | C)
+        launches.append([f"moe_quant_w_dual {G}x{H}x{F}", "quant_tile_kernel<true, false, true>",
+                         bytes_["moe_quant_w_dual"]])
+        mxq.mxq_quantize_grouped(dYm, ge, ldq, R | C, mdy["q_row"], mdy["s_row"], mdy["q_colT"], mdy["s_colT"])
+        launches.append([f"moe_quant_dy_row_grouped {T}x{F}", "quant_tile_kernel<true, true, true>",
+                         bytes_["moe_quant_dy_row_grouped"]])
+        mxq.mxq_quantize_grouped(Xm, ge, ldq, C, None, None, mxt["q_colT"], mxt["s_colT"])
+        launches.append([f"moe_quant_x_grouped {T}x{H}", "quant_tile_kernel<false, true, true>",
+                         bytes_["moe_quant_x_grouped"]])
+        torch.cuda.synchronize()
+        print(json.dumps({"quant_traffic_launches": launches}))
+        return
 
     # ---------------------------------------------------------------- warmup + timed steps
     for _ in range(args.warmup):
