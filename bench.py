@@ -372,6 +372,35 @@ def main():
                 if sched == "dual" else 0)
         dense_sched[sched] = {"fwd_ms": f_ms, "bwd_ms": b_ms, "quantised_held_fwd_to_bwd_bytes": held}
         grads[sched] = (dX.clone(), dW.clone())
+    # measured device memory of each schedule (untimed; as for the MoE layer
+    # below): every quantised copy allocated when produced, freed after its
+    # last use
+    def dense_memory(sched):
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        both = R | C if sched == "dual" else None
+        xq = mxq.quantize(X, both or R)
+        wq = mxq.quantize(W, both or C)
+        mxq.mxq_gemm(xq["q_row"], xq["s_row"], wq["q_colT"], wq["s_colT"], Y)
+        for k in ("q_row", "s_row"):
+            del xq[k]
+        for k in ("q_colT", "s_colT"):
+            del wq[k]
+        torch.cuda.synchronize()
+        held = torch.cuda.memory_allocated() - base
+        if sched == "fb_split":
+            xq.update(mxq.quantize(X, C))
+            wq.update(mxq.quantize(W, R))
+        yq = mxq.quantize(dY, R | C)
+        mxq.mxq_gemm(yq["q_row"], yq["s_row"], wq["q_row"], wq["s_row"], dX)
+        mxq.mxq_gemm(xq["q_colT"], xq["s_colT"], yq["q_colT"], yq["s_colT"], dW)
+        del xq, wq, yq
+        torch.cuda.synchronize()
+        return {"held_fwd_to_bwd_bytes": held, "fwd_bwd_peak_bytes": torch.cuda.max_memory_allocated() - base}
+
+    for sched in ("dual", "fb_split"):
+        dense_sched[sched]["measured_memory"] = dense_memory(sched)
     dense_sched["bitwise_equal_grads"] = bool(torch.equal(grads["dual"][0], grads["fb_split"][0]) and
                                               torch.equal(grads["dual"][1], grads["fb_split"][1]))
     del grads
@@ -491,6 +520,39 @@ def main():
         schedules[sched] = {"fwd_ms": round(sum(d["fwd"]) / len(d["fwd"]), 3),
                             "bwd_ms": round(sum(d["bwd"]) / len(d["bwd"]), 3),
                             "quantised_w_held_fwd_to_bwd_bytes": held}
+    # Measured device memory of each schedule (untimed): one MoE forward and
+    # backward in which every quantised copy is allocated when it is produced
+    # and freed after its last use, as a training step would.  `held` = bytes
+    # still allocated when the forward ends (the saved W row copy of the dual
+    # schedule), `peak` = the peak over forward and backward, both relative to
+    # the allocations before the forward (caching-allocator counters).
+    def moe_memory(sched):
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        xq = mxq.quantize(Xm, R)
+        wq = mxq.quantize_batched(Wm, R | C if sched == "dual" else C)
+        mxq.mxq_grouped_gemm(mxq.MXQ_GG_RAGGED_M, xq["q_row"], xq["s_row"], wq["q_colT"], wq["s_colT"], mY, ge)
+        del xq, wq["q_colT"], wq["s_colT"]
+        torch.cuda.synchronize()
+        held = torch.cuda.memory_allocated() - base
+        fwd_peak = torch.cuda.max_memory_allocated() - base
+        dyq = mxq.quantize_grouped(dYm, ge, R | C, ldq)
+        xt = mxq.quantize_grouped(Xm, ge, C, ldq)
+        if sched == "fb_split":
+            wq.update(mxq.quantize_batched(Wm, R))
+        mxq.mxq_grouped_gemm(mxq.MXQ_GG_RAGGED_M, dyq["q_row"], dyq["s_row"], wq["q_row"], wq["s_row"], mdX, ge)
+        mxq.mxq_grouped_gemm(mxq.MXQ_GG_RAGGED_K, xt["q_colT"], xt["s_colT"], dyq["q_colT"], dyq["s_colT"], mdW, ge)
+        del dyq, xt, wq
+        torch.cuda.synchronize()
+        return {"held_fwd_to_bwd_bytes": held, "fwd_peak_bytes": fwd_peak,
+                "fwd_bwd_peak_bytes": torch.cuda.max_memory_allocated() - base}
+
+    for sched in ("dual", "fb_split"):
+        schedules[sched]["measured_memory"] = moe_memory(sched)
+    schedules["measured_held_difference_bytes"] = (schedules["dual"]["measured_memory"]["held_fwd_to_bwd_bytes"] -
+                                                   schedules["fb_split"]["measured_memory"]["held_fwd_to_bwd_bytes"])
+
     # the two schedules must produce the same input gradient bit for bit
     ref = mdX.clone()
     moe_fwd(Timeline(torch), "dual")
