@@ -563,7 +563,7 @@ def main():
     # ---------------------------------------------------------------- CPU baseline (oracle)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args.cpu_seconds, X, W, dY, Xm, Wm, dYm, ge, sizes)
+        cpu = cpu_baseline(args.cpu_seconds, X, W, dY, Xm, Wm, dYm, ge, sizes, x4)
 
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     out = {
@@ -592,7 +592,7 @@ def main():
     print(json.dumps(out))
 
 
-def cpu_baseline(target_s, X, W, dY, Xm, Wm, dYm, ge, sizes):
+def cpu_baseline(target_s, X, W, dY, Xm, Wm, dYm, ge, sizes, x4):
     """The oracle (plain C, fp64) on a bounded sample of the same workload: for
     each of the six GEMMs, quantise the operand rows/columns a block of sampled
     outputs needs and compute those outputs; TFLOP/s = sampled GEMM FLOPs /
@@ -639,17 +639,51 @@ def cpu_baseline(target_s, X, W, dY, Xm, Wm, dYm, ge, sizes):
             fl += 2.0 * A.shape[0] * B.shape[0] * A.shape[1]
         return time.perf_counter() - t0, fl
 
-    # grow the sample (cost ~ s^2) until one run takes about target_s of CPU time
-    s = 64
-    t, fl = run(s)
-    while t < 0.5 * target_s and s < 4096:
-        s = int(min(4096, s * max(1.4, min(4.0, (target_s / max(t, 1e-3)) ** 0.5))))
+    def grow(target):
+        # grow the sample (cost ~ s^2) until one run takes about `target` seconds
+        s = 64
         t, fl = run(s)
-    return {"value": round(fl / t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.lib().oracle_num_threads(),
+        while t < 0.5 * target and s < 4096:
+            s = int(min(4096, s * max(1.4, min(4.0, (target / max(t, 1e-3)) ** 0.5))))
+            t, fl = run(s)
+        return s, t, fl
+
+    def qdq_rate(target):
+        # the MXFP4 QDQ oracle over leading rows of the 8192 x 8192 input,
+        # doubling them until a run takes about `target` seconds; GB/s over
+        # the same 8 bytes per element as the kernel (fp32 in, fp32 out)
+        n = 64
+        while True:
+            xs = x4[:n].cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.mxfp4_qdq(xs)
+            t = time.perf_counter() - t0
+            if t >= 0.5 * target or n >= x4.shape[0]:
+                return n, t, 8.0 * xs.size / t / 1e9
+            n = min(x4.shape[0], n * 2)
+
+    lib = oracle.lib()
+    cores = lib.oracle_num_threads()
+    s, t, fl = grow(target_s)
+    qn, qt, qgbs = qdq_rate(0.15 * target_s)
+    lib.oracle_set_num_threads(1)
+    try:
+        s1, t1, fl1 = grow(0.3 * target_s)
+        qn1, qt1, qgbs1 = qdq_rate(0.1 * target_s)
+    finally:
+        lib.oracle_set_num_threads(cores)
+    return {"value": round(fl / t / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{s}x{s} outputs of each of the six GEMMs (dense fwd/dgrad/wgrad; MoE fwd/dgrad/wgrad of "
                       f"the largest expert), with the oracle quantising the operand rows they need; "
-                      f"{fl / 1e9:.1f} GFLOP in {t:.1f} s"}
+                      f"{fl / 1e9:.1f} GFLOP in {t:.1f} s",
+            "single_thread": {"value": round(fl1 / t1 / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+                              "sample": f"{s1}x{s1} outputs of each of the six GEMMs; {fl1 / 1e9:.1f} GFLOP in "
+                                        f"{t1:.1f} s"},
+            "mxfp4_qdq": {"value": round(qgbs, 3), "unit": "GB/s", "cores": cores,
+                          "sample": f"first {qn} rows of the 8192x8192 input, 8 bytes per element, {qt:.2f} s",
+                          "single_thread": {"value": round(qgbs1, 3), "unit": "GB/s", "cores": 1,
+                                            "sample": f"first {qn1} rows, {qt1:.2f} s"}}}
 
 
 if __name__ == "__main__":

@@ -38,6 +38,7 @@ def _declare(lib):
     I32 = ctypes.c_int32
     sig = {
         "oracle_num_threads": ([], ctypes.c_int),
+        "oracle_set_num_threads": ([ctypes.c_int], None),
         "oracle_e4m3_decode": ([ctypes.c_uint8], ctypes.c_double),
         "oracle_e4m3_encode": ([ctypes.c_double], ctypes.c_uint8),
         "oracle_e4m3_encode_n": ([P, I64, P], None),

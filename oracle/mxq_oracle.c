@@ -60,6 +60,17 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Threads of the parallel loops that follow (n >= 1); only the timing of the
+ * oracle uses it, never its results, which do not depend on the split. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* NaN and Inf (exponent field all ones) are outside the method's contract */
 static int bf16_all_finite(const uint16_t* x, int64_t R, int64_t C, int64_t ldx)
 {
