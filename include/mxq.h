@@ -246,7 +246,8 @@ mxq_status mxq_quantize_fp4(const float* x, int64_t rows, int64_t L, float scale
  * numeric model, taken as a GEMM on the codes): A codes [M][K/2], B codes
  * [N][K/2] as written by mxq_quantize_fp4 (rows of K elements), scales in
  * the same operand layout.
- * M, N >= 1; K >= 32, K % 32 == 0; ldc >= N.  Unknown fmt:
+ * M, N >= 1; K >= 32, K % 32 == 0; ldc >= N.  A, B 16-byte aligned, sA, sB
+ * and C 4-byte aligned (else MXQ_ERR_INVALID_ARGUMENT).  Unknown fmt:
  * MXQ_ERR_UNSUPPORTED.
  */
 mxq_status mxq_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
@@ -271,7 +272,8 @@ mxq_status mxq_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const
  * expert g's B codes at byte g * N * K/2), MXQ_GG_RAGGED_M only (there is no
  * E2M1 token-axis quantiser): MXQ_GG_RAGGED_K with E2M1 gives
  * MXQ_ERR_UNSUPPORTED.
- * M, N >= 1; 1 <= G <= MXQ_MAX_GROUPS.
+ * M, N >= 1; K >= 32, K % 32 == 0; 1 <= G <= MXQ_MAX_GROUPS.  A, B 16-byte
+ * aligned, sA, sB and C 4-byte aligned (else MXQ_ERR_INVALID_ARGUMENT).
  */
 mxq_status mxq_grouped_gemm(mxq_gg_mode mode, const uint8_t* A, const uint8_t* sA,
                             const uint8_t* B, const uint8_t* sB, float* C,

@@ -276,6 +276,8 @@ mxq_status mxq_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const
   MXQ_REQUIRE(K >= 32 && K % 32 == 0, "mxq_gemm: K must be a positive multiple of 32 (got %lld)", (long long)K);
   MXQ_REQUIRE(ldc >= N, "mxq_gemm: ldc < N");
   MXQ_REQUIRE(aligned16(A) && aligned16(B) && ((uintptr_t)C & 3u) == 0, "mxq_gemm: A, B must be 16-byte aligned");
+  MXQ_REQUIRE((((uintptr_t)sA | (uintptr_t)sB) & 3u) == 0,
+              "mxq_gemm: sA, sB must be 4-byte aligned (the kernel reads scale dwords)");
   if (fmt != MXQ_FMT_E4M3 && fmt != MXQ_FMT_E2M1)
     return fail(MXQ_ERR_UNSUPPORTED, "mxq_gemm: unknown operand format %d", (int)fmt);
   MXQ_REQUIRE_DEVICE();
@@ -292,6 +294,8 @@ mxq_status mxq_grouped_gemm(mxq_gg_mode mode, const uint8_t* A, const uint8_t* s
   MXQ_REQUIRE(K >= 32 && K % 32 == 0, "mxq_grouped_gemm: K must be a positive multiple of 32");
   MXQ_REQUIRE(G >= 1 && G <= MXQ_MAX_GROUPS, "mxq_grouped_gemm: G must be in [1, %d]", MXQ_MAX_GROUPS);
   MXQ_REQUIRE(aligned16(A) && aligned16(B) && ((uintptr_t)C & 3u) == 0, "mxq_grouped_gemm: A, B must be 16-byte aligned");
+  MXQ_REQUIRE((((uintptr_t)sA | (uintptr_t)sB) & 3u) == 0,
+              "mxq_grouped_gemm: sA, sB must be 4-byte aligned (the kernel reads scale dwords)");
   if (fmt != MXQ_FMT_E4M3 && fmt != MXQ_FMT_E2M1)
     return fail(MXQ_ERR_UNSUPPORTED, "mxq_grouped_gemm: unknown operand format %d", (int)fmt);
   if (fmt == MXQ_FMT_E2M1 && mode == MXQ_GG_RAGGED_K)

@@ -125,6 +125,12 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     assert "multiple of 32" in err(lib)
     assert call(lib, "mxq_gemm", FAKE, FAKE, FAKE, FAKE, FAKE, I64(4), I64(8), I64(64), I64(4), 0, P(0)) == 1
     assert call(lib, "mxq_gemm", FAKE, FAKE, FAKE, FAKE, FAKE, I64(4), I64(4), I64(64), I64(4), 7, P(0)) == 2
+    # GEMM scale arrays are read as dwords
+    assert call(lib, "mxq_gemm", FAKE, P(0x1002), FAKE, FAKE, FAKE, I64(4), I64(4), I64(64), I64(4), 0, P(0)) == 1
+    assert "sA, sB" in err(lib)
+    assert call(lib, "mxq_grouped_gemm", 0, FAKE, FAKE, FAKE, P(0x1001), FAKE, I64(4), I64(4), I64(64), FAKE,
+                ctypes.c_int32(2), 0, P(0)) == 1
+    assert "sA, sB" in err(lib)
     # grouped: G out of range, bad mode, ldq not a multiple of 32
     assert call(lib, "mxq_grouped_gemm", 0, FAKE, FAKE, FAKE, FAKE, FAKE, I64(4), I64(4), I64(64), FAKE,
                 ctypes.c_int32(0), 0, P(0)) == 1
