@@ -560,6 +560,39 @@ def main():
     torch.cuda.synchronize()
     schedules["bitwise_equal_dgrad"] = bool(torch.equal(ref, mdX))
 
+    # ---------------------------------------------------------------- small linear forward
+    # X [256x512] and W [512x256] (N(0,1), seed 0): quantise X by rows and W
+    # by columns, then the GEMM into a [256x256] fp32 output.  Latency-bound
+    # (67.1 MFLOP); 100 timed repetitions after 10, median of each part.
+    Xs, Ws = workloads.linear_small(device=dev)
+    qxs = mxq.quantize(Xs, R)
+    qws = mxq.quantize(Ws, C)
+    Ys = f32(Xs.shape[0], Ws.shape[1])
+    small = {"quant_x_row": [], "quant_w_colT": [], "gemm": [], "total": []}
+    for i in range(110):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record()
+        mxq.mxq_quantize(Xs, R, qxs["q_row"], qxs["s_row"])
+        ev[1].record()
+        mxq.mxq_quantize(Ws, C, None, None, qws["q_colT"], qws["s_colT"])
+        ev[2].record()
+        mxq.mxq_gemm(qxs["q_row"], qxs["s_row"], qws["q_colT"], qws["s_colT"], Ys)
+        ev[3].record()
+        if i >= 10:
+            small["_ev"] = small.get("_ev", []) + [ev]
+    torch.cuda.synchronize()
+    for ev in small.pop("_ev"):
+        small["quant_x_row"].append(ev[0].elapsed_time(ev[1]))
+        small["quant_w_colT"].append(ev[1].elapsed_time(ev[2]))
+        small["gemm"].append(ev[2].elapsed_time(ev[3]))
+        small["total"].append(ev[0].elapsed_time(ev[3]))
+    med = lambda v: sorted(v)[len(v) // 2]
+    linear_small = {"shape": "X 256x512 . W 512x256 -> 256x256 fp32", "reps": len(small["total"])}
+    for k, v in small.items():
+        linear_small[f"{k}_us_median"] = round(1e3 * med(v), 2)
+    linear_small["gemm_tflops_median"] = round(2.0 * 256 * 256 * 512 / (med(small["gemm"]) * 1e-3) / 1e12, 2)
+    del Xs, Ws, qxs, qws, Ys
+
     # ---------------------------------------------------------------- CPU baseline (oracle)
     cpu = None
     if not args.no_cpu_baseline:
@@ -588,6 +621,7 @@ def main():
         "mxfp4_moe_gemm": mxfp4_moe_gemm,
         "moe_schedules": schedules,
         "moe_tiles": moe_tile_stats(sizes, H, F, torch.cuda.get_device_properties(0).multi_processor_count),
+        "linear_small": linear_small,
     }
     print(json.dumps(out))
 
