@@ -334,7 +334,10 @@ struct Tile {
 // fp32 stores of one tile's accumulators (32 consecutive floats per half
 // wave); rows / columns past the tile's valid range are skipped.  The row
 // pointer advances one row at a time (a 64-bit add), so the stores need no
-// per-element address arithmetic and few registers.
+// per-element address arithmetic and few registers.  The stores are
+// non-temporal: the output is never read back by the GEMM, and streaming it
+// past the caches keeps the operand panels resident in the memory-side cache
+// (and leaves no dirty output lines for the next kernel to write back).
 __device__ __forceinline__ void store_tile(const v16f (&acc)[TM][TN], const Tile& tl, int64_t ldo, int wm,
                                            int wn, int lane) {
   const int col0 = wn * WN + (lane & 31);
@@ -349,8 +352,8 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[TM][TN], const Tile
       for (int r = 0; r < 4; r++) {
         const int row = row0 + i * 32 + 8 * q + r;
         if (row >= tl.row_lo && row < tl.rows_a) {
-          if (c_ok0) p[0] = acc[i][0][q * 4 + r];
-          if (c_ok1) p[32] = acc[i][1][q * 4 + r];
+          if (c_ok0) __builtin_nontemporal_store(acc[i][0][q * 4 + r], p);
+          if (c_ok1) __builtin_nontemporal_store(acc[i][1][q * 4 + r], p + 32);
         }
         // next row of this lane: +1 within a run of 4, else +5 (27 -> 32 too)
         p += (r < 3 ? 1 : 5) * ldo;
