@@ -225,12 +225,15 @@ def main():
     def step(tl):
         tl("qdq_fp4")
         mxq.mxq_qdq_fp4(x4, y4)
-        tl("dense_quant_dual")
+        # forward operands, forward GEMM, then the gradient's operands and the
+        # backward GEMMs, in the order of a training step
+        tl("dense_quant_dual_x_w")
         mxq.mxq_quantize(X, R | C, qx["q_row"], qx["s_row"], qx["q_colT"], qx["s_colT"])
         mxq.mxq_quantize(W, R | C, qw["q_row"], qw["s_row"], qw["q_colT"], qw["s_colT"])
-        mxq.mxq_quantize(dY, R | C, qy["q_row"], qy["s_row"], qy["q_colT"], qy["s_colT"])
         tl("dense_gemm_fwd")
         mxq.mxq_gemm(qx["q_row"], qx["s_row"], qw["q_colT"], qw["s_colT"], Y)
+        tl("dense_quant_dual_dy")
+        mxq.mxq_quantize(dY, R | C, qy["q_row"], qy["s_row"], qy["q_colT"], qy["s_colT"])
         tl("dense_gemm_dgrad")
         mxq.mxq_gemm(qy["q_row"], qy["s_row"], qw["q_row"], qw["s_row"], dX)
         tl("dense_gemm_wgrad")
@@ -250,7 +253,7 @@ def main():
     padded = sum(c32(s) for s in sizes)
     bytes_ = {
         "qdq_fp4": 8.0 * x4.numel(),
-        "dense_quant_dual": qb(M, K, 2) + qb(K, N, 2) + qb(M, N, 2),
+        "dense_quant_dual_x_w": qb(M, K, 2) + qb(K, N, 2), "dense_quant_dual_dy": qb(M, N, 2),
         "moe_quant_x_row": qb(T, H, 1),
         "moe_quant_w_dual": qb(G * H, F, 2),
         "moe_quant_w_colT": qb(G * H, F, 1),
