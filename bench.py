@@ -2,15 +2,17 @@
 
 One step = one pass of the whole path over resident synthetic inputs:
   * MXFP4 quant-dequant of an 8192x8192 fp32 tensor (1% of rows scaled by 2^U(-20,20));
-  * MXFP8 dense linear M=8192, K=7168, N=18432: dual-axis quantisation of X, W
-    and dY, then the forward, input-gradient and weight-gradient GEMMs;
+  * MXFP8 dense linear M=8192, K=7168, N=18432: dual-axis quantisation of X and
+    W, the forward GEMM, dual-axis quantisation of dY, then the input-gradient
+    and weight-gradient GEMMs;
   * MoE expert layer, one GPU's 32 experts, 7168 -> 4096, 16384 tokens routed
-    top-8 over Zipf(1.1) weights (131072 rows): forward (X by rows, W[g] on both
-    axes, ragged-M GEMM) and backward (dY by rows and grouped by tokens, X
-    grouped by tokens, ragged-M input gradient, ragged-K weight gradient),
-    dual-axis schedule.
-The forward/backward-split schedule of the MoE layer (W[g] quantised on its
-reduction axis only in the forward, re-quantised along N in the backward) is
+    top-8 over Zipf(1.1) weights (131072 rows), dual-axis schedule: forward (X
+    by rows and by tokens within each expert group from one read, W[g] on both
+    axes, ragged-M GEMM) and backward (dY by rows and grouped by tokens,
+    ragged-M input gradient, ragged-K weight gradient).
+The forward/backward-split schedule of the MoE layer (X by rows and W[g] on
+its reduction axis only in the forward; X grouped by tokens and W[g] along N
+re-quantised in the backward) is
 timed beside the step, with the device memory each schedule holds from
 forward to backward; so are the dense linear's two schedules, the MXFP4 QDQ
 with its saturation mask and the masked (clipped-STE) backward, and the MXFP4
@@ -200,9 +202,18 @@ def main():
                                  mw["s_row"].view(G, H // 128, F // 32, 32, 4) if mask & R else None,
                                  mw["q_colT"] if mask & C else None, mw["s_colT"] if mask & C else None)
 
+    # The dual-axis schedule quantises, in the forward, every operand copy the
+    # backward needs from forward inputs, from one read of each: W[g] along K
+    # and along N, X by rows and by tokens within each expert group (as the
+    # dense dual schedule keeps X's column copy).  fb-split quantises only what
+    # the forward uses and re-quantises X and W[g] in the backward.
     def moe_fwd(tl, schedule):
-        tl("moe_quant_x_row")
-        mxq.mxq_quantize(Xm, R, mx["q_row"], mx["s_row"])
+        if schedule == "dual":
+            tl("moe_quant_x_row_grouped")
+            mxq.mxq_quantize_grouped(Xm, ge, ldq, R | C, mx["q_row"], mx["s_row"], mxt["q_colT"], mxt["s_colT"])
+        else:
+            tl("moe_quant_x_row")
+            mxq.mxq_quantize(Xm, R, mx["q_row"], mx["s_row"])
         tl("moe_quant_w_dual" if schedule == "dual" else "moe_quant_w_colT")
         quant_w_experts(R | C if schedule == "dual" else C)
         tl("moe_gemm_fwd_raggedM")
@@ -211,9 +222,9 @@ def main():
     def moe_bwd(tl, schedule):
         tl("moe_quant_dy_row_grouped")
         mxq.mxq_quantize_grouped(dYm, ge, ldq, R | C, mdy["q_row"], mdy["s_row"], mdy["q_colT"], mdy["s_colT"])
-        tl("moe_quant_x_grouped")
-        mxq.mxq_quantize_grouped(Xm, ge, ldq, C, None, None, mxt["q_colT"], mxt["s_colT"])
         if schedule == "fb_split":
+            tl("moe_quant_x_grouped")
+            mxq.mxq_quantize_grouped(Xm, ge, ldq, C, None, None, mxt["q_colT"], mxt["s_colT"])
             tl("moe_requant_w_row")
             quant_w_experts(R)
         tl("moe_gemm_dgrad_raggedM")
@@ -255,6 +266,7 @@ def main():
         "qdq_fp4": 8.0 * x4.numel(),
         "dense_quant_dual_x_w": qb(M, K, 2) + qb(K, N, 2), "dense_quant_dual_dy": qb(M, N, 2),
         "moe_quant_x_row": qb(T, H, 1),
+        "moe_quant_x_row_grouped": T * H * 2 + T * H * (1 + 1 / 32) + padded * H * (1 + 1 / 32),
         "moe_quant_w_dual": qb(G * H, F, 2),
         "moe_quant_w_colT": qb(G * H, F, 1),
         "moe_requant_w_row": qb(G * H, F, 1),
@@ -272,17 +284,15 @@ def main():
         for name, t, q, r, c in (("X", X, qx, M, K), ("W", W, qw, K, N), ("dY", dY, qy, M, N)):
             mxq.mxq_quantize(t, R | C, q["q_row"], q["s_row"], q["q_colT"], q["s_colT"])
             launches.append([f"dense_quant_dual {name} {r}x{c}", "quant_tile_kernel<true, false, true>", qb(r, c, 2)])
-        mxq.mxq_quantize(Xm, R, mx["q_row"], mx["s_row"])
-        launches.append([f"moe_quant_x_row {T}x{H}", "quant_row_kernel<true>", bytes_["moe_quant_x_row"]])
+        mxq.mxq_quantize_grouped(Xm, ge, ldq, R | C, mx["q_row"], mx["s_row"], mxt["q_colT"], mxt["s_colT"])
+        launches.append([f"moe_quant_x_row_grouped {T}x{H}", "quant_tile_kernel<true, true, true>",
+                         bytes_["moe_quant_x_row_grouped"]])
         quant_w_experts(R | C)
         launches.append([f"moe_quant_w_dual {G}x{H}x{F}", "quant_tile_kernel<true, false, true>",
                          bytes_["moe_quant_w_dual"]])
         mxq.mxq_quantize_grouped(dYm, ge, ldq, R | C, mdy["q_row"], mdy["s_row"], mdy["q_colT"], mdy["s_colT"])
         launches.append([f"moe_quant_dy_row_grouped {T}x{F}", "quant_tile_kernel<true, true, true>",
                          bytes_["moe_quant_dy_row_grouped"]])
-        mxq.mxq_quantize_grouped(Xm, ge, ldq, C, None, None, mxt["q_colT"], mxt["s_colT"])
-        launches.append([f"moe_quant_x_grouped {T}x{H}", "quant_tile_kernel<false, true, true>",
-                         bytes_["moe_quant_x_grouped"]])
         torch.cuda.synchronize()
         print(json.dumps({"quant_traffic_launches": launches}))
         return
@@ -519,10 +529,12 @@ def main():
         for tl in fb:
             for k, v in tl.durations().items():
                 d.setdefault(k, []).extend(v)
-        held = (mw["q_row"].numel() + mw["s_row"].numel()) if sched == "dual" else 0
+        held_w = (mw["q_row"].numel() + mw["s_row"].numel()) if sched == "dual" else 0
+        held_x = (mxt["q_colT"].numel() + mxt["s_colT"].numel()) if sched == "dual" else 0
         schedules[sched] = {"fwd_ms": round(sum(d["fwd"]) / len(d["fwd"]), 3),
                             "bwd_ms": round(sum(d["bwd"]) / len(d["bwd"]), 3),
-                            "quantised_w_held_fwd_to_bwd_bytes": held}
+                            "quantised_w_held_fwd_to_bwd_bytes": held_w,
+                            "quantised_x_held_fwd_to_bwd_bytes": held_x}
     # Measured device memory of each schedule (untimed): one MoE forward and
     # backward in which every quantised copy is allocated when it is produced
     # and freed after its last use, as a training step would.  `held` = bytes
@@ -533,20 +545,22 @@ def main():
         torch.cuda.synchronize()
         base = torch.cuda.memory_allocated()
         torch.cuda.reset_peak_memory_stats()
-        xq = mxq.quantize(Xm, R)
+        xq = mxq.quantize_grouped(Xm, ge, R | C, ldq) if sched == "dual" else mxq.quantize(Xm, R)
         wq = mxq.quantize_batched(Wm, R | C if sched == "dual" else C)
         mxq.mxq_grouped_gemm(mxq.MXQ_GG_RAGGED_M, xq["q_row"], xq["s_row"], wq["q_colT"], wq["s_colT"], mY, ge)
-        del xq, wq["q_colT"], wq["s_colT"]
+        for k in ("q_row", "s_row"):
+            del xq[k]
+        del wq["q_colT"], wq["s_colT"]
         torch.cuda.synchronize()
         held = torch.cuda.memory_allocated() - base
         fwd_peak = torch.cuda.max_memory_allocated() - base
         dyq = mxq.quantize_grouped(dYm, ge, R | C, ldq)
-        xt = mxq.quantize_grouped(Xm, ge, C, ldq)
+        xt = xq if sched == "dual" else mxq.quantize_grouped(Xm, ge, C, ldq)
         if sched == "fb_split":
             wq.update(mxq.quantize_batched(Wm, R))
         mxq.mxq_grouped_gemm(mxq.MXQ_GG_RAGGED_M, dyq["q_row"], dyq["s_row"], wq["q_row"], wq["s_row"], mdX, ge)
         mxq.mxq_grouped_gemm(mxq.MXQ_GG_RAGGED_K, xt["q_colT"], xt["s_colT"], dyq["q_colT"], dyq["s_colT"], mdW, ge)
-        del dyq, xt, wq
+        del dyq, xt, xq, wq
         torch.cuda.synchronize()
         return {"held_fwd_to_bwd_bytes": held, "fwd_peak_bytes": fwd_peak,
                 "fwd_bwd_peak_bytes": torch.cuda.max_memory_allocated() - base}
@@ -556,12 +570,15 @@ def main():
     schedules["measured_held_difference_bytes"] = (schedules["dual"]["measured_memory"]["held_fwd_to_bwd_bytes"] -
                                                    schedules["fb_split"]["measured_memory"]["held_fwd_to_bwd_bytes"])
 
-    # the two schedules must produce the same input gradient bit for bit
-    ref = mdX.clone()
+    # the two schedules must produce the same input and weight gradients bit for bit
+    # (the last pass, the fb-split memory leg, left its gradients in mdX, mdW)
+    ref, ref_w = mdX.clone(), mdW.clone()
     moe_fwd(Timeline(torch), "dual")
     moe_bwd(Timeline(torch), "dual")
     torch.cuda.synchronize()
     schedules["bitwise_equal_dgrad"] = bool(torch.equal(ref, mdX))
+    schedules["bitwise_equal_wgrad"] = bool(torch.equal(ref_w, mdW))
+    del ref, ref_w
 
     # ---------------------------------------------------------------- small linear forward
     # X [256x512] and W [512x256] (N(0,1), seed 0): quantise X by rows and W
@@ -611,7 +628,8 @@ def main():
         "config": {
             "workload": "MX hot path step: MXFP4 QDQ 8192x8192 fp32 + MXFP8 dense linear M8192 K7168 N18432 "
                         "fwd/dgrad/wgrad with dual-axis quantisation + MoE 32 experts x (7168->4096), "
-                        "131072 routed rows, fwd/bwd, dual-axis schedule",
+                        "131072 routed rows, fwd/bwd, dual-axis schedule (X and W[g] quantised on both axes in the "
+                        "forward)",
             "gemm_tflop_per_step": round(step_flops / 1e12, 3),
             "parallelism": "single GPU",
         },

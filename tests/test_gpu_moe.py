@@ -237,6 +237,28 @@ def test_moe_fb_split_equals_dual(moe_full):
     assert torch.equal(dX, moe_full["dX"])
 
 
+def test_moe_dual_x_copies_equal_separate_quantisations(moe_full):
+    """The dual-axis schedule quantises X by rows and by tokens within each
+    expert group from one read in the forward; fb-split quantises it by rows in
+    the forward and by tokens in the backward.  Both copies, and the weight
+    gradient built on the token-axis copy, must be the same bit for bit."""
+    m = mxq()
+    X, ge = moe_full["X"], moe_full["ge"]
+    both = m.quantize_grouped(X, ge, 3, ldq=moe_full["qy"]["ldq"])
+    for k in ("q_row", "s_row"):
+        assert torch.equal(both[k], moe_full["qx"][k]), k
+    # token-axis copies: the written columns only (each group's tokens padded
+    # to 32; the rest of the ceil32(T + 31 G) columns is never written)
+    sizes = np.diff(np.concatenate([[0], moe_full["ge_np"]]))
+    used = int(((sizes + 31) // 32 * 32).sum())
+    assert torch.equal(both["q_colT"][:, :used], moe_full["qxt"]["q_colT"][:, :used])
+    assert torch.equal(both["s_colT"][:, :used // 32], moe_full["qxt"]["s_colT"][:, :used // 32])
+    qy = moe_full["qy"]
+    dW = m.grouped_gemm(m.MXQ_GG_RAGGED_K, both["q_colT"], both["s_colT"], qy["q_colT"], qy["s_colT"], ge)
+    torch.cuda.synchronize()
+    assert torch.equal(dW, moe_full["dW"])
+
+
 # ------------------------------------------------------------------ many groups
 def many_group_sizes(G, seed):
     """Mostly empty groups, some of 1-40 rows, three of 257: exercises group
