@@ -293,6 +293,13 @@ def main():
         mxq.mxq_quantize_grouped(dYm, ge, ldq, R | C, mdy["q_row"], mdy["s_row"], mdy["q_colT"], mdy["s_colT"])
         launches.append([f"moe_quant_dy_row_grouped {T}x{F}", "quant_tile_kernel<true, true, true>",
                          bytes_["moe_quant_dy_row_grouped"]])
+        # beside the step: the fb-split schedule's two X launches
+        mxq.mxq_quantize(Xm, R, mx["q_row"], mx["s_row"])
+        launches.append([f"moe_quant_x_row {T}x{H} (fb-split forward)", "quant_row_kernel<true>",
+                         bytes_["moe_quant_x_row"]])
+        mxq.mxq_quantize_grouped(Xm, ge, ldq, C, None, None, mxt["q_colT"], mxt["s_colT"])
+        launches.append([f"moe_quant_x_grouped {T}x{H} (fb-split backward)", "quant_tile_kernel<false, true, true>",
+                         bytes_["moe_quant_x_grouped"]])
         torch.cuda.synchronize()
         print(json.dumps({"quant_traffic_launches": launches}))
         return
