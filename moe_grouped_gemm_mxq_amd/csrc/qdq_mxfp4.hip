@@ -128,12 +128,6 @@ __global__ __launch_bounds__(kThreads) void qdq_rows_kernel(const float* __restr
   }
 }
 
-// The masked gradient of the clipped-STE backward is written with
-// non-temporal stores, which stream it past the caches instead of leaving it
-// dirty there (measured 5% faster; the same stores made the QDQ's own output
-// slower, so the QDQ keeps ordinary stores).
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 // Clipped STE backward, flat layout: grad_x = bit ? 0 : grad_y.
 // grad_x may alias grad_y (each element is read, then written, by one lane).
 __global__ __launch_bounds__(kThreads) void ste_flat_kernel(const float* gy, const uint32_t* __restrict__ sat_mask,
@@ -142,8 +136,8 @@ __global__ __launch_bounds__(kThreads) void ste_flat_kernel(const float* gy, con
        i += (int64_t)gridDim.x * kThreads) {
     const uint4 g = reinterpret_cast<const uint4*>(gy)[i];
     const uint32_t m = sat_mask[i >> 3] >> (4 * (i & 7));
-    __builtin_nontemporal_store(u32x4{m & 1u ? 0u : g.x, m & 2u ? 0u : g.y, m & 4u ? 0u : g.z, m & 8u ? 0u : g.w},
-                                reinterpret_cast<u32x4*>(gx) + i);
+    reinterpret_cast<uint4*>(gx)[i] = make_uint4(m & 1u ? 0u : g.x, m & 2u ? 0u : g.y,
+                                                 m & 4u ? 0u : g.z, m & 8u ? 0u : g.w);
   }
 }
 
@@ -162,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void ste_rows_kernel(const float* gy, con
       if (col + j < L) {
         const int64_t o = row * L + col + j;
         const float g = gy[o];
-        __builtin_nontemporal_store((m >> j) & 1u ? 0.0f : g, gx + o);
+        gx[o] = (m >> j) & 1u ? 0.0f : g;
       }
   }
 }
