@@ -724,10 +724,22 @@ def cpu_baseline(target_s, X, W, dY, Xm, Wm, dYm, ge, sizes, x4):
                 return n, t, 8.0 * xs.size / t / 1e9
             n = min(x4.shape[0], n * 2)
 
+    def dual_rate():
+        # the MXFP8 dual-axis quantisation oracle (row copy + column copy) of
+        # the dense X [8192 x 7168] bf16, over the kernel's 4.0625 bytes per
+        # element (2 read, 2 x (1 + 1/32) written)
+        xb = bf16_bits(X)
+        t0 = time.perf_counter()
+        oracle.mxfp8_quant_row(xb)
+        oracle.mxfp8_quant_colT(xb)
+        t = time.perf_counter() - t0
+        return t, 4.0625 * xb.size / t / 1e9
+
     lib = oracle.lib()
     cores = lib.oracle_num_threads()
     s, t, fl = grow(target_s)
     qn, qt, qgbs = qdq_rate(0.15 * target_s)
+    dt, dgbs = dual_rate()
     lib.oracle_set_num_threads(1)
     try:
         s1, t1, fl1 = grow(0.3 * target_s)
@@ -745,7 +757,10 @@ def cpu_baseline(target_s, X, W, dY, Xm, Wm, dYm, ge, sizes, x4):
             "mxfp4_qdq": {"value": round(qgbs, 3), "unit": "GB/s", "cores": cores,
                           "sample": f"first {qn} rows of the 8192x8192 input, 8 bytes per element, {qt:.2f} s",
                           "single_thread": {"value": round(qgbs1, 3), "unit": "GB/s", "cores": 1,
-                                            "sample": f"first {qn1} rows, {qt1:.2f} s"}}}
+                                            "sample": f"first {qn1} rows, {qt1:.2f} s"}},
+            "mxfp8_quantize_dual": {"value": round(dgbs, 3), "unit": "GB/s", "cores": cores,
+                                    "sample": f"dense X {X.shape[0]}x{X.shape[1]} bf16, row and column copies, "
+                                              f"4.0625 bytes per element, {dt:.2f} s"}}
 
 
 if __name__ == "__main__":
