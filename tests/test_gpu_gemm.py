@@ -28,8 +28,12 @@ def gemm_case(M, N, K, seed):
     return host(C), Cr, Ca, mfma_group_bound(A, sA, B, sB)
 
 
+# (300, 300, 32) and (300, 300, 160): several tiles with one and two real
+# K stages, the last one partial; tiles on odd (m-tile + n-tile) walk K one
+# stage behind and start on that partial stage
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (16, 16, 128), (17, 33, 96), (256, 256, 512),
-                                   (300, 260, 544), (513, 257, 1056), (64, 600, 4128)])
+                                   (300, 260, 544), (513, 257, 1056), (64, 600, 4128),
+                                   (300, 300, 32), (300, 300, 160)])
 def test_gemm_shapes_with_tails(M, N, K):
     C, Cr, Ca, hw = gemm_case(M, N, K, seed=M + N + K)
     ratio = assert_gemm_close(C, Cr, Ca, f"gemm {M}x{N}x{K}", hw_bound=hw)
