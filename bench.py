@@ -7,17 +7,17 @@ One step = one pass of the whole path over resident synthetic inputs:
     and weight-gradient GEMMs;
   * MoE expert layer, one GPU's 32 experts, 7168 -> 4096, 16384 tokens routed
     top-8 over Zipf(1.1) weights (131072 rows), dual-axis schedule: forward (X
-    by rows and by tokens within each expert group from one read, W[g] on both
-    axes, ragged-M GEMM) and backward (dY by rows and grouped by tokens,
-    ragged-M input gradient, ragged-K weight gradient).
-The forward/backward-split schedule of the MoE layer (X by rows and W[g] on
-its reduction axis only in the forward; X grouped by tokens and W[g] along N
-re-quantised in the backward) is
-timed beside the step, with the device memory each schedule holds from
-forward to backward; so are the dense linear's two schedules, the MXFP4 QDQ
-with its saturation mask and the masked (clipped-STE) backward, and the MXFP4
-GEMMs (operand quantisation, the dense forward shape, and the ragged-M MoE
-forward shape) with E2M1 operands.
+    by rows, W[g] on both axes with the N-axis copy saved, ragged-M GEMM) and
+    backward (dY by rows and grouped by tokens, X grouped by tokens, ragged-M
+    input gradient, ragged-K weight gradient).
+Timed beside the step, with the device memory each holds from forward to
+backward: the MoE layer's forward/backward-split schedule (W[g] on its
+reduction axis only in the forward, along N re-quantised in the backward)
+and a dual schedule that also keeps X's token-axis copy from the forward; the
+dense linear's two schedules; the MoE layer on the Zipf-law routing; the
+MXFP4 QDQ with its saturation mask and the masked (clipped-STE) backward;
+and the MXFP4 GEMMs (operand quantisation, the dense forward shape, and the
+ragged-M MoE forward shape) with E2M1 operands.
 
 Prints one JSON line.  `value` = GEMM FLOPs of the step / step time.
 """
@@ -202,36 +202,44 @@ def main():
                                  mw["s_row"].view(G, H // 128, F // 32, 32, 4) if mask & R else None,
                                  mw["q_colT"] if mask & C else None, mw["s_colT"] if mask & C else None)
 
-    # The dual-axis schedule quantises, in the forward, every operand copy the
-    # backward needs from forward inputs, from one read of each: W[g] along K
-    # and along N, X by rows and by tokens within each expert group (as the
-    # dense dual schedule keeps X's column copy).  fb-split quantises only what
-    # the forward uses and re-quantises X and W[g] in the backward.
-    def moe_fwd(tl, schedule):
-        if schedule == "dual":
+    # Expert weights (MindSpeed PR 3852): the dual-axis schedule quantises
+    # W[g] along K and along N from one read in the forward and keeps the
+    # N-axis copy for the input gradient; fb-split quantises W[g] along K only
+    # and re-quantises it along N in the backward.  In both, X is quantised by
+    # rows in the forward and by tokens within each expert group in the
+    # backward.  "dual_x" is the dual schedule that also quantises X by
+    # tokens in the forward (one read of X for both copies) and keeps that
+    # copy, as the dense dual schedule keeps X's column copy.
+    def moe_fwd(tl, schedule, Xs=None, ges=None):
+        Xs = Xm if Xs is None else Xs
+        ges = ge if ges is None else ges
+        if schedule == "dual_x":
             tl("moe_quant_x_row_grouped")
-            mxq.mxq_quantize_grouped(Xm, ge, ldq, R | C, mx["q_row"], mx["s_row"], mxt["q_colT"], mxt["s_colT"])
+            mxq.mxq_quantize_grouped(Xs, ges, ldq, R | C, mx["q_row"], mx["s_row"], mxt["q_colT"], mxt["s_colT"])
         else:
             tl("moe_quant_x_row")
-            mxq.mxq_quantize(Xm, R, mx["q_row"], mx["s_row"])
-        tl("moe_quant_w_dual" if schedule == "dual" else "moe_quant_w_colT")
-        quant_w_experts(R | C if schedule == "dual" else C)
+            mxq.mxq_quantize(Xs, R, mx["q_row"], mx["s_row"])
+        tl("moe_quant_w_colT" if schedule == "fb_split" else "moe_quant_w_dual")
+        quant_w_experts(C if schedule == "fb_split" else R | C)
         tl("moe_gemm_fwd_raggedM")
-        mxq.mxq_grouped_gemm(mxq.MXQ_GG_RAGGED_M, mx["q_row"], mx["s_row"], mw["q_colT"], mw["s_colT"], mY, ge)
+        mxq.mxq_grouped_gemm(mxq.MXQ_GG_RAGGED_M, mx["q_row"], mx["s_row"], mw["q_colT"], mw["s_colT"], mY, ges)
 
-    def moe_bwd(tl, schedule):
+    def moe_bwd(tl, schedule, Xs=None, ges=None):
+        Xs = Xm if Xs is None else Xs
+        ges = ge if ges is None else ges
         tl("moe_quant_dy_row_grouped")
-        mxq.mxq_quantize_grouped(dYm, ge, ldq, R | C, mdy["q_row"], mdy["s_row"], mdy["q_colT"], mdy["s_colT"])
-        if schedule == "fb_split":
+        mxq.mxq_quantize_grouped(dYm, ges, ldq, R | C, mdy["q_row"], mdy["s_row"], mdy["q_colT"], mdy["s_colT"])
+        if schedule != "dual_x":
             tl("moe_quant_x_grouped")
-            mxq.mxq_quantize_grouped(Xm, ge, ldq, C, None, None, mxt["q_colT"], mxt["s_colT"])
+            mxq.mxq_quantize_grouped(Xs, ges, ldq, C, None, None, mxt["q_colT"], mxt["s_colT"])
+        if schedule == "fb_split":
             tl("moe_requant_w_row")
             quant_w_experts(R)
         tl("moe_gemm_dgrad_raggedM")
         mxq.mxq_grouped_gemm(mxq.MXQ_GG_RAGGED_M, mdy["q_row"], mdy["s_row"], mw["q_row"].view(G, H, F),
-                             mw["s_row"].view(G, H // 128, F // 32, 32, 4), mdX, ge)
+                             mw["s_row"].view(G, H // 128, F // 32, 32, 4), mdX, ges)
         tl("moe_gemm_wgrad_raggedK")
-        mxq.mxq_grouped_gemm(mxq.MXQ_GG_RAGGED_K, mxt["q_colT"], mxt["s_colT"], mdy["q_colT"], mdy["s_colT"], mdW, ge)
+        mxq.mxq_grouped_gemm(mxq.MXQ_GG_RAGGED_K, mxt["q_colT"], mxt["s_colT"], mdy["q_colT"], mdy["s_colT"], mdW, ges)
 
     def step(tl):
         tl("qdq_fp4")
@@ -334,12 +342,34 @@ def main():
             d.update(gbs=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
         components[k] = d
 
-    # dominant kernel: the GEMM launch taking the most time per step
-    dom = max((k for k in avg if k in flops), key=lambda k: avg[k])
-    dom_tf = flops[dom] / (avg[dom] * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 1), "peak": PEAK_FP8_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_FP8_TFLOPS, 4), "traffic": measured_traffic(dom),
-                "algorithmic_flops_per_launch": flops[dom], "avg_launch_ms": round(avg[dom], 4)}
+    # GEMM kernels of the step and the components (one launch each) they run
+    kernels = {
+        "moe_gemm_raggedM": ("gemm_mx_kernel ragged M (expert forward and input gradient)",
+                             ["moe_gemm_fwd_raggedM", "moe_gemm_dgrad_raggedM"]),
+        "dense_gemm": ("gemm_mx_kernel dense (forward, input and weight gradient)",
+                       ["dense_gemm_fwd", "dense_gemm_dgrad", "dense_gemm_wgrad"]),
+        "moe_gemm_wgrad_raggedK": ("gemm_mx_kernel ragged K (expert weight gradient; experts with more than "
+                                   "1024 tokens, then the exact-group launch for the rest)",
+                                   ["moe_gemm_wgrad_raggedK"]),
+    }
+
+    def kernel_roofline(label):
+        desc, comps = kernels[label]
+        launch_ms = sum(avg[c] for c in comps) / len(comps)        # mean over its launches
+        per_launch = sum(flops[c] for c in comps) / len(comps)     # (equal FLOPs per launch)
+        tf = per_launch / (launch_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "kernel": label, "description": desc, "achieved": round(tf, 1),
+                "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                "traffic": measured_traffic(label), "algorithmic_flops_per_launch": per_launch,
+                "avg_launch_ms": round(launch_ms, 4), "launches_per_step": len(comps),
+                "step_share": round(sum(avg[c] for c in comps) / ms_per_step, 4)}
+
+    # dominant kernel: the GEMM kernel with the largest share of the step;
+    # beside it the slowest single launch
+    dom = max(kernels, key=lambda k: sum(avg[c] for c in kernels[k][1]))
+    slow = max(kernels, key=lambda k: max(avg[c] for c in kernels[k][1]))
+    roofline = kernel_roofline(dom)
+    roofline_slowest = kernel_roofline(slow)
 
     # ---------------------------------------------------------------- dense schedules: time and memory
     # dual: the forward quantises X and W on both axes and keeps X's column
@@ -641,6 +671,7 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": roofline,
+        "roofline_slowest_launch": roofline_slowest,
         "cpu_baseline": cpu,
         "components": components,
         "dense_schedules": dense_sched,

@@ -63,6 +63,10 @@ extern "C" {
 #define MXQ_ABI_VERSION 5
 #define MXQ_BLOCK 32          /* elements per MX block; fixed */
 #define MXQ_MAX_GROUPS 1024   /* largest G the grouped entry points accept */
+/* E4M3 GEMM reductions of at most this many elements (dense and ragged M: K;
+ * ragged K: an expert's token count) run with exact 8-product MFMA groups;
+ * see mxq_gemm. */
+#define MXQ_EXACT_GROUPS_MAX_K 1024
 
 typedef enum {
     MXQ_OK = 0,

@@ -11,6 +11,8 @@
 
 namespace mxq {
 
+static_assert(kIlvMaxK == MXQ_EXACT_GROUPS_MAX_K, "the header states the kernels' threshold");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -184,6 +186,7 @@ mxq_status mxq_quantize_grouped(const uint16_t* x, int64_t T, int64_t C, int64_t
                                 hipStream_t st) {
   MXQ_REQUIRE(x != nullptr && group_end != nullptr, "mxq_quantize_grouped: x or group_end is NULL");
   MXQ_REQUIRE(T >= 1 && C >= 1, "mxq_quantize_grouped: T and C must be >= 1");
+  MXQ_REQUIRE(T <= INT32_MAX, "mxq_quantize_grouped: T must be < 2^31 (group ends are int32)");
   MXQ_REQUIRE(ldx >= C, "mxq_quantize_grouped: ldx < C");
   MXQ_REQUIRE(G >= 1 && G <= MXQ_MAX_GROUPS, "mxq_quantize_grouped: G must be in [1, %d] (got %d)",
               MXQ_MAX_GROUPS, G);
@@ -293,6 +296,8 @@ mxq_status mxq_grouped_gemm(mxq_gg_mode mode, const uint8_t* A, const uint8_t* s
   MXQ_REQUIRE(M >= 1 && N >= 1, "mxq_grouped_gemm: M and N must be >= 1");
   MXQ_REQUIRE(K >= 32 && K % 32 == 0, "mxq_grouped_gemm: K must be a positive multiple of 32");
   MXQ_REQUIRE(G >= 1 && G <= MXQ_MAX_GROUPS, "mxq_grouped_gemm: G must be in [1, %d]", MXQ_MAX_GROUPS);
+  MXQ_REQUIRE(mode != MXQ_GG_RAGGED_M || M <= INT32_MAX,
+              "mxq_grouped_gemm: M must be < 2^31 for MXQ_GG_RAGGED_M (group ends are int32)");
   MXQ_REQUIRE(aligned16(A) && aligned16(B) && ((uintptr_t)C & 3u) == 0, "mxq_grouped_gemm: A, B must be 16-byte aligned");
   MXQ_REQUIRE((((uintptr_t)sA | (uintptr_t)sB) & 3u) == 0,
               "mxq_grouped_gemm: sA, sB must be 4-byte aligned (the kernel reads scale dwords)");

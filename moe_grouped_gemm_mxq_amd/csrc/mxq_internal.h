@@ -6,6 +6,10 @@
 
 namespace mxq {
 
+// Longest reduction that the E4M3 GEMMs run with one real product per
+// 8-product MFMA group (exact group sums); MXQ_EXACT_GROUPS_MAX_K of mxq.h.
+constexpr int kIlvMaxK = 1024;
+
 // number of compute units of the current device (cached per device)
 int device_cu_count();
 

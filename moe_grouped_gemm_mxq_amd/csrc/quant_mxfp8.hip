@@ -158,6 +158,7 @@ __global__ __launch_bounds__(kRowThreads) void quant_row_kernel(const uint16_t* 
 constexpr int kTR = 128, kTC = 128, kLdsStride = kTC * 2 + 16;
 constexpr int kCodePitch = kTR + 16;  // code tile row pitch: 16-byte aligned, 4-pass b128 reads
 static_assert(kTC * kCodePitch <= kTR * kLdsStride, "the code tile reuses the bf16 tile's LDS");
+static_assert(kThreads * sizeof(int64_t) <= kTR * kLdsStride, "the group scan's scratch reuses the tile's LDS");
 
 template <bool ROW, bool GROUPED, bool VEC>
 __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
     // the scan's scratch is the tile buffer, not yet in use
     __shared__ int32_t bstart[kMaxGroups + 1];
     build_block_starts<kThreads>(group_end, G, R, 32, nullptr, nullptr, bstart,
-                                 reinterpret_cast<int32_t*>(tile));
+                                 reinterpret_cast<int64_t*>(tile));
     if (t < kTR / 32) {
       const int64_t pb = p0 / 32 + t;
       int64_t src = 0;
@@ -197,9 +198,10 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
         const int g = find_block_group(bstart, G, (int32_t)pb);
         int32_t gstart, gsize;
         group_span(group_end, g, R, gstart, gsize);
-        const int32_t off = ((int32_t)pb - bstart[g]) * 32;
+        // (bstart is non-decreasing and bstart[g] <= pb < bstart[g] + ceil32(gsize) / 32)
+        const int64_t off = (pb - bstart[g]) * 32;
         src = (int64_t)gstart + off;
-        valid = min(32, gsize - off);
+        valid = (int32_t)min<int64_t>(32, gsize - off);
         if (valid <= 0) valid = -1;  // cannot happen for consistent tables
       }
       rb_src[t] = src;

@@ -18,7 +18,10 @@ Workloads (shapes and distributions of the sources' configurations):
   Zipf(1.1) expert weights; X = tokens [16384x7168] N(0,1) gathered in expert
   order into [131072x7168]; W [32x7168x4096] N(0, 0.02^2); dY [131072x4096]
   N(0,1); all bf16.  The per-expert row counts are frozen in
-  ``data/moe_group_sizes_zipf1.1_top8.json``.
+  ``data/moe_group_sizes_zipf1.1_top8.json``.  A second routing,
+  ``routing="zipf_law"``, draws from Zipf-law expert popularity
+  w_e = (e + 1)^-1.1 instead (every expert gets tokens); its sizes are
+  frozen in ``data/moe_group_sizes_zipflaw1.1_top8.json``.
 """
 from __future__ import annotations
 
@@ -30,6 +33,8 @@ import torch
 
 _DATA = os.path.join(os.path.dirname(os.path.abspath(__file__)), "data")
 MOE_SIZES_FILE = os.path.join(_DATA, "moe_group_sizes_zipf1.1_top8.json")
+MOE_LAW_SIZES_FILE = os.path.join(_DATA, "moe_group_sizes_zipflaw1.1_top8.json")
+ROUTINGS = ("zipf_weights", "zipf_law")
 
 MOE_EXPERTS = 32
 MOE_TOKENS = 16384
@@ -96,8 +101,8 @@ def qdq_large(n: int = 8192, frac_rows: float = 0.01, device="cpu") -> torch.Ten
 
 
 # ------------------------------------------------------------------ MoE
-def moe_group_sizes() -> list[int]:
-    with open(MOE_SIZES_FILE) as f:
+def moe_group_sizes(routing: str = "zipf_weights") -> list[int]:
+    with open(MOE_SIZES_FILE if routing == "zipf_weights" else MOE_LAW_SIZES_FILE) as f:
         return list(json.load(f)["sizes"])
 
 
@@ -106,10 +111,17 @@ def group_end_from_sizes(sizes) -> torch.Tensor:
     return torch.tensor(np.cumsum(np.asarray(sizes, dtype=np.int64)), dtype=torch.int32)
 
 
-def moe_routing(experts=MOE_EXPERTS, tokens=MOE_TOKENS, top_k=MOE_TOPK, seed=0) -> torch.Tensor:
+def moe_routing(experts=MOE_EXPERTS, tokens=MOE_TOKENS, top_k=MOE_TOPK, seed=0,
+                routing: str = "zipf_weights") -> torch.Tensor:
     """[tokens x top_k] expert ids: top-k distinct experts per token by
-    multinomial sampling over Zipf(1.1) expert weights."""
-    w = np.random.default_rng(seed).zipf(1.1, experts).astype(np.float64)
+    multinomial sampling over expert weights -- i.i.d. Zipf(1.1) draws
+    ("zipf_weights") or the Zipf law (e + 1)^-1.1 ("zipf_law")."""
+    if routing == "zipf_weights":
+        w = np.random.default_rng(seed).zipf(1.1, experts).astype(np.float64)
+    elif routing == "zipf_law":
+        w = (np.arange(experts, dtype=np.float64) + 1.0) ** -1.1
+    else:
+        raise ValueError(f"unknown routing {routing!r}; one of {ROUTINGS}")
     p = torch.tensor(w / w.sum(), dtype=torch.float64)
     return torch.multinomial(p.expand(tokens, experts), top_k, replacement=False,
                              generator=generator(seed))
@@ -123,11 +135,11 @@ def moe_row_tokens(idx: torch.Tensor, experts=MOE_EXPERTS) -> tuple[torch.Tensor
     return tok[order], sizes
 
 
-def moe_layer(device="cpu", with_dy=True):
+def moe_layer(device="cpu", with_dy=True, routing: str = "zipf_weights"):
     """X [131072x7168], W [32x7168x4096], dY [131072x4096] (bf16) and group_end [32]."""
-    idx = moe_routing()
+    idx = moe_routing(routing=routing)
     row_tok, sizes = moe_row_tokens(idx)
-    if sizes != moe_group_sizes():
+    if sizes != moe_group_sizes(routing):
         raise RuntimeError("MoE routing draw differs from the frozen group sizes; "
                            "the random number streams of this torch build changed")
     xtok = randn_bf16((MOE_TOKENS, MOE_HIDDEN), 0, device=device)

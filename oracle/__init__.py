@@ -281,6 +281,22 @@ def gemm_fp4_sampled(A, sA, B, sB, mi, ni):
 
 
 # ---------------------------------------------------------------- GEMMs
+def gemm_dequantised(a: np.ndarray, b: np.ndarray):
+    """C = a b^T and sum_k |a_k b_k| = |a| |b|^T for operands already
+    dequantised to fp64 (mxfp8_dequant / mxfp4_dequant rows of K values).
+
+    The same definition as ``gemm`` -- fp64 sums of the exact products -- with
+    numpy's fp64 matrix product as the summation step (only the order of the
+    fp64 additions differs), for full-size checks where the plain loops take
+    minutes."""
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    b = np.ascontiguousarray(b, dtype=np.float64)
+    assert a.ndim == 2 and b.ndim == 2 and a.shape[1] == b.shape[1]
+    C = a @ b.T
+    Cabs = np.abs(a) @ np.abs(b).T
+    return C, Cabs
+
+
 def gemm(A, sA, B, sB):
     """C[m][n] = sum_k deq(A)[m][k]*deq(B)[n][k]; returns (C, sum|products|) in fp64."""
     M, K = A.shape

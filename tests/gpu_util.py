@@ -59,10 +59,13 @@ def scaled_randn(shape, seed, lo=-20, hi=20, zero_rows=0, axis=0):
 
 
 def mfma_group_bound(A, sA, B, sB, mi=None, ni=None):
-    """Error bound of the gfx950 FP8 scaled MFMA's internal summation: it adds
-    each group of 8 consecutive-K products with about 13 bits below the group's
-    largest product (measured), so per output
-    |err| <= 2^-10 * sum over groups of max |product| (on top of fp32 rounding)."""
+    """Error model of the gfx950 FP8 scaled MFMA's internal summation on the
+    plain (non-interleaved) path: it adds each group of 8 consecutive-K
+    products with about 13 bits below the group's largest product
+    (measured), so per output |err| <= 2^-10 * sum over groups of max
+    |product| on top of fp32 rounding.  Used only by the test that documents
+    this deviation on adversarial data; every parity test asserts the strict
+    bound alone."""
     a = oracle.mxfp8_dequant(A, sA)
     b = oracle.mxfp8_dequant(B, sB)
     if mi is not None:
@@ -79,21 +82,24 @@ def mfma_group_bound(A, sA, B, sB, mi=None, ni=None):
     return 2.0 ** -10 * out
 
 
-def assert_gemm_close(got: np.ndarray, ref: np.ndarray, refabs: np.ndarray, what: str,
-                      hw_bound: np.ndarray | None = None):
-    """|got - ref| <= 1e-5 * sum|ab| per element, plus `hw_bound` (the FP8 MFMA
-    group-truncation term of mfma_group_bound) where the reduction is short.
+def assert_gemm_close(got: np.ndarray, ref: np.ndarray, refabs: np.ndarray, what: str):
+    """|got - ref| <= 1e-5 * sum_k |a_k b_k| for every output, no NaN/Inf.
     Returns max err / sum|ab| (the strict ratio)."""
     got = np.asarray(got, np.float64)
     assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
     err = np.abs(got - ref)
-    bound = GEMM_TOL * refabs + (0.0 if hw_bound is None else hw_bound)
-    bad = err > bound
-    ratio = float(np.max(err / np.where(refabs > 0, refabs, 1.0)))
-    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} outputs outside the bound "
-                           f"({'strict' if hw_bound is None else 'with MFMA group term'}); "
+    bad = err > GEMM_TOL * refabs
+    ratio = float(np.max(err / np.where(refabs > 0, refabs, 1.0))) if err.size else 0.0
+    print(f"[strict] {what}: {err.size} outputs, max err/sum|ab| = {ratio:.3e} "
+          f"({ratio / GEMM_TOL:.3f} of the bound)")
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} outputs outside 1e-5*sum|ab|; "
                            f"max err/sum|ab| = {ratio:.3e}")
     return ratio
+
+
+def deq(q, s) -> np.ndarray:
+    """Oracle dequantisation of oracle codes and row-major scales (fp64)."""
+    return oracle.mxfp8_dequant(np.ascontiguousarray(q), np.ascontiguousarray(s))
 
 
 def boundary_indices(n: int, tile: int, rng, extra: int) -> np.ndarray:
@@ -112,36 +118,9 @@ def assert_bytes_equal(got: np.ndarray, ref: np.ndarray, what: str):
     got = np.asarray(got)
     ref = np.asarray(ref)
     assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
+    if np.array_equal(got, ref):
+        return
     bad = np.argwhere(got != ref)
     if len(bad):
         ex = [(tuple(int(i) for i in b), int(got[tuple(b)]), int(ref[tuple(b)])) for b in bad[:8]]
         raise AssertionError(f"{what}: {len(bad)} of {got.size} bytes differ; first (index, got, want): {ex}")
-
-
-def ragged_m_bound(A, sA, Bq, Bs, ge):
-    """mfma_group_bound for a ragged-M grouped GEMM (rows of group g x B[g])."""
-    out = np.zeros((A.shape[0], Bq.shape[1]))
-    start = 0
-    for g, e in enumerate(np.asarray(ge).tolist()):
-        if e > start:
-            out[start:e] = mfma_group_bound(np.ascontiguousarray(A[start:e]), np.ascontiguousarray(sA[start:e]),
-                                            Bq[g], Bs[g])
-        start = e
-    return out
-
-
-def ragged_k_bound(A, sA, B, sB, ge):
-    """mfma_group_bound for a ragged-K grouped GEMM over each group's padded columns."""
-    G = len(ge)
-    out = np.zeros((G, A.shape[0], B.shape[0]))
-    P, start = 0, 0
-    for g, e in enumerate(np.asarray(ge).tolist()):
-        w = (e - start + 31) // 32 * 32
-        if w:
-            sl = slice(P, P + w)
-            ss = slice(P // 32, (P + w) // 32)
-            out[g] = mfma_group_bound(np.ascontiguousarray(A[:, sl]), np.ascontiguousarray(sA[:, ss]),
-                                      np.ascontiguousarray(B[:, sl]), np.ascontiguousarray(sB[:, ss]))
-        P += w
-        start = e
-    return out

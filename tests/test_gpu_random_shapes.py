@@ -3,15 +3,14 @@ tails, group counts and group sizes (with empty and tiny groups) are drawn at
 random from fixed seeds, so tile tails, partial 128-row scale groups and
 group boundaries meet in combinations the hand-picked cases do not.  Same
 bars as the other parity tests: codes and scales bit-exact, GEMM outputs
-within 1e-5 * sum|ab| plus the measured MFMA group term, E2M1 outputs
-bit-exact."""
+within 1e-5 * sum|ab| (E2M1 outputs exact).  K is drawn on both sides of
+the 1024-element interleaving threshold."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from gpu_util import (assert_bytes_equal, assert_gemm_close, bits, host, mfma_group_bound, mxq, out_host,
-                      ragged_k_bound, ragged_m_bound, scaled_randn)
+from gpu_util import assert_bytes_equal, assert_gemm_close, bits, host, mxq, out_host, scaled_randn
 
 pytestmark = pytest.mark.gpu
 SEEDS = list(range(8))
@@ -66,7 +65,7 @@ def test_random_grouped_quantize(seed):
 @pytest.mark.parametrize("seed", SEEDS)
 def test_random_dense_gemm(seed):
     rng = np.random.default_rng(300 + seed)
-    M, N, K = int(rng.integers(1, 600)), int(rng.integers(1, 600)), int(rng.integers(1, 800))
+    M, N, K = int(rng.integers(1, 600)), int(rng.integers(1, 600)), int(rng.integers(1, 2000))
     m = mxq()
     X = scaled_randn((M, K), 300 + seed, lo=-8, hi=8)
     W = scaled_randn((N, K), 350 + seed, lo=-8, hi=8)
@@ -76,13 +75,13 @@ def test_random_dense_gemm(seed):
     A, sA = oracle.mxfp8_quant_row(bits(X))
     B, sB = oracle.mxfp8_quant_row(bits(W))
     Cr, Ca = oracle.gemm(A, sA, B, sB)
-    assert_gemm_close(host(C), Cr, Ca, f"dense {M}x{N}x{K}", hw_bound=mfma_group_bound(A, sA, B, sB))
+    assert_gemm_close(host(C), Cr, Ca, f"dense {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("seed", SEEDS)
 def test_random_ragged_m(seed):
     rng = np.random.default_rng(400 + seed)
-    G, N, K = int(rng.integers(1, 10)), int(rng.integers(1, 300)), int(rng.integers(1, 12)) * 32
+    G, N, K = int(rng.integers(1, 10)), int(rng.integers(1, 300)), int(rng.integers(1, 64)) * 32
     sizes = draw_sizes(rng, G, 400)
     T = int(sizes.sum())
     m = mxq()
@@ -101,8 +100,7 @@ def test_random_ragged_m(seed):
     got = host(C)
     if T:
         Cr, Ca = oracle.grouped_gemm_ragged_m(A, sA, Bq, Bs, ge)
-        hw = ragged_m_bound(A, sA, Bq, Bs, ge)
-        assert_gemm_close(got[:T], Cr[:T], Ca[:T], f"ragged M {sizes.tolist()} N {N} K {K}", hw_bound=hw[:T])
+        assert_gemm_close(got[:T], Cr[:T], Ca[:T], f"ragged M {sizes.tolist()} N {N} K {K}")
     assert np.all(got[T:] == 3.0), "rows in no group were written"
 
 
@@ -110,7 +108,7 @@ def test_random_ragged_m(seed):
 def test_random_ragged_k(seed):
     rng = np.random.default_rng(500 + seed)
     G, Mh, N = int(rng.integers(1, 10)), int(rng.integers(1, 300)), int(rng.integers(1, 300))
-    sizes = draw_sizes(rng, G, 300)
+    sizes = draw_sizes(rng, G, 2000)
     if sizes.sum() == 0:
         sizes[-1] = 5
     T = int(sizes.sum())
@@ -127,7 +125,7 @@ def test_random_ragged_k(seed):
     B, sB = oracle.mxfp8_quant_grouped_colT(bits(dY), ge_np, qx["ldq"])
     Cr, Ca = oracle.grouped_gemm_ragged_k(A, sA, B, sB, ge_np)
     got = host(C)
-    assert_gemm_close(got, Cr, Ca, f"ragged K {sizes.tolist()} {Mh}x{N}", hw_bound=ragged_k_bound(A, sA, B, sB, ge_np))
+    assert_gemm_close(got, Cr, Ca, f"ragged K {sizes.tolist()} {Mh}x{N}")
     for g, s in enumerate(sizes.tolist()):
         if s == 0:
             assert np.all(got[g] == 0.0), f"empty group {g} not exactly zero"

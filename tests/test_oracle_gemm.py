@@ -41,6 +41,19 @@ def test_gemm_equals_numpy_matmul_of_dequantised(M, N, K):
     assert np.allclose(Cabs, refabs, rtol=1e-13, atol=0)
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (33, 70, 160), (96, 40, 1024)])
+def test_gemm_dequantised_equals_gemm(M, N, K):
+    """The full-size checks' BLAS route (dequantise, then an fp64 matrix
+    product) gives the plain loops' sums up to fp64 rounding order."""
+    rng = np.random.default_rng(7 * M + N + K)
+    A, sA = rand_operand(rng, M, K, lo=90, hi=160)
+    B, sB = rand_operand(rng, N, K, lo=90, hi=160)
+    C, Cabs = oracle.gemm(A, sA, B, sB)
+    C2, Cabs2 = oracle.gemm_dequantised(oracle.mxfp8_dequant(A, sA), oracle.mxfp8_dequant(B, sB))
+    assert np.all(np.abs(C2 - C) <= 1e-13 * Cabs)
+    assert np.all(np.abs(Cabs2 - Cabs) <= 1e-13 * Cabs)
+
+
 def test_gemm_one_hot_rows_select_products_exactly():
     K = 128
     A = np.zeros((4, K), np.uint8)
