@@ -292,22 +292,21 @@ def main():
         for name, t, q, r, c in (("X", X, qx, M, K), ("W", W, qw, K, N), ("dY", dY, qy, M, N)):
             mxq.mxq_quantize(t, R | C, q["q_row"], q["s_row"], q["q_colT"], q["s_colT"])
             launches.append([f"dense_quant_dual {name} {r}x{c}", "quant_tile_kernel<true, false, true>", qb(r, c, 2)])
-        mxq.mxq_quantize_grouped(Xm, ge, ldq, R | C, mx["q_row"], mx["s_row"], mxt["q_colT"], mxt["s_colT"])
-        launches.append([f"moe_quant_x_row_grouped {T}x{H}", "quant_tile_kernel<true, true, true>",
-                         bytes_["moe_quant_x_row_grouped"]])
+        mxq.mxq_quantize(Xm, R, mx["q_row"], mx["s_row"])
+        launches.append([f"moe_quant_x_row {T}x{H}", "quant_row_kernel<true>", bytes_["moe_quant_x_row"]])
         quant_w_experts(R | C)
         launches.append([f"moe_quant_w_dual {G}x{H}x{F}", "quant_tile_kernel<true, false, true>",
                          bytes_["moe_quant_w_dual"]])
         mxq.mxq_quantize_grouped(dYm, ge, ldq, R | C, mdy["q_row"], mdy["s_row"], mdy["q_colT"], mdy["s_colT"])
         launches.append([f"moe_quant_dy_row_grouped {T}x{F}", "quant_tile_kernel<true, true, true>",
                          bytes_["moe_quant_dy_row_grouped"]])
-        # beside the step: the fb-split schedule's two X launches
-        mxq.mxq_quantize(Xm, R, mx["q_row"], mx["s_row"])
-        launches.append([f"moe_quant_x_row {T}x{H} (fb-split forward)", "quant_row_kernel<true>",
-                         bytes_["moe_quant_x_row"]])
         mxq.mxq_quantize_grouped(Xm, ge, ldq, C, None, None, mxt["q_colT"], mxt["s_colT"])
-        launches.append([f"moe_quant_x_grouped {T}x{H} (fb-split backward)", "quant_tile_kernel<false, true, true>",
+        launches.append([f"moe_quant_x_grouped {T}x{H}", "quant_tile_kernel<false, true, true>",
                          bytes_["moe_quant_x_grouped"]])
+        # beside the step: the dual_x schedule's X launch (rows and tokens from one read)
+        mxq.mxq_quantize_grouped(Xm, ge, ldq, R | C, mx["q_row"], mx["s_row"], mxt["q_colT"], mxt["s_colT"])
+        launches.append([f"moe_quant_x_row_grouped {T}x{H} (dual_x forward)", "quant_tile_kernel<true, true, true>",
+                         bytes_["moe_quant_x_row_grouped"]])
         torch.cuda.synchronize()
         print(json.dumps({"quant_traffic_launches": launches}))
         return
@@ -545,7 +544,7 @@ def main():
 
     # ---------------------------------------------------------------- MoE schedules: time and memory
     schedules = {}
-    for sched in ("dual", "fb_split"):
+    for sched in ("dual", "fb_split", "dual_x"):
         for _ in range(2):
             tl = Timeline(torch)
             moe_fwd(tl, sched)
@@ -566,8 +565,8 @@ def main():
         for tl in fb:
             for k, v in tl.durations().items():
                 d.setdefault(k, []).extend(v)
-        held_w = (mw["q_row"].numel() + mw["s_row"].numel()) if sched == "dual" else 0
-        held_x = (mxt["q_colT"].numel() + mxt["s_colT"].numel()) if sched == "dual" else 0
+        held_w = (mw["q_row"].numel() + mw["s_row"].numel()) if sched != "fb_split" else 0
+        held_x = (mxt["q_colT"].numel() + mxt["s_colT"].numel()) if sched == "dual_x" else 0
         schedules[sched] = {"fwd_ms": round(sum(d["fwd"]) / len(d["fwd"]), 3),
                             "bwd_ms": round(sum(d["bwd"]) / len(d["bwd"]), 3),
                             "quantised_w_held_fwd_to_bwd_bytes": held_w,
@@ -582,8 +581,8 @@ def main():
         torch.cuda.synchronize()
         base = torch.cuda.memory_allocated()
         torch.cuda.reset_peak_memory_stats()
-        xq = mxq.quantize_grouped(Xm, ge, R | C, ldq) if sched == "dual" else mxq.quantize(Xm, R)
-        wq = mxq.quantize_batched(Wm, R | C if sched == "dual" else C)
+        xq = mxq.quantize_grouped(Xm, ge, R | C, ldq) if sched == "dual_x" else mxq.quantize(Xm, R)
+        wq = mxq.quantize_batched(Wm, C if sched == "fb_split" else R | C)
         mxq.mxq_grouped_gemm(mxq.MXQ_GG_RAGGED_M, xq["q_row"], xq["s_row"], wq["q_colT"], wq["s_colT"], mY, ge)
         for k in ("q_row", "s_row"):
             del xq[k]
@@ -592,7 +591,7 @@ def main():
         held = torch.cuda.memory_allocated() - base
         fwd_peak = torch.cuda.max_memory_allocated() - base
         dyq = mxq.quantize_grouped(dYm, ge, R | C, ldq)
-        xt = xq if sched == "dual" else mxq.quantize_grouped(Xm, ge, C, ldq)
+        xt = xq if sched == "dual_x" else mxq.quantize_grouped(Xm, ge, C, ldq)
         if sched == "fb_split":
             wq.update(mxq.quantize_batched(Wm, R))
         mxq.mxq_grouped_gemm(mxq.MXQ_GG_RAGGED_M, dyq["q_row"], dyq["s_row"], wq["q_row"], wq["s_row"], mdX, ge)
@@ -602,20 +601,54 @@ def main():
         return {"held_fwd_to_bwd_bytes": held, "fwd_peak_bytes": fwd_peak,
                 "fwd_bwd_peak_bytes": torch.cuda.max_memory_allocated() - base}
 
-    for sched in ("dual", "fb_split"):
+    for sched in ("dual", "fb_split", "dual_x"):
         schedules[sched]["measured_memory"] = moe_memory(sched)
     schedules["measured_held_difference_bytes"] = (schedules["dual"]["measured_memory"]["held_fwd_to_bwd_bytes"] -
                                                    schedules["fb_split"]["measured_memory"]["held_fwd_to_bwd_bytes"])
 
-    # the two schedules must produce the same input and weight gradients bit for bit
-    # (the last pass, the fb-split memory leg, left its gradients in mdX, mdW)
-    ref, ref_w = mdX.clone(), mdW.clone()
-    moe_fwd(Timeline(torch), "dual")
-    moe_bwd(Timeline(torch), "dual")
+    # the schedules must produce the same input and weight gradients bit for bit
+    grads = {}
+    for sched in ("dual", "fb_split", "dual_x"):
+        moe_fwd(Timeline(torch), sched)
+        moe_bwd(Timeline(torch), sched)
+        grads[sched] = (mdX.clone(), mdW.clone())
     torch.cuda.synchronize()
-    schedules["bitwise_equal_dgrad"] = bool(torch.equal(ref, mdX))
-    schedules["bitwise_equal_wgrad"] = bool(torch.equal(ref_w, mdW))
-    del ref, ref_w
+    schedules["bitwise_equal_dgrad"] = all(torch.equal(grads["dual"][0], g[0]) for g in grads.values())
+    schedules["bitwise_equal_wgrad"] = all(torch.equal(grads["dual"][1], g[1]) for g in grads.values())
+    del grads
+
+    # ---------------------------------------------------------------- Zipf-law routing
+    # The same layer with tokens routed over Zipf-law expert popularity
+    # (e + 1)^-1.1: no empty expert, every size off a multiple of 32.  X and
+    # dY are the same draws as above, X gathered in this routing's expert
+    # order; the dual schedule, per-component times.
+    Xl, _, _, gel = workloads.moe_layer(device=dev, with_dy=False, routing="zipf_law")
+    gel = gel.to(dev)
+    law_runs = []
+    for i in range(6):
+        tl = Timeline(torch)
+        moe_fwd(tl, "dual", Xl, gel)
+        moe_bwd(tl, "dual", Xl, gel)
+        tl(None)
+        if i >= 2:
+            law_runs.append(tl)
+    torch.cuda.synchronize()
+    dl = {}
+    for tl in law_runs:
+        for k, v in tl.durations().items():
+            dl.setdefault(k, []).extend(v)
+    law_sizes = workloads.moe_group_sizes("zipf_law")
+    law = {"sizes": law_sizes, "components": {}}
+    for k, v in dl.items():
+        ms = sum(v) / len(v)
+        d = {"ms": round(ms, 4)}
+        if k.startswith("moe_gemm"):
+            tf = 2.0 * T * H * F / (ms * 1e-3) / 1e12
+            d.update(tflops=round(tf, 1), frac_fp8_peak=round(tf / PEAK_FP8_TFLOPS, 4))
+        law["components"][k] = d
+    law["fwd_bwd_ms"] = round(sum(d["ms"] for d in law["components"].values()), 3)
+    law["tiles"] = moe_tile_stats(law_sizes, H, F, torch.cuda.get_device_properties(0).multi_processor_count)
+    del Xl, gel
 
     # ---------------------------------------------------------------- small linear forward
     # X [256x512] and W [512x256] (N(0,1), seed 0): quantise X by rows and W
@@ -665,8 +698,8 @@ def main():
         "config": {
             "workload": "MX hot path step: MXFP4 QDQ 8192x8192 fp32 + MXFP8 dense linear M8192 K7168 N18432 "
                         "fwd/dgrad/wgrad with dual-axis quantisation + MoE 32 experts x (7168->4096), "
-                        "131072 routed rows, fwd/bwd, dual-axis schedule (X and W[g] quantised on both axes in the "
-                        "forward)",
+                        "131072 routed rows, fwd/bwd, dual-axis schedule (W[g] quantised on both axes in the forward, "
+                        "its N-axis copy saved; X by rows in the forward and by tokens in the backward)",
             "gemm_tflop_per_step": round(step_flops / 1e12, 3),
             "parallelism": "single GPU",
         },
@@ -679,10 +712,24 @@ def main():
         "mxfp4_gemm": mxfp4_gemm,
         "mxfp4_moe_gemm": mxfp4_moe_gemm,
         "moe_schedules": schedules,
+        "moe_zipf_law_routing": law,
         "moe_tiles": moe_tile_stats(sizes, H, F, torch.cuda.get_device_properties(0).multi_processor_count),
         "linear_small": linear_small,
     }
     print(json.dumps(out))
+
+
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(target_s, X, W, dY, Xm, Wm, dYm, ge, sizes, x4):
@@ -755,6 +802,26 @@ def cpu_baseline(target_s, X, W, dY, Xm, Wm, dYm, ge, sizes, x4):
                 return n, t, 8.0 * xs.size / t / 1e9
             n = min(x4.shape[0], n * 2)
 
+    def linear_small_rate(target):
+        # the small linear forward (X [256x512] rows, W [512x256] columns, the
+        # 256x256x512 GEMM) end to end in the oracle, repeated for about
+        # `target` seconds; ms per forward and TFLOP/s over its 67.1 MFLOP
+        from moe_grouped_gemm_mxq_amd.workloads import linear_small
+        xs, ws = linear_small()
+        xb, wb = bf16_bits(xs), bf16_bits(ws)
+        n, t0 = 0, time.perf_counter()
+        while True:
+            A, sA = oracle.mxfp8_quant_row(xb)
+            B, sB = oracle.mxfp8_quant_colT(wb)
+            oracle.gemm(A, sA, B, sB)
+            n += 1
+            t = time.perf_counter() - t0
+            if t >= target:
+                break
+        ms = 1e3 * t / n
+        return {"ms_per_forward": round(ms, 3), "tflops": round(2.0 * 256 * 256 * 512 / (ms * 1e-3) / 1e12, 6),
+                "reps": n}
+
     def dual_rate():
         # the MXFP8 dual-axis quantisation oracle (row copy + column copy) of
         # the dense X [8192 x 7168] bf16, over the kernel's 4.0625 bytes per
@@ -771,14 +838,16 @@ def cpu_baseline(target_s, X, W, dY, Xm, Wm, dYm, ge, sizes, x4):
     s, t, fl = grow(target_s)
     qn, qt, qgbs = qdq_rate(0.15 * target_s)
     dt, dgbs = dual_rate()
+    c0 = linear_small_rate(0.05 * target_s)
     lib.oracle_set_num_threads(1)
     try:
         s1, t1, fl1 = grow(0.3 * target_s)
         qn1, qt1, qgbs1 = qdq_rate(0.1 * target_s)
+        c01 = linear_small_rate(0.05 * target_s)
     finally:
         lib.oracle_set_num_threads(cores)
     return {"value": round(fl / t / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{s}x{s} outputs of each of the six GEMMs (dense fwd/dgrad/wgrad; MoE fwd/dgrad/wgrad of "
                       f"the largest expert), with the oracle quantising the operand rows they need; "
                       f"{fl / 1e9:.1f} GFLOP in {t:.1f} s",
@@ -789,6 +858,8 @@ def cpu_baseline(target_s, X, W, dY, Xm, Wm, dYm, ge, sizes, x4):
                           "sample": f"first {qn} rows of the 8192x8192 input, 8 bytes per element, {qt:.2f} s",
                           "single_thread": {"value": round(qgbs1, 3), "unit": "GB/s", "cores": 1,
                                             "sample": f"first {qn1} rows, {qt1:.2f} s"}},
+            "linear_small": {"workload": "X 256x512 rows, W 512x256 columns, GEMM 256x256x512 (whole forward)",
+                             "all_cores": {**c0, "cores": cores}, "single_thread": {**c01, "cores": 1}},
             "mxfp8_quantize_dual": {"value": round(dgbs, 3), "unit": "GB/s", "cores": cores,
                                     "sample": f"dense X {X.shape[0]}x{X.shape[1]} bf16, row and column copies, "
                                               f"4.0625 bytes per element, {dt:.2f} s"}}
