@@ -73,8 +73,14 @@ typedef enum {
     MXQ_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misaligned pointer, bad enum */
     MXQ_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement */
     MXQ_ERR_DEVICE = 3,           /* no HIP device, or the current device is not gfx950 */
-    MXQ_ERR_LAUNCH = 4            /* the HIP runtime rejected a kernel launch */
+    MXQ_ERR_LAUNCH = 4,           /* the HIP runtime rejected a kernel launch */
+    MXQ_STATUS_MAX_ENUM = 0x7FFFFFFF
 } mxq_status;
+
+/* Every enum of this header spans the int32 range (its *_MAX_ENUM member), so
+ * a caller passing any int32 value (for instance through a foreign-function
+ * binding) passes a valid value of the type; values outside the listed ones
+ * are rejected with MXQ_ERR_INVALID_ARGUMENT or MXQ_ERR_UNSUPPORTED. */
 
 /* axis bitmask for the quantisers; ROW|COLT is the dual-axis quantisation
  * (both copies from one read of the input). */
@@ -83,12 +89,13 @@ enum { MXQ_AXIS_ROW = 1, MXQ_AXIS_COLT = 2 };
 /* element format of a GEMM operand: E4M3 codes (one byte each, written by
  * the MXFP8 quantisers) or E2M1 codes (two per byte, element 2j in the low
  * nibble of byte j, written by mxq_quantize_fp4) */
-typedef enum { MXQ_FMT_E4M3 = 0, MXQ_FMT_E2M1 = 1 } mxq_fmt;
+typedef enum { MXQ_FMT_E4M3 = 0, MXQ_FMT_E2M1 = 1, MXQ_FMT_MAX_ENUM = 0x7FFFFFFF } mxq_fmt;
 
 /* grouped GEMM modes */
 typedef enum {
     MXQ_GG_RAGGED_M = 0, /* expert forward / input gradient: rows split into groups */
-    MXQ_GG_RAGGED_K = 1  /* expert weight gradient: reduction axis split into groups */
+    MXQ_GG_RAGGED_K = 1, /* expert weight gradient: reduction axis split into groups */
+    MXQ_GG_MAX_ENUM = 0x7FFFFFFF
 } mxq_gg_mode;
 
 /* Version of this ABI (MXQ_ABI_VERSION of the built library). */
