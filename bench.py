@@ -16,8 +16,9 @@ reduction axis only in the forward, along N re-quantised in the backward)
 and a dual schedule that also keeps X's token-axis copy from the forward; the
 dense linear's two schedules; the MoE layer on the Zipf-law routing; the
 MXFP4 QDQ with its saturation mask and the masked (clipped-STE) backward;
-and the MXFP4 GEMMs (operand quantisation, the dense forward shape, and the
-ragged-M MoE forward shape) with E2M1 operands.
+and the MXFP4 GEMMs (operand quantisation, the dense forward shape, the
+ragged-M MoE forward shape and the ragged-K MoE weight gradient) with E2M1
+operands.
 
 Prints one JSON line.  `value` = GEMM FLOPs of the step / step time.
 """
@@ -542,6 +543,40 @@ def main():
                       "gemm_tflops": round(m4_tf, 1), "frac_fp4_peak": round(m4_tf / PEAK_FP4_TFLOPS, 4)}
     del qxm, sxm, qwm, swm
 
+    # The MoE weight gradient with E2M1 operands: the fp32 token rows and dY
+    # quantised along the token axis within each expert group, then the
+    # ragged-K FP4 GEMM into every expert's dW.
+    xmf, dymf = Xm.float(), dYm.float()
+    gx4 = mxq.quantize_fp4_grouped(xmf, ge, ldq)
+    gy4 = mxq.quantize_fp4_grouped(dymf, ge, ldq)
+    wg4_runs = []
+    for i in range(6):
+        tl = Timeline(torch)
+        tl("quant_fp4_token_axis")
+        mxq.mxq_quantize_fp4_grouped(xmf, ge, ldq, gx4["codes"], gx4["scales"])
+        mxq.mxq_quantize_fp4_grouped(dymf, ge, ldq, gy4["codes"], gy4["scales"])
+        tl("gemm_fp4_raggedK")
+        mxq.mxq_grouped_gemm(mxq.MXQ_GG_RAGGED_K, gx4["codes"], gx4["scales"], gy4["codes"], gy4["scales"], mdW, ge,
+                             fmt=mxq.MXQ_FMT_E2M1)
+        tl(None)
+        if i >= 2:
+            wg4_runs.append(tl)
+    torch.cuda.synchronize()
+    dw4 = {}
+    for tl in wg4_runs:
+        for k, v in tl.durations().items():
+            dw4.setdefault(k, []).extend(v)
+    w4_ms = sum(dw4["gemm_fp4_raggedK"]) / len(dw4["gemm_fp4_raggedK"])
+    q4_ms = sum(dw4["quant_fp4_token_axis"]) / len(dw4["quant_fp4_token_axis"])
+    w4_tf = 2.0 * routed * H * F / (w4_ms * 1e-3) / 1e12
+    q4_bytes = T * (H + F) * 4 + padded * (H + F) * (0.5 + 1 / 32)
+    mxfp4_moe_wgrad = {"shape": f"{routed} routed rows, {G} experts, dW {H} x {F} each",
+                       "gemm_ms": round(w4_ms, 4), "gemm_tflops": round(w4_tf, 1),
+                       "frac_fp4_peak": round(w4_tf / PEAK_FP4_TFLOPS, 4), "quant_ms": round(q4_ms, 4),
+                       "quant_gbs": round(q4_bytes / (q4_ms * 1e-3) / 1e9, 1),
+                       "quant_frac_hbm_peak": round(q4_bytes / (q4_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del xmf, dymf, gx4, gy4
+
     # ---------------------------------------------------------------- MoE schedules: time and memory
     schedules = {}
     for sched in ("dual", "fb_split", "dual_x"):
@@ -711,6 +746,7 @@ def main():
         "mxfp4_clipped_ste": fake_quant,
         "mxfp4_gemm": mxfp4_gemm,
         "mxfp4_moe_gemm": mxfp4_moe_gemm,
+        "mxfp4_moe_wgrad": mxfp4_moe_wgrad,
         "moe_schedules": schedules,
         "moe_zipf_law_routing": law,
         "moe_tiles": moe_tile_stats(sizes, H, F, torch.cuda.get_device_properties(0).multi_processor_count),

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 5
+#define MXQ_ABI_VERSION 6
 #define MXQ_BLOCK 32          /* elements per MX block; fixed */
 #define MXQ_MAX_GROUPS 1024   /* largest G the grouped entry points accept */
 /* E4M3 GEMM reductions of at most this many elements (dense and ragged M: K;
@@ -245,6 +245,27 @@ mxq_status mxq_quantize_fp4(const float* x, int64_t rows, int64_t L, float scale
                             uint8_t* scales, hipStream_t st);
 
 /*
+ * Grouped token-axis MXFP4 GEMM operands for the expert weight gradient (the
+ * optional MXFP4 of routed experts, torchao_npu RFC section 3.4, with the
+ * numeric model of the AMCT FakeQuant article, section 2): x fp32 [T][ldx]
+ * (T x C used) on the device, 4-byte aligned; group_end as for
+ * mxq_quantize_grouped.  Blocks of 32 run down the token axis within each
+ * group and restart at each group start; group g occupies padded positions
+ * [P_g, P_g + ceil32(m_g)), P_g = sum_{j<g} ceil32(m_j), its tail zero.  The
+ * block rule and element rounding are mxq_quantize_fp4's (scale_factor 6 by
+ * default, same range).  codes: device bytes [C][ldq/2], 16-byte aligned,
+ * E2M1 nibbles with position 2j in the low nibble of byte j; scales: E8M0
+ * bytes in the GEMM operand layout (C rows, ldq/32 blocks).  Positions at
+ * and past P_G are not written.  ldq % 32 == 0; ldq >= sum_g ceil32(m_g) is
+ * a precondition (mxq_grouped_cols_max(T, G) suffices); blocks past ldq are
+ * dropped.  1 <= G <= MXQ_MAX_GROUPS; T, C >= 1.  The operands of
+ * mxq_grouped_gemm(MXQ_GG_RAGGED_K, .., MXQ_FMT_E2M1).
+ */
+mxq_status mxq_quantize_fp4_grouped(const float* x, int64_t T, int64_t C, int64_t ldx,
+                                    const int32_t* group_end, int32_t G, int64_t ldq, float scale_factor,
+                                    uint8_t* codes, uint8_t* scales, hipStream_t st);
+
+/*
  * Block-scaled GEMM C[m][n] = sum_k deq(A)[m][k] * deq(B)[n][k] (the FP8
  * linear GEMMs of the torchtitan-npu guide, "线性层低精度"), fp32
  * accumulation and fp32 output.  A codes [M][K] + scales (M rows);
@@ -280,9 +301,8 @@ mxq_status mxq_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const
  *     an empty group gets exact zeros.  Expert weight gradient:
  *     A = grouped copy of X (M = hidden), B = grouped copy of dY (N = ffn).
  * fmt MXQ_FMT_E2M1: MXFP4 operands as for mxq_gemm (codes K/2 bytes per row,
- * expert g's B codes at byte g * N * K/2), MXQ_GG_RAGGED_M only (there is no
- * E2M1 token-axis quantiser): MXQ_GG_RAGGED_K with E2M1 gives
- * MXQ_ERR_UNSUPPORTED.
+ * expert g's B codes at byte g * N * K/2); for MXQ_GG_RAGGED_K the grouped
+ * token-axis copies of mxq_quantize_fp4_grouped (K = their ldq).
  * M, N >= 1; K >= 32, K % 32 == 0; 1 <= G <= MXQ_MAX_GROUPS.  A, B 16-byte
  * aligned, sA, sB and C 4-byte aligned (else MXQ_ERR_INVALID_ARGUMENT).
  */

@@ -478,10 +478,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
       }
       order[rank] = g;
     }
-    // experts with more than kIlvMaxK tokens come first in `order`
+    // experts with more than kIlvMaxK tokens come first in `order` (E2M1:
+    // every expert takes the plain loop)
     static_assert(2 * kThreads >= kMaxGroups, "two groups per thread");
-    const int n_long = __syncthreads_count(t < G && gt.size[t] > kIlvMaxK) +
-                       __syncthreads_count(t + kThreads < G && gt.size[t + kThreads] > kIlvMaxK);
+    const int n_long = KIND != kE4M3 ? G
+                                     : __syncthreads_count(t < G && gt.size[t] > kIlvMaxK) +
+                                           __syncthreads_count(t + kThreads < G && gt.size[t + kThreads] > kIlvMaxK);
     kbp = kb;
     orderp = order;
     first_g = ILV ? n_long : 0;
@@ -781,16 +783,15 @@ hipError_t launch_gemm_kind(int mode, const uint8_t* A, const uint8_t* sA, const
     launch_mode<kRaggedM, KIND>(K <= kIlvMaxK, (unsigned)grid, st, A, sA, B, sB, C, M, N, K, ldc, group_end, G,
                                 (int)tiles_m, (int)tiles_n);
   } else {
-    if constexpr (KIND != kE4M3) {
-      return hipErrorInvalidValue;  // no E2M1 token-axis operands
-    } else {
-      const int64_t total = (int64_t)G * tiles_m * tiles_n;
-      if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-      const int64_t grid = total < cus ? total : cus;
-      // experts with more than kIlvMaxK tokens, then the others (each launch
-      // finds its experts from group_end on the device)
-      launch_mode<kRaggedK, KIND>(false, (unsigned)grid, st, A, sA, B, sB, C, M, N, K, N, group_end, G,
-                                  (int)tiles_m, (int)tiles_n);
+    const int64_t total = (int64_t)G * tiles_m * tiles_n;
+    if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const int64_t grid = total < cus ? total : cus;
+    // E4M3: experts with more than kIlvMaxK tokens, then the others (each
+    // launch finds its experts from group_end on the device); E2M1: one
+    // launch for all experts
+    launch_mode<kRaggedK, KIND>(false, (unsigned)grid, st, A, sA, B, sB, C, M, N, K, N, group_end, G,
+                                (int)tiles_m, (int)tiles_n);
+    if (KIND == kE4M3) {
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       launch_mode<kRaggedK, KIND>(true, (unsigned)grid, st, A, sA, B, sB, C, M, N, K, N, group_end, G,
@@ -804,7 +805,6 @@ hipError_t launch_gemm(int mode, bool fp4, const uint8_t* A, const uint8_t* sA, 
                        const uint8_t* sB, float* C, int64_t M, int64_t N, int64_t K, int64_t ldc,
                        const int32_t* group_end, int32_t G, hipStream_t st) {
   if (!fp4) return launch_gemm_kind<kE4M3>(mode, A, sA, B, sB, C, M, N, K, ldc, group_end, G, st);
-  if (mode == kRaggedK) return hipErrorInvalidValue;  // no E2M1 token-axis operands
   return launch_gemm_kind<kE2M1>(mode, A, sA, B, sB, C, M, N, K, ldc, group_end, G, st);
 }
 

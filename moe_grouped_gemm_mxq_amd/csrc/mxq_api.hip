@@ -250,6 +250,28 @@ mxq_status mxq_quantize_fp4(const float* x, int64_t rows, int64_t L, float scale
   return launched(launch_qdq_fp4(x, nullptr, rows, L, F, T, codes, scales, nullptr, st, true), "mxq_quantize_fp4");
 }
 
+mxq_status mxq_quantize_fp4_grouped(const float* x, int64_t T, int64_t C, int64_t ldx, const int32_t* group_end,
+                                    int32_t G, int64_t ldq, float scale_factor, uint8_t* codes, uint8_t* scales,
+                                    hipStream_t st) {
+  MXQ_REQUIRE(x && group_end && codes && scales, "mxq_quantize_fp4_grouped: NULL pointer");
+  MXQ_REQUIRE(T >= 1 && C >= 1, "mxq_quantize_fp4_grouped: T and C must be >= 1");
+  MXQ_REQUIRE(T <= INT32_MAX, "mxq_quantize_fp4_grouped: T must be < 2^31 (group ends are int32)");
+  MXQ_REQUIRE(ldx >= C, "mxq_quantize_fp4_grouped: ldx < C");
+  MXQ_REQUIRE(G >= 1 && G <= MXQ_MAX_GROUPS, "mxq_quantize_fp4_grouped: G must be in [1, %d] (got %d)",
+              MXQ_MAX_GROUPS, G);
+  MXQ_REQUIRE(ldq >= 32 && ldq % 32 == 0, "mxq_quantize_fp4_grouped: ldq must be a positive multiple of 32");
+  MXQ_REQUIRE(((uintptr_t)x & 3u) == 0, "mxq_quantize_fp4_grouped: x must be 4-byte aligned");
+  MXQ_REQUIRE(aligned16(codes), "mxq_quantize_fp4_grouped: codes must be 16-byte aligned");
+  int F;
+  uint32_t Tth;
+  MXQ_REQUIRE(fp4_scale_params(scale_factor, &F, &Tth),
+              "mxq_quantize_fp4_grouped: scale_factor must be a normal fp32 value in [2^-64, 2^64) (got %g)",
+              (double)scale_factor);
+  MXQ_REQUIRE_DEVICE();
+  return launched(launch_quant_fp4_grouped(x, T, C, ldx, group_end, G, ldq, F, Tth, codes, scales, st),
+                  "mxq_quantize_fp4_grouped");
+}
+
 mxq_status mxq_ste_backward_fp4(const float* grad_y, const uint8_t* sat_mask, float* grad_x,
                                 int64_t rows, int64_t L, hipStream_t st) {
   MXQ_REQUIRE(grad_y && sat_mask && grad_x, "mxq_ste_backward_fp4: NULL operand");
@@ -303,8 +325,6 @@ mxq_status mxq_grouped_gemm(mxq_gg_mode mode, const uint8_t* A, const uint8_t* s
               "mxq_grouped_gemm: sA, sB must be 4-byte aligned (the kernel reads scale dwords)");
   if (fmt != MXQ_FMT_E4M3 && fmt != MXQ_FMT_E2M1)
     return fail(MXQ_ERR_UNSUPPORTED, "mxq_grouped_gemm: unknown operand format %d", (int)fmt);
-  if (fmt == MXQ_FMT_E2M1 && mode == MXQ_GG_RAGGED_K)
-    return fail(MXQ_ERR_UNSUPPORTED, "mxq_grouped_gemm: MXQ_FMT_E2M1 operands are implemented for MXQ_GG_RAGGED_M only");
   MXQ_REQUIRE_DEVICE();
   return launched(launch_gemm(mode == MXQ_GG_RAGGED_M ? 1 : 2, fmt == MXQ_FMT_E2M1, A, sA, B, sB, C, M, N, K, N,
                               group_end, G, st),

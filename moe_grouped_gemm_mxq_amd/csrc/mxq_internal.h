@@ -41,9 +41,14 @@ hipError_t launch_qdq_fp4(const float* x, float* y, int64_t rows, int64_t L, int
                           bool operand_layout = false);
 hipError_t launch_ste_backward_fp4(const float* grad_y, const uint8_t* sat_mask, float* grad_x,
                                    int64_t rows, int64_t L, hipStream_t st);
+// MXFP4 grouped token-axis GEMM operand: x fp32 [T][ldx] -> codes [C][ldq/2],
+// scales (C rows, ldq/32 blocks, operand layout); (F, Tth) as for launch_qdq_fp4.
+hipError_t launch_quant_fp4_grouped(const float* x, int64_t T, int64_t C, int64_t ldx, const int32_t* group_end,
+                                    int32_t G, int64_t ldq, int F, uint32_t Tth, uint8_t* codes, uint8_t* scales,
+                                    hipStream_t st);
 
-// Block-scaled GEMMs.  mode 0: dense (G = 1, no group_end); 1: ragged M; 2: ragged K
-// (E4M3 only).  fp4: E2M1 codes (two per byte) instead of E4M3.
+// Block-scaled GEMMs.  mode 0: dense (G = 1, no group_end); 1: ragged M; 2: ragged K.
+// fp4: E2M1 codes (two per byte) instead of E4M3.
 hipError_t launch_gemm(int mode, bool fp4, const uint8_t* A, const uint8_t* sA, const uint8_t* B,
                        const uint8_t* sB, float* C, int64_t M, int64_t N, int64_t K, int64_t ldc,
                        const int32_t* group_end, int32_t G, hipStream_t st);

@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include "mxq_device.h"
+#include "mxq_groups.h"
 #include "mxq_internal.h"
 
 namespace mxq {
@@ -161,6 +162,110 @@ __global__ __launch_bounds__(kThreads) void ste_rows_kernel(const float* gy, con
   }
 }
 
+// ------------------------------------------------------------------ grouped token axis
+// MXFP4 GEMM operands of the expert weight gradient: blocks of 32 run down
+// the token axis of x [T][C] within each group (the same block rule and
+// element rounding as the QDQ above), group g's tokens at padded positions
+// [P_g, P_g + ceil32(m_g)) of output row c = column c of x.  A workgroup
+// takes 256 padded positions (8 blocks) x 32 columns: it loads the 256 fp32
+// rows' 128-byte pieces into LDS, then each thread quantises one column over
+// one block (32 values down the column) and stores its 16 code bytes; the
+// eight blocks of a column make one 128-byte code line.  Tile rows are
+// stored with one spare row per 32 (row r at r + r/32), so the two blocks a
+// wave reads at once sit in opposite halves of the LDS banks.
+constexpr int kTokTile = 256, kColTile = 32;
+constexpr int kTokRows = kTokTile + kTokTile / 32;
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void quant_fp4_grouped_kernel(
+    const float* __restrict__ x, int64_t T, int64_t C, int64_t ldx, const int32_t* __restrict__ group_end,
+    int32_t G, int64_t ldq, int n_col_tiles, Fp4Scale p, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales) {
+  __shared__ __attribute__((aligned(16))) float tile[kTokRows * kColTile];
+  __shared__ int32_t bstart[kMaxGroups + 1];
+  __shared__ int64_t rb_src[kTokTile / 32];   // first source row of each block of the tile
+  __shared__ int32_t rb_valid[kTokTile / 32]; // its valid rows (0: no output block)
+  static_assert(kThreads * sizeof(int64_t) <= sizeof(tile), "the group scan's scratch reuses the tile");
+  const int t = threadIdx.x;
+  const int rt = blockIdx.x / n_col_tiles;
+  const int ct = blockIdx.x - rt * n_col_tiles;
+  const int64_t p0 = (int64_t)rt * kTokTile;  // first padded position of the tile
+  const int64_t c0 = (int64_t)ct * kColTile;
+  build_block_starts<kThreads>(group_end, G, T, 32, nullptr, nullptr, bstart, reinterpret_cast<int64_t*>(tile));
+  if (t < kTokTile / 32) {
+    const int64_t pb = p0 / 32 + t;
+    int64_t src = 0;
+    int32_t valid = 0;
+    if (pb < bstart[G] && (pb + 1) * 32 <= ldq) {
+      const int g = find_block_group(bstart, G, (int32_t)pb);
+      int32_t gstart, gsize;
+      group_span(group_end, g, T, gstart, gsize);
+      // (bstart is non-decreasing and bstart[g] <= pb < bstart[g] + ceil32(gsize) / 32)
+      const int64_t off = (pb - bstart[g]) * 32;
+      src = (int64_t)gstart + off;
+      valid = (int32_t)min<int64_t>(32, gsize - off);
+    }
+    rb_src[t] = src;
+    rb_valid[t] = valid;
+  }
+  __syncthreads();
+  if (rb_valid[0] <= 0) return;  // the tile lies past the last block (uniform)
+
+  // ---- load: eight 16-byte pieces per thread, rows (t / 8) + 32 i, columns 4 (t % 8) ..
+  const int cq = t & 7;
+  const int64_t col4 = c0 + 4 * cq;
+  float4 w[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int lr = (t >> 3) + 32 * i;
+    const int rb = lr >> 5;
+    const bool row_ok = (lr & 31) < rb_valid[rb];
+    const float* xr = x + (row_ok ? rb_src[rb] + (lr & 31) : 0) * ldx;
+    w[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row_ok) {
+      if (VEC && col4 + 4 <= C) {
+        w[i] = *reinterpret_cast<const float4*>(xr + col4);
+      } else {
+        if (col4 < C) w[i].x = xr[col4];
+        if (col4 + 1 < C) w[i].y = xr[col4 + 1];
+        if (col4 + 2 < C) w[i].z = xr[col4 + 2];
+        if (col4 + 3 < C) w[i].w = xr[col4 + 3];
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int lr = (t >> 3) + 32 * i;
+    *reinterpret_cast<float4*>(tile + (lr + (lr >> 5)) * kColTile + 4 * cq) = w[i];
+  }
+  __syncthreads();
+
+  // ---- one column over one block per thread
+  const int blk = t >> 5, col = t & 31;
+  uint32_t v[32];
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 32; i++) {
+    const int lr = blk * 32 + i;
+    v[i] = __float_as_uint(tile[(lr + blk) * kColTile + col]);
+    amax = max(amax, v[i] & 0x7FFFFFFFu);
+  }
+  const int e = mxfp4_scale_exp(amax, p);
+  uint32_t nib[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 32; i++) {
+    const uint32_t sign = v[i] & 0x80000000u;
+    const float yabs = __builtin_amdgcn_ldexpf(__uint_as_float(v[i] & 0x7FFFFFFFu), -e);
+    nib[i >> 3] |= ((sign >> 28) | mxfp4_index(yabs)) << (4 * (i & 7));
+  }
+  const int64_t cg = c0 + col;
+  if (rb_valid[blk] > 0 && cg < C) {
+    const int64_t pos = p0 + 32 * blk;  // padded position of the block
+    *reinterpret_cast<uint4*>(codes + cg * (ldq / 2) + pos / 2) = make_uint4(nib[0], nib[1], nib[2], nib[3]);
+    scales[scale_offset(cg, pos / 32, ldq / 32)] = (uint8_t)(e + 127);
+  }
+}
+
 // One chunk per thread and one workgroup per 256 chunks (4 KB of fp32),
 // capped only by the grid-size limit: measured on MI355X, many short
 // workgroups over contiguous chunks stream HBM faster (a plain copy:
@@ -204,6 +309,24 @@ hipError_t launch_qdq_fp4(const float* x, float* y, int64_t rows, int64_t L, int
                                                              operand_layout ? L / 32 : 0);
   else
     qdq_rows_kernel<<<grid_for(n_chunks), kThreads, 0, st>>>(x, y, rows, L, p, codes, scales, mask, operand_layout);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_fp4_grouped(const float* x, int64_t T, int64_t C, int64_t ldx, const int32_t* group_end,
+                                    int32_t G, int64_t ldq, int F, uint32_t Tth, uint8_t* codes, uint8_t* scales,
+                                    hipStream_t st) {
+  const Fp4Scale p{F, Tth};
+  const int64_t n_row_tiles = (T + 31 * (int64_t)G + kTokTile - 1) / kTokTile;
+  const int n_col_tiles = (int)((C + kColTile - 1) / kColTile);
+  const int64_t grid = n_row_tiles * n_col_tiles;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const bool vec = ldx % 4 == 0 && (uintptr_t)x % 16 == 0;
+  if (vec)
+    quant_fp4_grouped_kernel<true><<<(unsigned)grid, kThreads, 0, st>>>(x, T, C, ldx, group_end, G, ldq, n_col_tiles,
+                                                                         p, codes, scales);
+  else
+    quant_fp4_grouped_kernel<false><<<(unsigned)grid, kThreads, 0, st>>>(x, T, C, ldx, group_end, G, ldq,
+                                                                          n_col_tiles, p, codes, scales);
   return hipGetLastError();
 }
 

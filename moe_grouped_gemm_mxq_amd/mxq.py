@@ -46,7 +46,7 @@ EXPORTED = [
     "mxq_abi_version", "mxq_last_error", "mxq_device_check", "mxq_grouped_cols_max", "mxq_operand_sizes",
     "mxq_quantize", "mxq_quantize_batched", "mxq_quantize_grouped", "mxq_qdq_fp4", "mxq_qdq_fp4_ex",
     "mxq_ste_backward_fp4", "mxq_fp4_scale_threshold", "mxq_quantize_fp4", "mxq_gemm", "mxq_grouped_gemm",
-    "mxq_validate_group_end",
+    "mxq_validate_group_end", "mxq_quantize_fp4_grouped",
 ]
 
 
@@ -74,6 +74,7 @@ def _load(path: str = LIB_PATH):
         "mxq_gemm": ([P, P, P, P, P, I64, I64, I64, I64, I, P], I),
         "mxq_grouped_gemm": ([I, P, P, P, P, P, I64, I64, I64, P, I32, I, P], I),
         "mxq_validate_group_end": ([P, I32, I64, P, P], I),
+        "mxq_quantize_fp4_grouped": ([P, I64, I64, I64, P, I32, I64, ctypes.c_float, P, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -82,7 +83,7 @@ def _load(path: str = LIB_PATH):
     return lib
 
 
-ABI_VERSION = 5  # MXQ_ABI_VERSION of include/mxq.h this binding is written against
+ABI_VERSION = 6  # MXQ_ABI_VERSION of include/mxq.h this binding is written against
 
 _lib = _load()
 if _lib.mxq_abi_version() != ABI_VERSION:
@@ -337,6 +338,21 @@ def mxq_quantize_fp4(x, codes, scales, scale_factor=6.0, stream=None):
                                  _stream(stream, x.device)), "mxq_quantize_fp4")
 
 
+def mxq_quantize_fp4_grouped(x, group_end, ldq, codes, scales, scale_factor=6.0, stream=None):
+    """Grouped token-axis MXFP4 operand: x fp32 [T][C] (unit column stride) ->
+    codes uint8 [C][ldq/2], scales scale_shape(C, ldq/32) (the operand layout)."""
+    _need(x, torch.float32, "x", 2)
+    _need(group_end, torch.int32, "group_end", 1)
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit stride along its last dim")
+    T, C = x.shape
+    _need_u8(codes, "codes", (C, ldq // 2))
+    _need_u8(scales, "scales", scale_shape(C, ldq // BLOCK))
+    _check(_lib.mxq_quantize_fp4_grouped(_ptr(x), T, C, x.stride(0), _ptr(group_end), group_end.numel(), ldq,
+                                         float(scale_factor), _ptr(codes), _ptr(scales), _stream(stream, x.device)),
+           "mxq_quantize_fp4_grouped")
+
+
 def mxq_validate_group_end(group_end, T, flag, stream=None):
     _need(group_end, torch.int32, "group_end", 1)
     _need(flag, torch.int32, "flag")
@@ -414,6 +430,16 @@ def quantize_fp4(x, scale_factor=6.0, stream=None):
     scales = _u8(scale_shape(rows, ceil32(L) // BLOCK), x.device)
     mxq_quantize_fp4(x, codes, scales, scale_factor, stream)
     return codes, scales
+
+
+def quantize_fp4_grouped(x, group_end, ldq=None, scale_factor=6.0, stream=None):
+    """Grouped token-axis MXFP4 operand of x fp32 [T][C]: {"ldq", "codes", "scales"}."""
+    T, C = x.shape
+    if ldq is None:
+        ldq = mxq_grouped_cols_max(T, group_end.numel())
+    out = {"ldq": ldq, "codes": _u8((C, ldq // 2), x.device), "scales": _u8(scale_shape(C, ldq // BLOCK), x.device)}
+    mxq_quantize_fp4_grouped(x, group_end, ldq, out["codes"], out["scales"], scale_factor, stream)
+    return out
 
 
 def qdq_fp4_ste(x, scale_factor=6.0, want_codes=False, stream=None):

@@ -280,6 +280,32 @@ def gemm_fp4_sampled(A, sA, B, sB, mi, ni):
     return C, Cabs
 
 
+def mxfp4_quant_grouped_colT(x: np.ndarray, group_end, ldq: int, scale_factor: float = 6.0):
+    """MXFP4 blocks down the token axis of x fp32 [T][C] within each group
+    (the weight-gradient operands of the MXFP4 expert GEMMs): group g's rows,
+    transposed to [C][m_g], go through the MXFP4 quantiser above (row padding =
+    the group's zero tail), and land at padded positions [P_g, P_g +
+    ceil32(m_g)).  Returns codes [C][ldq/2] and row-major scales [C][ldq/32];
+    positions at and past P_G are zero."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    T, C = x.shape
+    ge = np.asarray(group_end, dtype=np.int64)
+    assert ldq % BLOCK == 0 and grouped_cols(ge) <= ldq
+    codes = np.zeros((C, ldq // 2), np.uint8)
+    scales = np.zeros((C, ldq // BLOCK), np.uint8)
+    start, P = 0, 0
+    for e in ge.tolist():
+        assert start <= e <= T, "group ends must be non-decreasing and <= T"
+        m = e - start
+        if m:
+            _, cg, sg, _ = mxfp4_qdq_ex(np.ascontiguousarray(x[start:e].T), scale_factor)
+            codes[:, P // 2:(P + ceil32(m)) // 2] = cg
+            scales[:, P // BLOCK:(P + ceil32(m)) // BLOCK] = sg
+        P += ceil32(m)
+        start = e
+    return codes, scales
+
+
 # ---------------------------------------------------------------- GEMMs
 def gemm_dequantised(a: np.ndarray, b: np.ndarray):
     """C = a b^T and sum_k |a_k b_k| = |a| |b|^T for operands already

@@ -107,6 +107,12 @@ int main() {
   EXPECT(mxq_quantize_fp4(f32, 2, 33, 6.0f, nullptr, p, nullptr), INV);
   EXPECT(mxq_quantize_fp4(f32, 2, 33, 1e-30f, p, p, nullptr), INV);
   EXPECT(mxq_quantize_fp4(f32, 2, 33, 6.0f, p, p, nullptr), DEV);
+  EXPECT(mxq_quantize_fp4_grouped(nullptr, 64, 8, 8, ge, 2, 128, 6.0f, p, p, nullptr), INV);
+  EXPECT(mxq_quantize_fp4_grouped(f32, 64, 8, 8, ge, 2, 100, 6.0f, p, p, nullptr), INV);
+  EXPECT(mxq_quantize_fp4_grouped(f32, 64, 8, 8, ge, 2, 128, 6.0f, p + 8, p, nullptr), INV);
+  EXPECT(mxq_quantize_fp4_grouped(f32, 64, 8, 8, ge, 2, 128, -1.0f, p, p, nullptr), INV);
+  EXPECT(mxq_quantize_fp4_grouped(f32, (int64_t)1 << 31, 8, 8, ge, 2, 128, 6.0f, p, p, nullptr), INV);
+  EXPECT(mxq_quantize_fp4_grouped(f32, 64, 8, 8, ge, 2, 128, 6.0f, p, p, nullptr), DEV);
   EXPECT(mxq_ste_backward_fp4(f32, p, f32 + 1, 2, 33, nullptr), INV);
   EXPECT(mxq_ste_backward_fp4(f32, p, f32, 2, 33, nullptr), DEV);
   // GEMMs
@@ -123,6 +129,7 @@ int main() {
   EXPECT(mxq_grouped_gemm(MXQ_GG_RAGGED_M, p, p, p, p, f32, 4, 4, 32, nullptr, 2, MXQ_FMT_E4M3, nullptr), INV);
   EXPECT(mxq_grouped_gemm(MXQ_GG_RAGGED_K, p, p, p, p, f32, 4, 4, 32, ge, 2, MXQ_FMT_E4M3, nullptr), DEV);
   EXPECT(mxq_grouped_gemm(MXQ_GG_RAGGED_M, p, p, p, p, f32, 4, 4, 32, ge, 2, MXQ_FMT_E2M1, nullptr), DEV);
+  EXPECT(mxq_grouped_gemm(MXQ_GG_RAGGED_K, p, p, p, p, f32, 4, 4, 32, ge, 2, MXQ_FMT_E2M1, nullptr), DEV);
   EXPECT(mxq_validate_group_end(ge, 0, 10, ge, nullptr), INV);
   EXPECT(mxq_validate_group_end(ge, 2, -1, ge, nullptr), INV);
   EXPECT(mxq_validate_group_end(ge, 2, 10, ge, nullptr), DEV);

@@ -154,10 +154,17 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
         assert call(lib, "mxq_qdq_fp4_ex", FAKE, FAKE, I64(2), I64(64), F32(sf), P(0), P(0), P(0), P(0)) == 1
     assert "scale_factor" in err(lib)
     assert call(lib, "mxq_qdq_fp4_ex", FAKE, FAKE, I64(2), I64(64), F32(6.0), P(0), P(0), P(0x1002), P(0)) == 1
-    # E2M1 operands: ragged K is not offered
-    assert call(lib, "mxq_grouped_gemm", 1, FAKE, FAKE, FAKE, FAKE, FAKE, I64(4), I64(4), I64(64), FAKE,
-                ctypes.c_int32(2), 1, P(0)) == 2
-    assert "RAGGED_M only" in err(lib)
+    # grouped token-axis MXFP4 operands: NULL, bad ldq, misaligned codes, bad factor, T >= 2^31
+    assert call(lib, "mxq_quantize_fp4_grouped", P(0), I64(64), I64(8), I64(8), FAKE, ctypes.c_int32(2), I64(128),
+                F32(6.0), FAKE, FAKE, P(0)) == 1
+    assert call(lib, "mxq_quantize_fp4_grouped", FAKE, I64(64), I64(8), I64(8), FAKE, ctypes.c_int32(2), I64(100),
+                F32(6.0), FAKE, FAKE, P(0)) == 1
+    assert call(lib, "mxq_quantize_fp4_grouped", FAKE, I64(64), I64(8), I64(8), FAKE, ctypes.c_int32(2), I64(128),
+                F32(6.0), P(0x1008), FAKE, P(0)) == 1
+    assert call(lib, "mxq_quantize_fp4_grouped", FAKE, I64(64), I64(8), I64(8), FAKE, ctypes.c_int32(2), I64(128),
+                F32(0.0), FAKE, FAKE, P(0)) == 1
+    assert call(lib, "mxq_quantize_fp4_grouped", FAKE, I64(2 ** 31), I64(8), I64(8), FAKE, ctypes.c_int32(2),
+                I64(128), F32(6.0), FAKE, FAKE, P(0)) == 1
     assert call(lib, "mxq_quantize_fp4", FAKE, I64(2), I64(64), F32(6.0), P(0x1008), FAKE, P(0)) == 1
     # STE backward: NULL mask, partial overlap of grad_x and grad_y
     assert call(lib, "mxq_ste_backward_fp4", FAKE, P(0), FAKE, I64(2), I64(64), P(0)) == 1
@@ -177,6 +184,12 @@ def test_valid_call_without_gfx950_reports_device_error(lib):
     assert call(lib, "mxq_device_check", 0) == 3
     assert call(lib, "mxq_quantize", FAKE, I64(4), I64(32), I64(32), 1, FAKE, FAKE, P(0), P(0), P(0)) == 3
     assert err(lib)
+    # E2M1 operands in both grouped modes and the grouped token-axis MXFP4
+    # quantiser: well-formed, so they stop at the device gate
+    assert call(lib, "mxq_grouped_gemm", 1, FAKE, FAKE, FAKE, FAKE, FAKE, I64(4), I64(4), I64(64), FAKE,
+                ctypes.c_int32(2), 1, P(0)) == 3
+    assert call(lib, "mxq_quantize_fp4_grouped", FAKE, I64(64), I64(8), I64(8), FAKE, ctypes.c_int32(2), I64(128),
+                ctypes.c_float(6.0), FAKE, FAKE, P(0)) == 3
 
 
 def test_binding_fails_loudly_without_the_library(tmp_path):

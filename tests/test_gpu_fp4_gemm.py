@@ -110,3 +110,103 @@ def test_grouped_gemm_fp4_ragged_m(sizes, K):
             assert_gemm_close(got[start:start + s], Cr, Ca, f"fp4 ragged M group {g}")
         start += s
     assert np.all(got[T:] == 3.0)
+
+
+# ------------------------------------------------------------------ grouped token axis (expert weight gradient)
+def grouped_fp4_case(sizes, C, seed, sf=6.0):
+    m = mxq()
+    T = sum(sizes)
+    x = fp4_inputs((T, C), seed)
+    ge_np = np.cumsum(sizes).astype(np.int32)
+    ge = torch.from_numpy(ge_np).cuda()
+    q = m.quantize_fp4_grouped(x.cuda(), ge, scale_factor=sf)
+    torch.cuda.synchronize()
+    rc, rs = oracle.mxfp4_quant_grouped_colT(x.numpy(), ge_np, q["ldq"], sf)
+    return q, rc, rs, ge_np
+
+
+@pytest.mark.parametrize("sizes,C,sf", [([5, 0, 33, 1, 257, 64], 70, 6.0), ([0, 0, 300], 32, 6.0),
+                                        ([1], 1, 6.0), ([31, 32, 33, 0, 513], 200, 5.0),
+                                        ([0, 31, 0, 32, 0, 33, 512, 0], 96, 7.25)])
+def test_quantize_fp4_grouped_bitexact(sizes, C, sf):
+    q, rc, rs, ge_np = grouped_fp4_case(sizes, C, sum(sizes) + C, sf)
+    P = oracle.grouped_cols(ge_np)
+    assert np.array_equal(host(q["codes"])[:, :P // 2], rc[:, :P // 2])
+    assert np.array_equal(unpack_scales(q["scales"], C)[:, :P // 32], rs[:, :P // 32])
+
+
+def test_quantize_fp4_grouped_unaligned_input():
+    """A row pitch that is not a multiple of 4 floats takes the scalar loads."""
+    m = mxq()
+    sizes, C = [40, 0, 77], 45
+    T = sum(sizes)
+    x = fp4_inputs((T, C), 3)
+    base = torch.zeros((T, C + 1), device="cuda")
+    base[:, :C] = x.cuda()
+    ge_np = np.cumsum(sizes).astype(np.int32)
+    q = m.quantize_fp4_grouped(base[:, :C], torch.from_numpy(ge_np).cuda())
+    torch.cuda.synchronize()
+    rc, rs = oracle.mxfp4_quant_grouped_colT(x.numpy(), ge_np, q["ldq"])
+    P = oracle.grouped_cols(ge_np)
+    assert np.array_equal(host(q["codes"])[:, :P // 2], rc[:, :P // 2])
+    assert np.array_equal(unpack_scales(q["scales"], C)[:, :P // 32], rs[:, :P // 32])
+
+
+def check_fp4_wgrad(dW, xc, xs, yc, ys, ge_np, what):
+    """Every output of every expert against the oracle's fp64 product of the
+    dequantised codes; empty experts exact zeros."""
+    start, P = 0, 0
+    for g, e in enumerate(np.asarray(ge_np).tolist()):
+        w = oracle.ceil32(e - start)
+        if w == 0:
+            assert not dW[g].any(), f"{what}: empty expert {g} has nonzero dW"
+        else:
+            a = oracle.mxfp4_dequant(np.ascontiguousarray(xc[:, P // 2:(P + w) // 2]),
+                                     np.ascontiguousarray(xs[:, P // 32:(P + w) // 32]), w)
+            b = oracle.mxfp4_dequant(np.ascontiguousarray(yc[:, P // 2:(P + w) // 2]),
+                                     np.ascontiguousarray(ys[:, P // 32:(P + w) // 32]), w)
+            Cr, Ca = oracle.gemm_dequantised(a, b)
+            assert_gemm_close(dW[g], Cr, Ca, f"{what} expert {g} ({e - start} tokens)")
+        P += w
+        start = e
+
+
+@pytest.mark.parametrize("sizes", [[5, 0, 33, 1, 257, 64], [0, 0, 300], [513, 4, 1024, 0, 1500], [1]])
+def test_grouped_gemm_fp4_ragged_k(sizes):
+    m = mxq()
+    qx, xc, xs, ge_np = grouped_fp4_case(sizes, 70, sum(sizes) + 1)
+    qy, yc, ys, _ = grouped_fp4_case(sizes, 90, sum(sizes) + 2)
+    ge = torch.from_numpy(ge_np).cuda()
+    dW = m.grouped_gemm(m.MXQ_GG_RAGGED_K, qx["codes"], qx["scales"], qy["codes"], qy["scales"], ge,
+                        fmt=m.MXQ_FMT_E2M1)
+    torch.cuda.synchronize()
+    check_fp4_wgrad(host(dW), xc, xs, yc, ys, ge_np, f"fp4 ragged K {sizes}")
+
+
+def test_grouped_gemm_fp4_ragged_k_moe_every_output():
+    """The MoE weight-gradient shape in MXFP4: fp32 token rows X [131072x7168]
+    and dY [131072x4096], N(0,1), grouped by the frozen Zipf(1.1) routing;
+    every output of all 32 experts' dW [7168x4096]."""
+    from moe_grouped_gemm_mxq_amd import workloads
+    m = mxq()
+    sizes = workloads.moe_group_sizes()
+    ge_np = np.cumsum(sizes).astype(np.int32)
+    ge = torch.from_numpy(ge_np).cuda()
+    g = torch.Generator(device="cuda").manual_seed(3)
+    T = int(ge_np[-1])
+    X = torch.randn(T, 7168, generator=g, device="cuda")
+    dY = torch.randn(T, 4096, generator=g, device="cuda")
+    qx = m.quantize_fp4_grouped(X, ge)
+    qy = m.quantize_fp4_grouped(dY, ge, ldq=qx["ldq"])
+    dW = m.grouped_gemm(m.MXQ_GG_RAGGED_K, qx["codes"], qx["scales"], qy["codes"], qy["scales"], ge,
+                        fmt=m.MXQ_FMT_E2M1)
+    torch.cuda.synchronize()
+    P = oracle.grouped_cols(ge_np)
+    xc, xs = oracle.mxfp4_quant_grouped_colT(host(X), ge_np, qx["ldq"])
+    assert np.array_equal(host(qx["codes"])[:, :P // 2], xc[:, :P // 2])
+    assert np.array_equal(unpack_scales(qx["scales"], 7168)[:, :P // 32], xs[:, :P // 32])
+    del X
+    yc, ys = oracle.mxfp4_quant_grouped_colT(host(dY), ge_np, qx["ldq"])
+    assert np.array_equal(host(qy["codes"])[:, :P // 2], yc[:, :P // 2])
+    del dY
+    check_fp4_wgrad(host(dW), xc, xs, yc, ys, ge_np, "fp4 moe wgrad")

@@ -71,3 +71,39 @@ def test_gemm_fp4_sampled_equals_full():
     mi = np.array([0, 8, 3, 5, 8]); ni = np.array([0, 10, 7, 2, 0])
     Cs, Cas = oracle.gemm_fp4_sampled(ca, sa, cb, sb, mi, ni)
     assert np.allclose(Cs, C[mi, ni], rtol=1e-13, atol=0) and np.allclose(Cas, Cabs[mi, ni], rtol=1e-13, atol=0)
+
+
+def test_grouped_token_axis_fp4_operand():
+    """The grouped token-axis MXFP4 operand: one group is the QDQ of the
+    transpose; groups restart their blocks (a group's codes do not depend on
+    its neighbours' tokens); tails and unused positions are zero codes; the
+    dequantised operand reproduces the QDQ of each group's transposed rows."""
+    rng = np.random.default_rng(5)
+    T, C = 90, 40
+    x = (rng.standard_normal((T, C)) * np.exp2(rng.integers(-6, 6, (T, 1)))).astype(np.float32)
+    ge = np.array([0, 33, 33, 70, 90], np.int32)
+    ldq = 224
+    codes, scales = oracle.mxfp4_quant_grouped_colT(x, ge, ldq)
+    # one group: the QDQ of the transpose
+    c1, s1 = oracle.mxfp4_quant_grouped_colT(x, np.array([T], np.int32), 96)
+    _, cr, sr, _ = oracle.mxfp4_qdq_ex(np.ascontiguousarray(x.T))
+    assert np.array_equal(c1, cr) and np.array_equal(s1, sr)
+    # sizes 0, 33, 0, 37, 20: padded positions [0, 64), [64, 128), [128, 160)
+    # group 3 (rows 33..70) alone gives the same bytes as inside the grouped copy
+    P2 = 64
+    cg, sg = oracle.mxfp4_quant_grouped_colT(np.ascontiguousarray(x[33:70]), np.array([37], np.int32), 64)
+    assert np.array_equal(codes[:, P2 // 2:(P2 + 64) // 2], cg[:, :32])
+    assert np.array_equal(scales[:, P2 // 32:(P2 + 64) // 32], sg[:, :2])
+    # padding: group 1 (33 tokens) occupies 64 positions, its last 31 are zero codes
+    assert not codes[:, 33 // 2 + 1:64 // 2].any() and not (codes[:, 16] >> 4).any()
+    assert not codes[:, 160 // 2:].any() and not scales[:, 160 // 32:].any()
+    # dequantised operand = QDQ values of each group's transposed rows
+    deq = oracle.mxfp4_dequant(codes, scales, ldq)
+    start, P = 0, 0
+    for e in ge.tolist():
+        m = e - start
+        if m:
+            y, _, _, _ = oracle.mxfp4_qdq_ex(np.ascontiguousarray(x[start:e].T))
+            assert np.array_equal(deq[:, P:P + m], y.astype(np.float64))
+        P += (m + 31) // 32 * 32
+        start = e
