@@ -125,20 +125,33 @@ def moe_tile_stats(sizes, H, F, cus, BM=256, BN=256, BK=128):
         out[name] = {"tiles": tiles, "rows_computed": m_tiles * BM, "rows_routed": routed,
                      "row_waste_frac": round(1 - routed / (m_tiles * BM), 4),
                      "max_over_mean_tiles_per_workgroup": round(rounds / (tiles / cus), 4)}
-    # ragged K (weight gradient: M = H, N = F), empty groups' tiles store zeros
+    # ragged K (weight gradient: M = H, N = F): the plain launch walks the
+    # experts above 1024 tokens (their tiles' stages are 128 tokens deep, an
+    # even number of them), the exact-group launch the others (empty ones
+    # store zeros; a stage of 128 padded tokens runs one interleaved step per
+    # 8 of them)
     per_g = ((H + BM - 1) // BM) * ((F + BN - 1) // BN)
-    nst = [(-(-((m + 31) // 32 * 32) // BK) + 1) // 2 * 2 for m in sizes]
-    order = sorted(range(len(sizes)), key=lambda g: (-sizes[g], g))
+    long_g = [g for g in range(len(sizes)) if sizes[g] > 1024]
+    nst = {g: (-(-((sizes[g] + 31) // 32 * 32) // BK) + 1) // 2 * 2 for g in long_g}
+    order = sorted(long_g, key=lambda g: (-sizes[g], g))
     work = [0] * cus
     tile = 0
     for g in order:
         for _ in range(per_g):
             work[tile % cus] += nst[g] + 1  # its stages plus one for the output tile
             tile += 1
-    k_computed = sum(nst[g] * BK for g in range(len(sizes)))
-    out["raggedK_wgrad"] = {"tiles": tile, "tokens_routed": routed, "tokens_computed": k_computed,
-                            "token_waste_frac": round(1 - routed / k_computed, 4),
-                            "max_over_mean_stages_per_workgroup": round(max(work) / (sum(work) / cus), 4)}
+    k_computed = sum(nst[g] * BK for g in long_g)
+    routed_long = sum(sizes[g] for g in long_g)
+    short = [g for g in range(len(sizes)) if sizes[g] <= 1024]
+    out["raggedK_wgrad"] = {
+        "plain_launch": {"experts": len(long_g), "tiles": tile, "tokens_routed": routed_long,
+                         "tokens_computed": k_computed,
+                         "token_waste_frac": round(1 - routed_long / k_computed, 4) if k_computed else 0.0,
+                         "max_over_mean_stages_per_workgroup": round(max(work) / (sum(work) / cus), 4)
+                         if tile else 0.0},
+        "exact_group_launch": {"experts": len(short), "empty_experts": sum(1 for g in short if sizes[g] == 0),
+                               "tiles": len(short) * per_g, "tokens_routed": sum(sizes[g] for g in short),
+                               "interleaved_steps_per_tile": sum((sizes[g] + 31) // 32 * 4 for g in short)}}
     return out
 
 

@@ -35,21 +35,29 @@ def test_committed_profiles_name_the_profiled_source():
 
 def test_moe_tile_stats_small_cases():
     """Tile accounting of the grouped GEMMs, checked by hand: ragged-M tiles
-    start at the 128-row boundary below their group; ragged-K stages are
-    128 tokens deep, an even number per group, zero for an empty group."""
+    start at the 128-row boundary below their group; ragged-K experts above
+    1024 tokens run 128-token stages, an even number per expert, and the
+    others go to the exact-group launch (one interleaved step per 8 padded
+    tokens)."""
     b = load_bench()
-    # one group of 256 rows: a single m-tile, nothing wasted
+    # one group of 256 rows: a single m-tile, nothing wasted; exact-group launch
     st = b.moe_tile_stats([256], 256, 512, cus=4)
     assert st["raggedM_fwd"]["tiles"] == 2 and st["raggedM_fwd"]["row_waste_frac"] == 0
-    assert st["raggedK_wgrad"]["tokens_computed"] == 256        # 2 stages of 128
+    assert st["raggedK_wgrad"]["plain_launch"]["experts"] == 0
+    assert st["raggedK_wgrad"]["exact_group_launch"]["interleaved_steps_per_tile"] == 256 // 8
     # groups 5, 0, 300: group 2 starts at row 5 (aligned down to 0), so it
     # spans rows 0..304 of its tiles: 2 m-tiles; group 0 needs 1
     st = b.moe_tile_stats([5, 0, 300], 256, 256, cus=2)
     assert st["raggedM_fwd"]["rows_computed"] == 3 * 256
     assert st["raggedM_fwd"]["rows_routed"] == 305
-    # ragged K: ceil32 -> 32 and 320 tokens -> 1 and 3 stages -> even: 2 and 4
-    assert st["raggedK_wgrad"]["tokens_computed"] == (2 + 0 + 4) * 128
-    assert st["raggedK_wgrad"]["tiles"] == 3
-    # the largest group's tile goes first: workgroup 0 gets 4 + 1 and 0 + 1
-    # (the empty group), workgroup 1 gets 2 + 1
-    assert st["raggedK_wgrad"]["max_over_mean_stages_per_workgroup"] == round(6 / (9 / 2), 4)
+    ex = st["raggedK_wgrad"]["exact_group_launch"]
+    assert ex["experts"] == 3 and ex["empty_experts"] == 1 and ex["tokens_routed"] == 305
+    assert ex["interleaved_steps_per_tile"] == (32 + 0 + 320) // 8
+    # ragged K plain launch: 1100 and 2000 tokens -> ceil32 1120, 2016 -> 9 and
+    # 16 stages -> even: 10 and 16; the larger expert's tile goes first
+    st = b.moe_tile_stats([1100, 7, 2000], 256, 256, cus=2)
+    pl = st["raggedK_wgrad"]["plain_launch"]
+    assert pl["experts"] == 2 and pl["tiles"] == 2
+    assert pl["tokens_computed"] == (10 + 16) * 128 and pl["tokens_routed"] == 3100
+    # workgroup 0: 16 + 1, workgroup 1: 10 + 1
+    assert pl["max_over_mean_stages_per_workgroup"] == round(17 / (28 / 2), 4)
