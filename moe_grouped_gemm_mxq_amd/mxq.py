@@ -300,7 +300,7 @@ def mxq_grouped_gemm(mode, A, sA, B, sB, C, group_end, stream=None, fmt=MXQ_FMT_
     """RAGGED_M: A [M][K], B [G][N][K], C [M][N].  RAGGED_K: A [M][K], B [N][K], C [G][M][N].
 
     Scales: sA scale_shape(M, K/32); sB (G,) + scale_shape(N, K/32) (ragged M) or scale_shape(N, K/32).
-    fmt MXQ_FMT_E2M1 (ragged M only): code rows of K/2 bytes."""
+    fmt MXQ_FMT_E2M1: code rows of K/2 bytes (ragged K: from mxq_quantize_fp4_grouped)."""
     for t, n in ((A, "A"), (sA, "sA"), (B, "B"), (sB, "sB")):
         _need(t, torch.uint8, n)
     _need(C, torch.float32, "C")

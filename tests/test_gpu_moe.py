@@ -100,7 +100,8 @@ def test_ragged_k_exact_groups_on_spread_tokens():
 def test_malformed_group_end_stays_in_bounds(ends):
     """Group ends that are not non-decreasing or lie past T break the
     precondition (results are unspecified) but are clamped on the device:
-    the grouped quantiser and both grouped GEMMs finish without touching
+    the grouped quantisers (MXFP8 and MXFP4) and the grouped GEMMs (E4M3
+    ragged M and K, E2M1 ragged K) finish without touching
     memory outside their buffers (guard bytes around the outputs stay), and
     the validator reports the first bad entry."""
     m = mxq()
@@ -130,10 +131,18 @@ def test_malformed_group_end_stays_in_bounds(ends):
     ws = torch.full((G,) + m.scale_shape(N, C // 32), 127, dtype=torch.uint8, device="cuda")
     ybuf, Y = guarded((T, N), torch.float32, 7.0)
     m.mxq_grouped_gemm(m.MXQ_GG_RAGGED_M, xr["q_row"], xr["s_row"], wq, ws, Y, ge)
+    # MXFP4: grouped token-axis quantiser of fp32 input and the E2M1 weight gradient
+    q4buf, q4 = guarded((C, ldq // 2), torch.uint8, 0x5A)
+    s4buf, s4 = guarded(m.scale_shape(C, ldq // 32), torch.uint8, 0x5A)
+    m.mxq_quantize_fp4_grouped(x.float(), ge, ldq, q4, s4)
+    qy4 = torch.zeros((N, ldq // 2), dtype=torch.uint8, device="cuda")
+    c4buf, dW4 = guarded((G, C, N), torch.float32, 7.0)
+    m.mxq_grouped_gemm(m.MXQ_GG_RAGGED_K, q4, s4, qy4, sy, dW4, ge, fmt=m.MXQ_FMT_E2M1)
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
     m.mxq_validate_group_end(ge, T, flag)
     torch.cuda.synchronize()
-    for buf, fill in ((qbuf, 0x5A), (sbuf, 0x5A), (cbuf, 7.0), (ybuf, 7.0)):
+    for buf, fill in ((qbuf, 0x5A), (sbuf, 0x5A), (cbuf, 7.0), (ybuf, 7.0), (q4buf, 0x5A), (s4buf, 0x5A),
+                      (c4buf, 7.0)):
         assert bool((buf[:guard] == fill).all()) and bool((buf[-guard:] == fill).all()), "guard bytes overwritten"
     bad = next(i for i, e in enumerate(ends) if e < (ends[i - 1] if i else 0) or e < 0 or e > T)
     assert int(flag.item()) == bad + 1

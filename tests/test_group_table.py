@@ -9,8 +9,9 @@ The replica follows the kernels step by step:
   * build_block_starts: ends clamped into [0, R], per-group unit counts
     ceil((size + start % align) / unit) in 64 bits, prefix sums saturated at
     INT32_MAX;
-  * the grouped quantiser: padded block pb -> group g (largest g with
-    bstart[g] <= pb), source rows [gstart + off, + valid);
+  * the grouped quantisers (MXFP8 tiles of 128 padded positions, MXFP4 of
+    256): padded block pb -> group g (largest g with bstart[g] <= pb), source
+    rows [gstart + off, + valid);
   * the ragged-M GEMM: m-tile -> (group, first row m0, rows), tile count cut
     at the launcher's bound tiles_m + 2G;
   * the ragged-K GEMM: expert g's reduction range [k_begin, k_end) in [0, K].
@@ -78,12 +79,14 @@ def sample_units(total, n=4000, seed=0):
 
 @pytest.mark.parametrize("ends", ARRAYS)
 @pytest.mark.parametrize("T", [1, 96, 5000])
-def test_grouped_quantiser_reads_inside_the_input(ends, T):
+@pytest.mark.parametrize("tile_rows", [128, 256])  # MXFP8 tile quantiser / grouped MXFP4 quantiser
+def test_grouped_quantiser_reads_inside_the_input(ends, T, tile_rows):
     G = len(ends)
     ldq = (T + 31 * G + 31) // 32 * 32            # mxq_grouped_cols_max
     start, size, bstart, nb = build_block_starts(ends, T, 32)
     assert all(bstart[g] <= bstart[g + 1] <= bstart[g] + nb[g] for g in range(G))
-    launched_blocks = (T + 31 * G + 127) // 128 * 4   # tiles of 128 padded rows over R + 31 G
+    # tiles of tile_rows padded positions over T + 31 G
+    launched_blocks = (T + 31 * G + tile_rows - 1) // tile_rows * (tile_rows // 32)
     for pb in sample_units(min(bstart[G], launched_blocks)):
         if (pb + 1) * 32 > ldq:
             continue                                    # the kernel drops such blocks
