@@ -32,7 +32,8 @@ constexpr int kThreads = 256;
 // the row's loads.  A workgroup therefore takes four 256-thread sub-groups,
 // sub-group j on rows 32j + q .. 32j + q + rps - 1 of a group (rps = 256/tpr),
 // gathers their scale bytes in LDS and writes them as dwords: one line per
-// block for 4 * rps rows.
+// block for 4 * rps rows.  The workgroups of one 128-row group run on
+// one XCD (see the unit mapping in the kernel).
 constexpr int kRowUnroll = 4;
 constexpr int kRowSub = 256, kRowThreads = 4 * kRowSub;
 
@@ -75,7 +76,21 @@ __global__ __launch_bounds__(kRowThreads) void quant_row_kernel(const uint16_t* 
   const int64_t n_units = (R + 127) / 128 * per_group;
   const int n_steps = (cpr + kRowUnroll * tpr - 1) / (kRowUnroll * tpr);  // uniform
   int parity = 0;
-  for (int64_t unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
+  // A 128-row group's scale lines are completed by its per_group workgroups
+  // (each writes its rows' dwords).  Workgroups are dealt to the 8 XCDs round
+  // robin, so within each run of 8 groups workgroup b takes a unit that puts
+  // all of a group's workgroups on one XCD, whose L2 merges their pieces of
+  // each line before it is written back (spread over the XCDs, the pieces
+  // went out as partial lines: 1.075 of the algorithmic bytes written for
+  // 131072 x 7168).
+  const int64_t span = 8 * (int64_t)per_group;
+  const int64_t full = n_units / span * span;
+  for (int64_t b = blockIdx.x; b < n_units; b += gridDim.x) {
+    int64_t unit = b;
+    if (b < full) {
+      const int64_t r = b % span;
+      unit = b - r + (r & 7) * per_group + (r >> 3);
+    }
     const int64_t g = unit / per_group;
     const int qb = (int)(unit - g * per_group) << rps_log2;
     const int64_t row = g * 128 + 32 * j + qb + i;

@@ -1,0 +1,39 @@
+"""Host replica of the MXFP8 row quantiser's workgroup-to-unit mapping
+(quant_mxfp8.hip): unit u covers rows 32 j + (u % per_group) * rps + i of
+128-row group u / per_group; workgroup b runs the unit that puts every
+workgroup of one group on the XCD b % 8.  The mapping must be a permutation
+of the units, so every row is quantised exactly once, for every row length
+(per_group = 1 .. 32) and row count, full runs of 8 groups or not."""
+import pytest
+
+
+def row_unit(b, n_units, per_group):
+    span = 8 * per_group
+    full = n_units // span * span
+    if b < full:
+        r = b % span
+        return b - r + (r & 7) * per_group + (r >> 3)
+    return b
+
+
+def launch_shape(R, C):
+    """tpr_log2, per_group and units as the launcher and kernel derive them."""
+    cpr = (C + 31) // 32 * 4
+    tpr_log2 = 3
+    while (1 << tpr_log2) < cpr and tpr_log2 < 8:
+        tpr_log2 += 1
+    per_group = 32 >> (8 - tpr_log2)
+    return per_group, (R + 127) // 128 * per_group
+
+
+@pytest.mark.parametrize("R", [1, 127, 128, 1000, 8 * 128, 8 * 128 + 1, 131072])
+@pytest.mark.parametrize("C", [1, 32, 100, 512, 1024, 4096, 7168])
+def test_row_units_are_a_permutation(R, C):
+    per_group, n_units = launch_shape(R, C)
+    units = [row_unit(b, n_units, per_group) for b in range(n_units)]
+    assert sorted(units) == list(range(n_units))
+    span = 8 * per_group
+    full = n_units // span * span
+    # within full runs, a group's workgroups share one XCD
+    for b in range(full):
+        assert (units[b] // per_group) % 8 == b % 8
