@@ -193,8 +193,21 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
   __shared__ int64_t rb_src[kTR / 32];   // first source row of each block of the tile
   __shared__ int32_t rb_valid[kTR / 32]; // valid rows in that block (0: no output block)
   const int t = threadIdx.x;
-  const int rt = blockIdx.x / n_col_tiles;
-  const int ct = blockIdx.x - rt * n_col_tiles;
+  // Ungrouped tiles: workgroups go to the 8 XCDs round robin; within each run
+  // of 64, workgroup b takes tile b - r + 8 (r % 8) + r / 8 (r = b % 64), so
+  // an XCD runs eight consecutive tiles of a row of tiles (2 KB of each input
+  // row) rather than every eighth (measured 3-5% faster).  Grouped tiles keep
+  // the plain order, which measured 35% faster for them.
+  int bt = blockIdx.x;
+  if constexpr (!GROUPED) {
+    const int full = (int)(gridDim.x / 64 * 64);
+    if (bt < full) {
+      const int r = bt & 63;
+      bt = bt - r + (r & 7) * 8 + (r >> 3);
+    }
+  }
+  const int rt = bt / n_col_tiles;
+  const int ct = bt - rt * n_col_tiles;
   const int64_t p0 = (int64_t)rt * kTR;  // first padded position of the tile
   const int64_t c0 = (int64_t)ct * kTC;
 

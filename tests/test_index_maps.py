@@ -1,9 +1,10 @@
-"""Host replica of the MXFP8 row quantiser's workgroup-to-unit mapping
-(quant_mxfp8.hip): unit u covers rows 32 j + (u % per_group) * rps + i of
-128-row group u / per_group; workgroup b runs the unit that puts every
-workgroup of one group on the XCD b % 8.  The mapping must be a permutation
-of the units, so every row is quantised exactly once, for every row length
-(per_group = 1 .. 32) and row count, full runs of 8 groups or not."""
+"""Host replicas of the MXFP8 quantisers' workgroup-to-work mappings
+(quant_mxfp8.hip).  Row quantiser: unit u covers rows 32 j + (u % per_group)
+* rps + i of 128-row group u / per_group, and workgroup b runs the unit that
+puts every workgroup of one group on the XCD b % 8.  Ungrouped tile
+quantiser: workgroup b runs the tile that gives each XCD eight consecutive
+tiles.  Each mapping must be a permutation, so every row or tile is
+quantised exactly once, for every size, full runs or not."""
 import pytest
 
 
@@ -37,3 +38,19 @@ def test_row_units_are_a_permutation(R, C):
     # within full runs, a group's workgroups share one XCD
     for b in range(full):
         assert (units[b] // per_group) % 8 == b % 8
+
+
+def tile_of(b, grid):
+    full = grid // 64 * 64
+    if b < full:
+        r = b & 63
+        return b - r + (r & 7) * 8 + (r >> 3)
+    return b
+
+
+@pytest.mark.parametrize("grid", [1, 63, 64, 65, 1000, 4096, 14680064 // 256])
+def test_tile_order_is_a_permutation(grid):
+    tiles = [tile_of(b, grid) for b in range(grid)]
+    assert sorted(tiles) == list(range(grid))
+    for b in range(grid // 64 * 64):   # eight consecutive tiles per XCD
+        assert (tiles[b] // 8) % 8 == b % 8
