@@ -67,6 +67,10 @@ extern "C" {
  * ragged K: an expert's token count) run with exact 8-product MFMA groups;
  * see mxq_gemm. */
 #define MXQ_EXACT_GROUPS_MAX_K 1024
+/* Code bytes per operand row the GEMMs address (K for E4M3, K/2 for E2M1)
+ * must stay below this: a 256-row tile of codes is addressed with 32-bit
+ * offsets.  So K <= 2^23 - 32 (E4M3) and K <= 2^24 - 32 (E2M1). */
+#define MXQ_GEMM_MAX_ROW_BYTES (1 << 23)
 
 typedef enum {
     MXQ_OK = 0,
@@ -278,8 +282,9 @@ mxq_status mxq_quantize_fp4_grouped(const float* x, int64_t T, int64_t C, int64_
  * numeric model, taken as a GEMM on the codes): A codes [M][K/2], B codes
  * [N][K/2] as written by mxq_quantize_fp4 (rows of K elements), scales in
  * the same operand layout.
- * M, N >= 1; K >= 32, K % 32 == 0; ldc >= N.  A, B 16-byte aligned, sA, sB
- * and C 4-byte aligned (else MXQ_ERR_INVALID_ARGUMENT).  Unknown fmt:
+ * M, N >= 1; K >= 32, K % 32 == 0; code bytes per row (K, or K/2 for
+ * E2M1) below MXQ_GEMM_MAX_ROW_BYTES; ldc >= N.  A, B 16-byte aligned, sA,
+ * sB and C 4-byte aligned (else MXQ_ERR_INVALID_ARGUMENT).  Unknown fmt:
  * MXQ_ERR_UNSUPPORTED.
  */
 mxq_status mxq_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
@@ -303,8 +308,10 @@ mxq_status mxq_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const
  * fmt MXQ_FMT_E2M1: MXFP4 operands as for mxq_gemm (codes K/2 bytes per row,
  * expert g's B codes at byte g * N * K/2); for MXQ_GG_RAGGED_K the grouped
  * token-axis copies of mxq_quantize_fp4_grouped (K = their ldq).
- * M, N >= 1; K >= 32, K % 32 == 0; 1 <= G <= MXQ_MAX_GROUPS.  A, B 16-byte
- * aligned, sA, sB and C 4-byte aligned (else MXQ_ERR_INVALID_ARGUMENT).
+ * M, N >= 1; K >= 32, K % 32 == 0; code bytes per row below
+ * MXQ_GEMM_MAX_ROW_BYTES (as for mxq_gemm); 1 <= G <= MXQ_MAX_GROUPS.  A, B
+ * 16-byte aligned, sA, sB and C 4-byte aligned (else
+ * MXQ_ERR_INVALID_ARGUMENT).
  */
 mxq_status mxq_grouped_gemm(mxq_gg_mode mode, const uint8_t* A, const uint8_t* sA,
                             const uint8_t* B, const uint8_t* sB, float* C,

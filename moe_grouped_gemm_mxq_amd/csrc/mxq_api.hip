@@ -305,6 +305,8 @@ mxq_status mxq_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const
               "mxq_gemm: sA, sB must be 4-byte aligned (the kernel reads scale dwords)");
   if (fmt != MXQ_FMT_E4M3 && fmt != MXQ_FMT_E2M1)
     return fail(MXQ_ERR_UNSUPPORTED, "mxq_gemm: unknown operand format %d", (int)fmt);
+  MXQ_REQUIRE((fmt == MXQ_FMT_E2M1 ? K / 2 : K) < MXQ_GEMM_MAX_ROW_BYTES,
+              "mxq_gemm: K = %lld gives code rows of MXQ_GEMM_MAX_ROW_BYTES or more", (long long)K);
   MXQ_REQUIRE_DEVICE();
   return launched(launch_gemm(0, fmt == MXQ_FMT_E2M1, A, sA, B, sB, C, M, N, K, ldc, nullptr, 1, st), "mxq_gemm");
 }
@@ -325,6 +327,8 @@ mxq_status mxq_grouped_gemm(mxq_gg_mode mode, const uint8_t* A, const uint8_t* s
               "mxq_grouped_gemm: sA, sB must be 4-byte aligned (the kernel reads scale dwords)");
   if (fmt != MXQ_FMT_E4M3 && fmt != MXQ_FMT_E2M1)
     return fail(MXQ_ERR_UNSUPPORTED, "mxq_grouped_gemm: unknown operand format %d", (int)fmt);
+  MXQ_REQUIRE((fmt == MXQ_FMT_E2M1 ? K / 2 : K) < MXQ_GEMM_MAX_ROW_BYTES,
+              "mxq_grouped_gemm: K = %lld gives code rows of MXQ_GEMM_MAX_ROW_BYTES or more", (long long)K);
   MXQ_REQUIRE_DEVICE();
   return launched(launch_gemm(mode == MXQ_GG_RAGGED_M ? 1 : 2, fmt == MXQ_FMT_E2M1, A, sA, B, sB, C, M, N, K, N,
                               group_end, G, st),

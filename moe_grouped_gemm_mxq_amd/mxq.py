@@ -41,6 +41,7 @@ MXQ_GG_RAGGED_M = 0
 MXQ_GG_RAGGED_K = 1
 BLOCK = 32
 MAX_GROUPS = 1024
+MAX_ROW_BYTES = 1 << 23  # MXQ_GEMM_MAX_ROW_BYTES: GEMM code rows (K, or K/2 for E2M1) stay below this
 
 EXPORTED = [
     "mxq_abi_version", "mxq_last_error", "mxq_device_check", "mxq_grouped_cols_max", "mxq_operand_sizes",

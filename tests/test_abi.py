@@ -125,6 +125,15 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     assert "multiple of 32" in err(lib)
     assert call(lib, "mxq_gemm", FAKE, FAKE, FAKE, FAKE, FAKE, I64(4), I64(8), I64(64), I64(4), 0, P(0)) == 1
     assert call(lib, "mxq_gemm", FAKE, FAKE, FAKE, FAKE, FAKE, I64(4), I64(4), I64(64), I64(4), 7, P(0)) == 2
+    # code rows of 2^23 bytes or more (K >= 2^23 for E4M3, 2^24 for E2M1) are rejected
+    for fmt, K in ((0, 1 << 23), (1, 1 << 24)):
+        assert call(lib, "mxq_gemm", FAKE, FAKE, FAKE, FAKE, FAKE, I64(256), I64(256), I64(K), I64(256), fmt,
+                    P(0)) == 1
+        assert "MXQ_GEMM_MAX_ROW_BYTES" in err(lib)
+        for mode in (0, 1):
+            assert call(lib, "mxq_grouped_gemm", mode, FAKE, FAKE, FAKE, FAKE, FAKE, I64(256), I64(256), I64(K),
+                        FAKE, ctypes.c_int32(2), fmt, P(0)) == 1
+            assert "MXQ_GEMM_MAX_ROW_BYTES" in err(lib)
     # GEMM scale arrays are read as dwords
     assert call(lib, "mxq_gemm", FAKE, P(0x1002), FAKE, FAKE, FAKE, I64(4), I64(4), I64(64), I64(4), 0, P(0)) == 1
     assert "sA, sB" in err(lib)
@@ -190,6 +199,10 @@ def test_valid_call_without_gfx950_reports_device_error(lib):
                 ctypes.c_int32(2), 1, P(0)) == 3
     assert call(lib, "mxq_quantize_fp4_grouped", FAKE, I64(64), I64(8), I64(8), FAKE, ctypes.c_int32(2), I64(128),
                 ctypes.c_float(6.0), FAKE, FAKE, P(0)) == 3
+    # the largest K of each format passes the host checks
+    for fmt, K in ((0, (1 << 23) - 32), (1, (1 << 24) - 32)):
+        assert call(lib, "mxq_gemm", FAKE, FAKE, FAKE, FAKE, FAKE, I64(256), I64(256), I64(K), I64(256), fmt,
+                    P(0)) == 3
 
 
 def test_binding_fails_loudly_without_the_library(tmp_path):
@@ -257,3 +270,15 @@ def test_fp4_exponent_rule_from_threshold_matches_oracle(lib):
         e = (amax >> 23) - 127 - F + ((amax & 0x7FFFFF) >= T)
         e = np.where(amax >> 23 == 0, -30, np.maximum(e, -30))
         assert np.array_equal(s[:, 0].astype(np.int64) - 127, e), sf
+
+
+def test_binding_constants_match_the_header():
+    """Constants the binding mirrors from include/mxq.h."""
+    import re
+    from moe_grouped_gemm_mxq_amd import mxq as m
+    text = open(os.path.join(ROOT, "include", "mxq.h")).read()
+    define = lambda name: eval(re.search(rf"#define {name} (.+?)(?:\s*/\*|\n)", text).group(1))
+    assert define("MXQ_ABI_VERSION") == m.ABI_VERSION
+    assert define("MXQ_MAX_GROUPS") == m.MAX_GROUPS
+    assert define("MXQ_BLOCK") == m.BLOCK
+    assert define("MXQ_GEMM_MAX_ROW_BYTES") == m.MAX_ROW_BYTES == 1 << 23
