@@ -1,4 +1,6 @@
-"""GEMMs at the largest reduction length their tile addressing allows: code
+"""Largest sizes.  The quantisers past 2^31 elements (64-bit output
+offsets; sampled rows and columns against the oracle), and the GEMMs at the
+largest reduction length their tile addressing allows: code
 rows of MXQ_GEMM_MAX_ROW_BYTES - 32 bytes, K = 2^23 - 32 for E4M3 and
 2^24 - 32 for E2M1 (a 256-row tile of 2 GiB of codes).
 
@@ -115,3 +117,72 @@ def test_gemm_at_the_largest_k(fmt):
         m.mxq_gemm(qa["q_row"], qa["s_row"], qb["q_row"], qb["s_row"], C)
     got = host(C).astype(np.float64)
     assert np.array_equal(got, ref), f"max |diff| {np.abs(got - ref).max()}"
+
+
+def _randn_bf16(R, C, seed):
+    """N(0,1) bf16 [R][C] on the GPU, every 64th row and 48th column scaled by
+    a power of two (so blocks of very different scales meet), a few rows at a time."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    x = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
+    col_scale = torch.where(torch.arange(C, device="cuda") % 48 == 5, 2.0 ** 20, 1.0)
+    for r0 in range(0, R, 4096):
+        r1 = min(R, r0 + 4096)
+        row_scale = torch.where(torch.arange(r0, r1, device="cuda")[:, None] % 64 == 3, 2.0 ** -30, 1.0)
+        x[r0:r1] = (torch.randn((r1 - r0, C), generator=g, device="cuda") * row_scale * col_scale).to(torch.bfloat16)
+    return x
+
+
+def _bits(t):
+    return host(t.contiguous().view(torch.int16)).view(np.uint16)
+
+
+@pytest.mark.gpu
+def test_dual_quantise_beyond_2_31_elements():
+    """Row and column copies of a 65536 x 36864 bf16 matrix (2.4e9 elements,
+    output offsets past 2^31) in one dual-axis launch: sampled rows and
+    columns, at the ends of the matrix and of its 128-row scale groups, equal
+    the oracle's bytes."""
+    import oracle
+    from gpu_util import scale_rows
+    m = mxq()
+    R, C = 65536, 36864
+    print(f"[limits] dual quantise {R}x{C}", flush=True)
+    x = _randn_bf16(R, C, 11)
+    got = m.quantize(x, m.MXQ_AXIS_ROW | m.MXQ_AXIS_COLT)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 3, 127, 128, 32767, 32768, 65411, 65535])
+    cols = np.array([0, 5, 31, 32, 127, 128, 18431, 36805, 36863])
+    q, s = oracle.mxfp8_quant_row(_bits(x[torch.as_tensor(rows, device="cuda")]))
+    assert np.array_equal(host(got["q_row"][torch.as_tensor(rows, device="cuda")]), q)
+    assert np.array_equal(scale_rows(got["s_row"], rows), s)
+    qt, st = oracle.mxfp8_quant_colT(_bits(x[:, torch.as_tensor(cols, device="cuda")]))
+    assert np.array_equal(host(got["q_colT"][torch.as_tensor(cols, device="cuda")]), qt)
+    assert np.array_equal(scale_rows(got["s_colT"], cols), st)
+
+
+@pytest.mark.gpu
+def test_grouped_quantise_beyond_2_31_elements():
+    """Token-axis copy (row copy too) of 131072 x 32768 bf16 in 32 groups of
+    the MoE layer's sizes (4.3e9 elements; column-copy offsets past 2^32):
+    sampled columns and rows equal the oracle's bytes."""
+    import oracle
+    from gpu_util import scale_rows
+    from moe_grouped_gemm_mxq_amd import workloads
+    m = mxq()
+    T, C = 131072, 32768
+    print(f"[limits] grouped quantise {T}x{C}", flush=True)
+    sizes = workloads.moe_group_sizes()
+    ge_np = np.cumsum(sizes).astype(np.int32)
+    ge = torch.from_numpy(ge_np).cuda()
+    x = _randn_bf16(T, C, 12)
+    got = m.quantize_grouped(x, ge, m.MXQ_AXIS_ROW | m.MXQ_AXIS_COLT)
+    torch.cuda.synchronize()
+    cols = np.array([0, 5, 31, 127, 128, 16383, 32709, 32767])
+    qt, st = oracle.mxfp8_quant_grouped_colT(_bits(x[:, torch.as_tensor(cols, device="cuda")]), ge_np, got["ldq"])
+    P = oracle.grouped_cols(ge_np)   # positions past the groups' padded columns are not written
+    assert np.array_equal(host(got["q_colT"][torch.as_tensor(cols, device="cuda")])[:, :P], qt[:, :P])
+    assert np.array_equal(scale_rows(got["s_colT"], cols)[:, :P // 32], st[:, :P // 32])
+    rows = np.array([0, 3, 65535, 131071])
+    q, s = oracle.mxfp8_quant_row(_bits(x[torch.as_tensor(rows, device="cuda")]))
+    assert np.array_equal(host(got["q_row"][torch.as_tensor(rows, device="cuda")]), q)
+    assert np.array_equal(scale_rows(got["s_row"], rows), s)
