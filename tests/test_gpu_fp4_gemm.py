@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import assert_gemm_close, boundary_indices, host, mxq, unpack_scales
+from gpu_util import assert_gemm_close, host, mxq, unpack_scales
 
 pytestmark = pytest.mark.gpu
 
@@ -58,8 +58,10 @@ def test_gemm_fp4_matches_oracle(M, N, K):
     assert_gemm_close(host(C), Cr, Ca, f"fp4 gemm {M}x{N}x{K}")
 
 
-def test_gemm_fp4_full_size_sampled():
-    """The dense linear's forward shape, M 8192 x N 18432 x K 7168, in MXFP4."""
+def test_gemm_fp4_full_size_every_output():
+    """The dense linear's forward shape, M 8192 x N 18432 x K 7168, in MXFP4:
+    every code and scale byte of both operands and every one of the 151M
+    outputs against the oracle's fp64 product of its own dequantised codes."""
     m = mxq()
     M, N, K = 8192, 18432, 7168
     g = torch.Generator(device="cuda").manual_seed(0)
@@ -69,17 +71,52 @@ def test_gemm_fp4_full_size_sampled():
     qb, sb = m.quantize_fp4(xb)
     C = m.gemm(qa, sa, qb, sb, fmt=m.MXQ_FMT_E2M1)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(5)
-    mi = boundary_indices(M, 256, rng, 24)
-    ni = boundary_indices(N, 256, rng, 24)
-    ra = host(xa[torch.as_tensor(mi, device="cuda")])
-    rb = host(xb[torch.as_tensor(ni, device="cuda")])
-    ca, csa = oracle_operand(torch.from_numpy(ra))
-    cb, csb = oracle_operand(torch.from_numpy(rb))
-    Cr, Ca = oracle.gemm_fp4(ca, csa, cb, csb)
-    got = host(C[torch.as_tensor(mi, device="cuda")][:, torch.as_tensor(ni, device="cuda")])
-    ratio = assert_gemm_close(got, Cr, Ca, "fp4 gemm 8192x18432x7168")
-    print(f"fp4 gemm full size: {got.size} sampled outputs, max err/sum|ab| = {ratio:.3e}")
+    ca, csa = oracle_operand(torch.from_numpy(host(xa)))
+    del xa
+    assert np.array_equal(host(qa), ca) and np.array_equal(unpack_scales(sa, M), csa)
+    cb, csb = oracle_operand(torch.from_numpy(host(xb)))
+    del xb
+    assert np.array_equal(host(qb), cb) and np.array_equal(unpack_scales(sb, N), csb)
+    Cr, Ca = oracle.gemm_dequantised(oracle.mxfp4_dequant(ca, csa, K), oracle.mxfp4_dequant(cb, csb, K))
+    ratio = assert_gemm_close(host(C), Cr, Ca, "fp4 gemm 8192x18432x7168 (every output)")
+    print(f"fp4 gemm full size: every output, max err/sum|ab| = {ratio:.3e}")
+
+
+def test_grouped_gemm_fp4_ragged_m_moe_every_output():
+    """The MoE forward shape in MXFP4: fp32 token rows X [131072x7168] N(0,1)
+    grouped by the frozen Zipf(1.1) routing, expert weights W[g] [4096x7168]
+    N(0, 0.02^2); every output of Y [131072x4096], expert by expert."""
+    from moe_grouped_gemm_mxq_amd import workloads
+    m = mxq()
+    sizes = workloads.moe_group_sizes()
+    ge_np = np.cumsum(sizes).astype(np.int32)
+    ge = torch.from_numpy(ge_np).cuda()
+    G, N, K, T = len(sizes), 4096, 7168, int(ge_np[-1])
+    g = torch.Generator(device="cuda").manual_seed(4)
+    X = torch.randn(T, K, generator=g, device="cuda")
+    W = torch.randn(G, N, K, generator=g, device="cuda") * 0.02
+    qx, sx = m.quantize_fp4(X)
+    qw = torch.empty((G, N, K // 2), dtype=torch.uint8, device="cuda")
+    sw = torch.empty((G,) + m.scale_shape(N, K // 32), dtype=torch.uint8, device="cuda")
+    for e in range(G):
+        m.mxq_quantize_fp4(W[e], qw[e], sw[e])
+    Y = m.grouped_gemm(m.MXQ_GG_RAGGED_M, qx, sx, qw, sw, ge, fmt=m.MXQ_FMT_E2M1)
+    torch.cuda.synchronize()
+    xc, xs = oracle_operand(torch.from_numpy(host(X)))
+    del X
+    assert np.array_equal(host(qx), xc) and np.array_equal(unpack_scales(sx, T), xs)
+    out = host(Y)
+    worst, start = 0.0, 0
+    for e, end in enumerate(ge_np.tolist()):
+        wc, ws = oracle_operand(torch.from_numpy(host(W[e])))
+        assert np.array_equal(host(qw[e]), wc) and np.array_equal(unpack_scales(sw[e], N), ws)
+        if end > start:
+            Cr, Ca = oracle.gemm_dequantised(oracle.mxfp4_dequant(xc[start:end], xs[start:end], K),
+                                             oracle.mxfp4_dequant(wc, ws, K))
+            worst = max(worst, assert_gemm_close(out[start:end], Cr, Ca,
+                                                 f"fp4 moe fwd expert {e} ({end - start} rows)"))
+        start = end
+    print(f"fp4 moe fwd: every output, max err/sum|ab| = {worst:.3e}")
 
 
 @pytest.mark.parametrize("sizes", [[5, 0, 300, 33], [256, 1, 0, 0, 513]])
