@@ -129,6 +129,58 @@ __global__ __launch_bounds__(kThreads) void qdq_rows_kernel(const float* __restr
   }
 }
 
+// GEMM operand copy (codes and packed scales, no dequantised output) of rows
+// whose length is a multiple of 1024: a unit is 1024 elements (32 blocks) of
+// one row, 256 lanes of four elements, so the row and its first block are
+// uniform per unit and a lane's scale offset needs no division.  A workgroup
+// takes kOpUnits consecutive units and issues all their loads before any
+// arithmetic.  (Dealing each 128-row group's workgroups to one XCD, so that
+// its L2 completes the group's scale lines, measured 3.5% slower here: the
+// scale bytes are 1/128 of the input.)
+constexpr int kOpUnits = 2;
+
+__global__ __launch_bounds__(kThreads) void quant_fp4_rows_kernel(const float* __restrict__ x, int64_t rows,
+                                                                 int64_t L, Fp4Scale p,
+                                                                 uint8_t* __restrict__ codes,
+                                                                 uint8_t* __restrict__ scales) {
+  const int64_t upr = L / 1024;      // units per row
+  const int64_t nbr = L / 32;        // blocks per row
+  const int64_t n_units = rows * upr;
+  const int64_t w = blockIdx.x;
+  const int t = threadIdx.x;
+  uint4 v[kOpUnits];
+#pragma unroll
+  for (int k = 0; k < kOpUnits; k++) {
+    const int64_t u = w * kOpUnits + k;
+    // units are whole rows' 1024-element pieces, so unit u starts at element 1024 u
+    if (u < n_units) v[k] = reinterpret_cast<const uint4*>(x)[u * 256 + t];
+  }
+  // row and piece of the first unit (uniform); the next unit is the next piece
+  int64_t row = w * kOpUnits / upr;
+  int64_t seg = w * kOpUnits - row * upr;
+#pragma unroll
+  for (int k = 0; k < kOpUnits; k++) {
+    const int64_t u = w * kOpUnits + k;
+    if (u < n_units) {
+      const uint32_t xb[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+      const int e = mxfp4_scale_exp(oct_max(absmax4(xb)), p);
+      uint32_t nib = 0;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const uint32_t sign = xb[j] & 0x80000000u;
+        const float yabs = __builtin_amdgcn_ldexpf(__uint_as_float(xb[j] & 0x7FFFFFFFu), -e);
+        nib |= ((sign >> 28) | mxfp4_index(yabs)) << (4 * j);
+      }
+      reinterpret_cast<uint16_t*>(codes)[u * 256 + t] = (uint16_t)nib;
+      if ((t & 7) == 0) scales[scale_offset(row, seg * 32 + (t >> 3), nbr)] = (uint8_t)(e + 127);
+    }
+    if (++seg == upr) {
+      seg = 0;
+      row++;
+    }
+  }
+}
+
 // Clipped STE backward, flat layout: grad_x = bit ? 0 : grad_y.
 // grad_x may alias grad_y (each element is read, then written, by one lane).
 __global__ __launch_bounds__(kThreads) void ste_flat_kernel(const float* gy, const uint32_t* __restrict__ sat_mask,
@@ -301,6 +353,13 @@ bool fp4_scale_params(float scale_factor, int* F, uint32_t* T) {
 hipError_t launch_qdq_fp4(const float* x, float* y, int64_t rows, int64_t L, int F, uint32_t T,
                           uint8_t* codes, uint8_t* scales, uint8_t* sat_mask, hipStream_t st, bool operand_layout) {
   const Fp4Scale p{F, T};
+  if (operand_layout && !y && !sat_mask && L % 1024 == 0 && (uintptr_t)x % 16 == 0) {
+    const int64_t n_wg = (rows * (L / 1024) + kOpUnits - 1) / kOpUnits;
+    if (n_wg <= 0x7FFFFFFF) {
+      quant_fp4_rows_kernel<<<(unsigned)n_wg, kThreads, 0, st>>>(x, rows, L, p, codes, scales);
+      return hipGetLastError();
+    }
+  }
   const bool flat = L % 32 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)y % 16 == 0;
   const int64_t n_chunks = flat ? rows * L / 4 : rows * ((L + 31) / 32) * 8;
   uint32_t* mask = reinterpret_cast<uint32_t*>(sat_mask);

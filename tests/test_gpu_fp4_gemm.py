@@ -22,7 +22,12 @@ def oracle_operand(x: torch.Tensor, sf: float = 6.0):
 
 
 @pytest.mark.parametrize("shape,sf", [((1, 32), 6.0), ((5, 64), 6.0), ((33, 96), 5.0), ((70, 45), 6.0),
-                                      ((300, 4096), 6.0), ((64, 160), 0.75)])
+                                      ((300, 4096), 6.0), ((64, 160), 0.75),
+                                      # rows of a multiple of 1024 elements: 1024-element pieces,
+                                      # two per workgroup (odd counts, partial 128-row groups,
+                                      # full runs of eight groups and a tail)
+                                      ((3, 1024), 6.0), ((129, 3072), 5.0), ((1029, 1024), 6.0),
+                                      ((2053, 3072), 0.75)])
 def test_quantize_fp4_matches_oracle(shape, sf):
     m = mxq()
     x = fp4_inputs(shape, sum(shape))

@@ -54,3 +54,31 @@ def test_tile_order_is_a_permutation(grid):
     assert sorted(tiles) == list(range(grid))
     for b in range(grid // 64 * 64):   # eight consecutive tiles per XCD
         assert (tiles[b] // 8) % 8 == b % 8
+
+
+
+FP4_UNITS = 2   # 1024-element row pieces per workgroup of the MXFP4 operand row quantiser
+
+
+@pytest.mark.parametrize("rows", [1, 3, 127, 128, 129, 1029, 18432])
+@pytest.mark.parametrize("L", [1024, 3072, 4096, 7168])
+def test_fp4_operand_rows_cover_every_piece_once(rows, L):
+    """MXFP4 operand row quantiser (qdq_mxfp4.hip): workgroup w takes pieces
+    2w and 2w + 1 (those below rows * L / 1024); the first piece's row and
+    place come from one division and the next piece follows, wrapping to the
+    next row."""
+    upr = L // 1024
+    n_units = rows * upr
+    n_wg = (n_units + FP4_UNITS - 1) // FP4_UNITS
+    seen = []
+    for w in range(n_wg):
+        row, seg = divmod(w * FP4_UNITS, upr)
+        for k in range(FP4_UNITS):
+            u = w * FP4_UNITS + k
+            if u < n_units:
+                assert u == row * upr + seg and 0 <= row < rows   # element 1024 u = row * L + 1024 seg
+                seen.append((row, seg))
+            seg += 1
+            if seg == upr:
+                seg, row = 0, row + 1
+    assert seen == [(r, g) for r in range(rows) for g in range(upr)]
