@@ -227,11 +227,32 @@ __global__ __launch_bounds__(kThreads) void ste_rows_kernel(const float* gy, con
 // wave reads at once sit in opposite halves of the LDS banks.
 constexpr int kTokTile = 256, kColTile = 32;
 constexpr int kTokRows = kTokTile + kTokTile / 32;
+constexpr int kGrpColTiles = 4;  // column tiles per workgroup
+
+// the eight 16-byte pieces of one thread: rows (t / 8) + 32 i, columns col4 ..
+template <bool VEC>
+__device__ __forceinline__ void load_fp4_tile_pieces(const float* const (&xr)[8], uint32_t row_ok, int64_t col4,
+                                                     int64_t C, float4 (&w)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    w[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row_ok >> i & 1u) {
+      if (VEC && col4 + 4 <= C) {
+        w[i] = *reinterpret_cast<const float4*>(xr[i] + col4);
+      } else {
+        if (col4 < C) w[i].x = xr[i][col4];
+        if (col4 + 1 < C) w[i].y = xr[i][col4 + 1];
+        if (col4 + 2 < C) w[i].z = xr[i][col4 + 2];
+        if (col4 + 3 < C) w[i].w = xr[i][col4 + 3];
+      }
+    }
+  }
+}
 
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void quant_fp4_grouped_kernel(
     const float* __restrict__ x, int64_t T, int64_t C, int64_t ldx, const int32_t* __restrict__ group_end,
-    int32_t G, int64_t ldq, int n_col_tiles, Fp4Scale p, uint8_t* __restrict__ codes,
+    int32_t G, int64_t ldq, int n_col_tiles, int n_col_groups, Fp4Scale p, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales) {
   __shared__ __attribute__((aligned(16))) float tile[kTokRows * kColTile];
   __shared__ int32_t bstart[kMaxGroups + 1];
@@ -239,10 +260,10 @@ __global__ __launch_bounds__(kThreads) void quant_fp4_grouped_kernel(
   __shared__ int32_t rb_valid[kTokTile / 32]; // its valid rows (0: no output block)
   static_assert(kThreads * sizeof(int64_t) <= sizeof(tile), "the group scan's scratch reuses the tile");
   const int t = threadIdx.x;
-  const int rt = blockIdx.x / n_col_tiles;
-  const int ct = blockIdx.x - rt * n_col_tiles;
+  const int rt = blockIdx.x / n_col_groups;
+  const int ct_begin = (blockIdx.x - rt * n_col_groups) * kGrpColTiles;
+  const int ct_end = min(ct_begin + kGrpColTiles, n_col_tiles);
   const int64_t p0 = (int64_t)rt * kTokTile;  // first padded position of the tile
-  const int64_t c0 = (int64_t)ct * kColTile;
   build_block_starts<kThreads>(group_end, G, T, 32, nullptr, nullptr, bstart, reinterpret_cast<int64_t*>(tile));
   if (t < kTokTile / 32) {
     const int64_t pb = p0 / 32 + t;
@@ -263,58 +284,58 @@ __global__ __launch_bounds__(kThreads) void quant_fp4_grouped_kernel(
   __syncthreads();
   if (rb_valid[0] <= 0) return;  // the tile lies past the last block (uniform)
 
-  // ---- load: eight 16-byte pieces per thread, rows (t / 8) + 32 i, columns 4 (t % 8) ..
+  // source rows of this thread's eight pieces, the same for every column tile
   const int cq = t & 7;
-  const int64_t col4 = c0 + 4 * cq;
-  float4 w[8];
+  const float* xr[8];
+  uint32_t row_ok = 0;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     const int lr = (t >> 3) + 32 * i;
     const int rb = lr >> 5;
-    const bool row_ok = (lr & 31) < rb_valid[rb];
-    const float* xr = x + (row_ok ? rb_src[rb] + (lr & 31) : 0) * ldx;
-    w[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (row_ok) {
-      if (VEC && col4 + 4 <= C) {
-        w[i] = *reinterpret_cast<const float4*>(xr + col4);
-      } else {
-        if (col4 < C) w[i].x = xr[col4];
-        if (col4 + 1 < C) w[i].y = xr[col4 + 1];
-        if (col4 + 2 < C) w[i].z = xr[col4 + 2];
-        if (col4 + 3 < C) w[i].w = xr[col4 + 3];
-      }
-    }
+    const bool ok = (lr & 31) < rb_valid[rb];
+    row_ok |= (uint32_t)ok << i;
+    xr[i] = x + (ok ? rb_src[rb] + (lr & 31) : 0) * ldx;
   }
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const int lr = (t >> 3) + 32 * i;
-    *reinterpret_cast<float4*>(tile + (lr + (lr >> 5)) * kColTile + 4 * cq) = w[i];
-  }
-  __syncthreads();
-
-  // ---- one column over one block per thread
   const int blk = t >> 5, col = t & 31;
-  uint32_t v[32];
-  uint32_t amax = 0;
+  const bool blk_ok = rb_valid[blk] > 0;
+  const int64_t pos = p0 + 32 * blk;  // padded position of this thread's block
+
+  // The workgroup walks its column tiles with the next tile's loads in flight
+  // while the current one is quantised from LDS.
+  float4 w[8];
+  load_fp4_tile_pieces<VEC>(xr, row_ok, (int64_t)ct_begin * kColTile + 4 * cq, C, w);
+  for (int ct = ct_begin; ct < ct_end; ct++) {
 #pragma unroll
-  for (int i = 0; i < 32; i++) {
-    const int lr = blk * 32 + i;
-    v[i] = __float_as_uint(tile[(lr + blk) * kColTile + col]);
-    amax = max(amax, v[i] & 0x7FFFFFFFu);
-  }
-  const int e = mxfp4_scale_exp(amax, p);
-  uint32_t nib[4] = {0u, 0u, 0u, 0u};
+    for (int i = 0; i < 8; i++) {
+      const int lr = (t >> 3) + 32 * i;
+      *reinterpret_cast<float4*>(tile + (lr + (lr >> 5)) * kColTile + 4 * cq) = w[i];
+    }
+    __syncthreads();
+    if (ct + 1 < ct_end) load_fp4_tile_pieces<VEC>(xr, row_ok, (int64_t)(ct + 1) * kColTile + 4 * cq, C, w);
+
+    // ---- one column over one block per thread
+    uint32_t v[32];
+    uint32_t amax = 0;
 #pragma unroll
-  for (int i = 0; i < 32; i++) {
-    const uint32_t sign = v[i] & 0x80000000u;
-    const float yabs = __builtin_amdgcn_ldexpf(__uint_as_float(v[i] & 0x7FFFFFFFu), -e);
-    nib[i >> 3] |= ((sign >> 28) | mxfp4_index(yabs)) << (4 * (i & 7));
-  }
-  const int64_t cg = c0 + col;
-  if (rb_valid[blk] > 0 && cg < C) {
-    const int64_t pos = p0 + 32 * blk;  // padded position of the block
-    *reinterpret_cast<uint4*>(codes + cg * (ldq / 2) + pos / 2) = make_uint4(nib[0], nib[1], nib[2], nib[3]);
-    scales[scale_offset(cg, pos / 32, ldq / 32)] = (uint8_t)(e + 127);
+    for (int i = 0; i < 32; i++) {
+      const int lr = blk * 32 + i;
+      v[i] = __float_as_uint(tile[(lr + blk) * kColTile + col]);
+      amax = max(amax, v[i] & 0x7FFFFFFFu);
+    }
+    const int e = mxfp4_scale_exp(amax, p);
+    uint32_t nib[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 32; i++) {
+      const uint32_t sign = v[i] & 0x80000000u;
+      const float yabs = __builtin_amdgcn_ldexpf(__uint_as_float(v[i] & 0x7FFFFFFFu), -e);
+      nib[i >> 3] |= ((sign >> 28) | mxfp4_index(yabs)) << (4 * (i & 7));
+    }
+    const int64_t cg = (int64_t)ct * kColTile + col;
+    if (blk_ok && cg < C) {
+      *reinterpret_cast<uint4*>(codes + cg * (ldq / 2) + pos / 2) = make_uint4(nib[0], nib[1], nib[2], nib[3]);
+      scales[scale_offset(cg, pos / 32, ldq / 32)] = (uint8_t)(e + 127);
+    }
+    __syncthreads();  // every wave has read the tile before the next one is written
   }
 }
 
@@ -377,15 +398,16 @@ hipError_t launch_quant_fp4_grouped(const float* x, int64_t T, int64_t C, int64_
   const Fp4Scale p{F, Tth};
   const int64_t n_row_tiles = (T + 31 * (int64_t)G + kTokTile - 1) / kTokTile;
   const int n_col_tiles = (int)((C + kColTile - 1) / kColTile);
-  const int64_t grid = n_row_tiles * n_col_tiles;
+  const int n_col_groups = (n_col_tiles + kGrpColTiles - 1) / kGrpColTiles;
+  const int64_t grid = n_row_tiles * n_col_groups;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   const bool vec = ldx % 4 == 0 && (uintptr_t)x % 16 == 0;
   if (vec)
     quant_fp4_grouped_kernel<true><<<(unsigned)grid, kThreads, 0, st>>>(x, T, C, ldx, group_end, G, ldq, n_col_tiles,
-                                                                         p, codes, scales);
+                                                                         n_col_groups, p, codes, scales);
   else
     quant_fp4_grouped_kernel<false><<<(unsigned)grid, kThreads, 0, st>>>(x, T, C, ldx, group_end, G, ldq,
-                                                                          n_col_tiles, p, codes, scales);
+                                                                          n_col_tiles, n_col_groups, p, codes, scales);
   return hipGetLastError();
 }
 
