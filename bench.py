@@ -321,6 +321,20 @@ def main():
         mxq.mxq_quantize_grouped(Xm, ge, ldq, R | C, mx["q_row"], mx["s_row"], mxt["q_colT"], mxt["s_colT"])
         launches.append([f"moe_quant_x_row_grouped {T}x{H} (dual_x forward)", "quant_tile_kernel<true, true, true>",
                          bytes_["moe_quant_x_row_grouped"]])
+        # beside the step: the MXFP4 operand quantisers of the MXFP4 GEMMs (fp32
+        # inputs): the dense forward's X and W^T by rows, the MoE weight
+        # gradient's X and dY along each expert's tokens
+        for name, t in (("X", X.float()), ("W^T", W.t().contiguous().float())):
+            mxq.quantize_fp4(t)
+            r, c = t.shape
+            launches.append([f"mxfp4_operand {name} {r}x{c}", "quant_fp4_rows_kernel", r * c * (4 + 0.5 + 1 / 32)])
+            del t
+        for name, t in (("X", Xm.float()), ("dY", dYm.float())):
+            mxq.quantize_fp4_grouped(t, ge, ldq)
+            c = t.shape[1]
+            launches.append([f"mxfp4_token_axis {name} {T}x{c}", "quant_fp4_grouped_kernel<true>",
+                             T * c * 4 + padded * c * (0.5 + 1 / 32)])
+            del t
         torch.cuda.synchronize()
         print(json.dumps({"quant_traffic_launches": launches}))
         return
