@@ -82,3 +82,33 @@ def test_fp4_operand_rows_cover_every_piece_once(rows, L):
             if seg == upr:
                 seg, row = 0, row + 1
     assert seen == [(r, g) for r in range(rows) for g in range(upr)]
+
+
+FP4_GROUP_COL_TILES = 4   # column tiles of one row tile walked by a workgroup of the MXFP4 grouped quantiser
+
+
+@pytest.mark.parametrize("C", [1, 31, 32, 33, 96, 128, 129, 200, 4096, 7168])
+@pytest.mark.parametrize("n_row_tiles", [1, 3, 516])
+def test_fp4_grouped_column_walk_covers_every_tile_once(C, n_row_tiles):
+    """MXFP4 grouped token-axis quantiser (qdq_mxfp4.hip): workgroup b takes
+    row tile b / n_col_groups and column tiles [4 (b % n_col_groups), + 4)
+    cut at n_col_tiles; the launcher sizes the grid n_row_tiles x n_col_groups."""
+    n_col_tiles = (C + 31) // 32
+    n_col_groups = (n_col_tiles + FP4_GROUP_COL_TILES - 1) // FP4_GROUP_COL_TILES
+    seen = []
+    for b in range(n_row_tiles * n_col_groups):
+        rt = b // n_col_groups
+        ct_begin = (b - rt * n_col_groups) * FP4_GROUP_COL_TILES
+        ct_end = min(ct_begin + FP4_GROUP_COL_TILES, n_col_tiles)
+        assert 0 <= rt < n_row_tiles and ct_begin < ct_end
+        seen += [(rt, ct) for ct in range(ct_begin, ct_end)]
+    assert seen == [(r, c) for r in range(n_row_tiles) for c in range(n_col_tiles)]
+
+
+def test_replica_constants_match_the_kernel_source():
+    """The replicas above use the kernels' own constants."""
+    import re
+    from pathlib import Path
+    src = (Path(__file__).resolve().parents[1] / "moe_grouped_gemm_mxq_amd" / "csrc" / "qdq_mxfp4.hip").read_text()
+    assert int(re.search(r"constexpr int kOpUnits = (\d+);", src).group(1)) == FP4_UNITS
+    assert int(re.search(r"constexpr int kGrpColTiles = (\d+);", src).group(1)) == FP4_GROUP_COL_TILES
