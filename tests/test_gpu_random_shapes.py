@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import assert_bytes_equal, assert_gemm_close, bits, host, mxq, out_host, scaled_randn
+from gpu_util import assert_bytes_equal, assert_gemm_close, bits, host, mxq, out_host, scaled_randn, unpack_scales
 
 pytestmark = pytest.mark.gpu
 SEEDS = list(range(8))
@@ -155,3 +155,20 @@ def test_random_fp4_qdq_and_gemm(seed):
     _, cb, s_b, _ = oracle.mxfp4_qdq_ex(w.numpy(), 6.0)
     Cr, Ca = oracle.gemm_fp4(ca, s_a, cb, s_b)
     assert_gemm_close(host(C), Cr, Ca, f"FP4 GEMM {rows}x{N}x{L}")
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_fp4_operand_rows_of_whole_kilo_elements(seed):
+    """MXFP4 GEMM operands of rows whose length is a multiple of 1024 (the
+    row-piece kernel): random row counts (partial 128-row groups, odd piece
+    counts) and scale factors, every code and scale byte against the oracle."""
+    rng = np.random.default_rng(700 + seed)
+    rows, L = int(rng.integers(1, 700)), 1024 * int(rng.integers(1, 6))
+    sf = float(np.float32(rng.choice([6.0, 5.0, 7.25, 3.0])))
+    g = torch.Generator().manual_seed(700 + seed)
+    x = torch.randn(rows, L, generator=g) * torch.exp2(torch.randint(-20, 20, (rows, 1), generator=g).float())
+    codes, scales = mxq().quantize_fp4(x.cuda(), sf)
+    torch.cuda.synchronize()
+    _, rc, rs, _ = oracle.mxfp4_qdq_ex(x.numpy(), sf)
+    assert np.array_equal(host(codes), rc), f"codes {rows}x{L} sf {sf}"
+    assert np.array_equal(unpack_scales(scales, rows), rs), f"scales {rows}x{L} sf {sf}"
