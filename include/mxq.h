@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 6
+#define MXQ_ABI_VERSION 7
 #define MXQ_BLOCK 32          /* elements per MX block; fixed */
 #define MXQ_MAX_GROUPS 1024   /* largest G the grouped entry points accept */
 /* E4M3 GEMM reductions of at most this many elements (dense and ragged M: K;
@@ -112,8 +112,13 @@ const char* mxq_last_error(void);
 /* MXQ_OK iff HIP device `device` exists and is gfx950. */
 mxq_status mxq_device_check(int device);
 
-/* Columns a grouped token-axis copy of T rows in G groups may need: an upper
- * bound of sum_g ceil32(m_g), rounded up to 32.  Pure host arithmetic. */
+/* Row pitch (ldq) for a grouped token-axis copy of T rows in G groups: at
+ * least T + 31 G, an upper bound of sum_g ceil32(m_g), rounded up to an odd
+ * multiple of 256.  Rows then start on 128-byte lines (E4M3 rows of ldq
+ * bytes, E2M1 rows of ldq/2), which the weight-gradient GEMM loads whole,
+ * and consecutive rows do not fall in the same memory channels (a pitch of
+ * 2^10 x 129 bytes measured 1.2x slower).  Any ldq that is a multiple of 32
+ * and at least sum_g ceil32(m_g) stays valid.  Pure host arithmetic. */
 int64_t mxq_grouped_cols_max(int64_t T, int32_t G);
 
 /* Bytes of a quantised GEMM operand of `rows` rows and reduction length K in
@@ -305,6 +310,10 @@ mxq_status mxq_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const
  *     C[g] = sum over group g's padded columns of deq(A) deq(B);
  *     an empty group gets exact zeros.  Expert weight gradient:
  *     A = grouped copy of X (M = hidden), B = grouped copy of dY (N = ffn).
+ *     The kernel reads each group's rows from the 128-byte line at or below
+ *     its first column and zeroes the columns before it, so the columns
+ *     before P_g must hold quantised data (the earlier groups' blocks, as the
+ *     grouped quantisers write them: no positions lie between groups).
  * fmt MXQ_FMT_E2M1: MXFP4 operands as for mxq_gemm (codes K/2 bytes per row,
  * expert g's B codes at byte g * N * K/2); for MXQ_GG_RAGGED_K the grouped
  * token-axis copies of mxq_quantize_fp4_grouped (K = their ldq).

@@ -113,7 +113,9 @@ mxq_status mxq_device_check(int device) {
 
 int64_t mxq_grouped_cols_max(int64_t T, int32_t G) {
   if (T < 0 || G < 0) return 0;
-  return (T + 31 * (int64_t)G + 31) / 32 * 32;
+  int64_t n = (T + 31 * (int64_t)G + 255) / 256;  // 256-column units
+  if (n % 2 == 0) n++;                              // an odd number of them
+  return n * 256;
 }
 
 mxq_status mxq_operand_sizes(int64_t rows, int64_t K, int fmt, int64_t* code_bytes, int64_t* scale_bytes) {

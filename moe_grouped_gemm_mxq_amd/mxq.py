@@ -84,7 +84,7 @@ def _load(path: str = LIB_PATH):
     return lib
 
 
-ABI_VERSION = 6  # MXQ_ABI_VERSION of include/mxq.h this binding is written against
+ABI_VERSION = 7  # MXQ_ABI_VERSION of include/mxq.h this binding is written against
 
 _lib = _load()
 if _lib.mxq_abi_version() != ABI_VERSION:

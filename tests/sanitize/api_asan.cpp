@@ -67,7 +67,7 @@ int main() {
   EXPECT(mxq_operand_sizes(0, 64, MXQ_FMT_E4M3, &cb, &sb), INV);
   EXPECT(mxq_operand_sizes(5, 64, 7, &cb, &sb), INV);
   EXPECT(mxq_operand_sizes(5, 64, MXQ_FMT_E4M3, nullptr, &sb), INV);
-  if (mxq_grouped_cols_max(100, 3) != 224 || mxq_grouped_cols_max(-1, 3) != 0) fails++;
+  if (mxq_grouped_cols_max(100, 3) != 256 || mxq_grouped_cols_max(300, 3) != 768 || mxq_grouped_cols_max(-1, 3) != 0) fails++;
   int32_t F = 0;
   uint32_t T = 0;
   EXPECT(mxq_fp4_scale_threshold(6.0f, &F, &T), MXQ_OK);

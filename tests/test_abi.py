@@ -59,9 +59,13 @@ def test_abi_version_and_pure_host_helpers(lib):
     f = lib.mxq_grouped_cols_max
     f.restype = ctypes.c_int64
     f.argtypes = [ctypes.c_int64, ctypes.c_int32]
-    assert f(131072, 32) == 131072 + 992
-    assert f(1, 1) == 32
-    assert f(70, 6) % 32 == 0 and f(70, 6) >= 70 + 31 * 6
+    # at least T + 31 G, an odd multiple of 256
+    assert f(131072, 32) == 517 * 256
+    assert f(1, 1) == 256
+    assert f(0, 0) == 256
+    for T, G in ((70, 6), (131072, 1), (256, 1), (513, 1024), (2 ** 31 - 1, 1024)):
+        v = f(T, G)
+        assert v >= T + 31 * G and v % 256 == 0 and (v // 256) % 2 == 1 and v - (T + 31 * G) < 512
 
 
 def test_operand_sizes(lib):

@@ -82,7 +82,7 @@ def sample_units(total, n=4000, seed=0):
 @pytest.mark.parametrize("tile_rows", [128, 256])  # MXFP8 tile quantiser / grouped MXFP4 quantiser
 def test_grouped_quantiser_reads_inside_the_input(ends, T, tile_rows):
     G = len(ends)
-    ldq = (T + 31 * G + 31) // 32 * 32            # mxq_grouped_cols_max
+    ldq = (((T + 31 * G + 255) // 256) | 1) * 256  # mxq_grouped_cols_max: an odd multiple of 256
     start, size, bstart, nb = build_block_starts(ends, T, 32)
     assert all(bstart[g] <= bstart[g + 1] <= bstart[g] + nb[g] for g in range(G))
     # tiles of tile_rows padded positions over T + 31 G
