@@ -110,7 +110,8 @@ def moe_tile_stats(sizes, H, F, cus, BM=256, BN=256, BK=128):
     arithmetic following the kernels' tiling: ragged-M tiles start at the
     128-row boundary at or below their group's first row; ragged-K tiles of a
     group reduce over its 32-padded tokens in 128-deep stages, an even number
-    of them, and are dealt round robin, largest group first)."""
+    of them, from the 128-token boundary at or below the group's first padded
+    position, and are dealt round robin, largest group first)."""
     out = {}
     # ragged M (forward: N = F; input gradient: N = H), K = H or F
     start, m_tiles = 0, 0
@@ -132,7 +133,8 @@ def moe_tile_stats(sizes, H, F, cus, BM=256, BN=256, BK=128):
     # 8 of them)
     per_g = ((H + BM - 1) // BM) * ((F + BN - 1) // BN)
     long_g = [g for g in range(len(sizes)) if sizes[g] > 1024]
-    nst = {g: (-(-((sizes[g] + 31) // 32 * 32) // BK) + 1) // 2 * 2 for g in long_g}
+    pos = [sum((m + 31) // 32 * 32 for m in sizes[:g]) for g in range(len(sizes))]  # padded group starts
+    nst = {g: (-(-(pos[g] % BK + (sizes[g] + 31) // 32 * 32) // BK) + 1) // 2 * 2 for g in long_g}
     order = sorted(long_g, key=lambda g: (-sizes[g], g))
     work = [0] * cus
     tile = 0

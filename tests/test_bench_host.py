@@ -36,7 +36,8 @@ def test_committed_profiles_name_the_profiled_source():
 def test_moe_tile_stats_small_cases():
     """Tile accounting of the grouped GEMMs, checked by hand: ragged-M tiles
     start at the 128-row boundary below their group; ragged-K experts above
-    1024 tokens run 128-token stages, an even number per expert, and the
+    1024 tokens run 128-token stages, an even number per expert, from the
+    128-token boundary at or below the expert's first padded position, and the
     others go to the exact-group launch (one interleaved step per 8 padded
     tokens)."""
     b = load_bench()
@@ -61,3 +62,7 @@ def test_moe_tile_stats_small_cases():
     assert pl["tokens_computed"] == (10 + 16) * 128 and pl["tokens_routed"] == 3100
     # workgroup 0: 16 + 1, workgroup 1: 10 + 1
     assert pl["max_over_mean_stages_per_workgroup"] == round(17 / (28 / 2), 4)
+    # a group starting off a 128-token boundary reduces from the boundary below:
+    # [40, 1250]: group 1 at padded position 64, 64 + 1280 tokens -> 11 stages -> 12
+    st = b.moe_tile_stats([40, 1250], 256, 256, cus=1)
+    assert st["raggedK_wgrad"]["plain_launch"]["tokens_computed"] == 12 * 128
