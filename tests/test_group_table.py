@@ -14,7 +14,8 @@ The replica follows the kernels step by step:
     rows [gstart + off, + valid);
   * the ragged-M GEMM: m-tile -> (group, first row m0, rows), tile count cut
     at the launcher's bound tiles_m + 2G;
-  * the ragged-K GEMM: expert g's reduction range [k_begin, k_end) in [0, K].
+  * the ragged-K GEMM: expert g's reduction range [k_begin, k_end) in [0, K],
+    read from the 128-byte line at or below k_begin (the head zeroed).
 """
 import numpy as np
 import pytest
@@ -131,6 +132,15 @@ def test_ragged_k_ranges_stay_inside_the_reduction(ends, K):
         assert 0 <= k_begin <= K and 0 <= k_end <= K
         klen = k_end - k_begin if k_end > k_begin else 0
         assert k_begin + klen <= K
+        # the plain launch starts at the 128-byte line at or below k_begin (128
+        # E4M3 or 256 E2M1 tokens) and zeroes the head chunks (16 or 32 tokens)
+        for stage_elems, chunk_elems in ((128, 16), (256, 32)):
+            if klen > 0:
+                al = k_begin // stage_elems * stage_elems
+                head_chunks = (k_begin - al) // chunk_elems
+                assert 0 <= al <= k_begin and (k_begin - al) % chunk_elems == 0
+                assert 0 <= head_chunks < stage_elems // chunk_elems
+                assert al + (klen + k_begin - al) == k_end <= K
 
 
 def test_valid_arrays_are_unchanged():
