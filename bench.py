@@ -307,21 +307,21 @@ def main():
         launches.append(["qdq_fp4 8192x8192", "qdq_flat_kernel", bytes_["qdq_fp4"]])
         for name, t, q, r, c in (("X", X, qx, M, K), ("W", W, qw, K, N), ("dY", dY, qy, M, N)):
             mxq.mxq_quantize(t, R | C, q["q_row"], q["s_row"], q["q_colT"], q["s_colT"])
-            launches.append([f"dense_quant_dual {name} {r}x{c}", "quant_tile_kernel<true, false, true>", qb(r, c, 2)])
+            launches.append([f"dense_quant_dual {name} {r}x{c}", "quant_tile_kernel<true, true>", qb(r, c, 2)])
         mxq.mxq_quantize(Xm, R, mx["q_row"], mx["s_row"])
         launches.append([f"moe_quant_x_row {T}x{H}", "quant_row_kernel<true>", bytes_["moe_quant_x_row"]])
         quant_w_experts(R | C)
-        launches.append([f"moe_quant_w_dual {G}x{H}x{F}", "quant_tile_kernel<true, false, true>",
+        launches.append([f"moe_quant_w_dual {G}x{H}x{F}", "quant_tile_kernel<true, true>",
                          bytes_["moe_quant_w_dual"]])
         mxq.mxq_quantize_grouped(dYm, ge, ldq, R | C, mdy["q_row"], mdy["s_row"], mdy["q_colT"], mdy["s_colT"])
-        launches.append([f"moe_quant_dy_row_grouped {T}x{F}", "quant_tile_kernel<true, true, true>",
+        launches.append([f"moe_quant_dy_row_grouped {T}x{F}", "quant_tile_grouped_kernel<true, true>",
                          bytes_["moe_quant_dy_row_grouped"]])
         mxq.mxq_quantize_grouped(Xm, ge, ldq, C, None, None, mxt["q_colT"], mxt["s_colT"])
-        launches.append([f"moe_quant_x_grouped {T}x{H}", "quant_tile_kernel<false, true, true>",
+        launches.append([f"moe_quant_x_grouped {T}x{H}", "quant_tile_grouped_kernel<false, true>",
                          bytes_["moe_quant_x_grouped"]])
         # beside the step: the dual_x schedule's X launch (rows and tokens from one read)
         mxq.mxq_quantize_grouped(Xm, ge, ldq, R | C, mx["q_row"], mx["s_row"], mxt["q_colT"], mxt["s_colT"])
-        launches.append([f"moe_quant_x_row_grouped {T}x{H} (dual_x forward)", "quant_tile_kernel<true, true, true>",
+        launches.append([f"moe_quant_x_row_grouped {T}x{H} (dual_x forward)", "quant_tile_grouped_kernel<true, true>",
                          bytes_["moe_quant_x_row_grouped"]])
         # beside the step: the MXFP4 operand quantisers of the MXFP4 GEMMs (fp32
         # inputs): the dense forward's X and W^T by rows, the MoE weight

@@ -175,133 +175,15 @@ constexpr int kCodePitch = kTR + 16;  // code tile row pitch: 16-byte aligned, 4
 static_assert(kTC * kCodePitch <= kTR * kLdsStride, "the code tile reuses the bf16 tile's LDS");
 static_assert(kThreads * sizeof(int64_t) <= kTR * kLdsStride, "the group scan's scratch reuses the tile's LDS");
 
-template <bool ROW, bool GROUPED, bool VEC>
-__global__ __launch_bounds__(kThreads) void quant_tile_kernel(
-    const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx,
-    const int32_t* __restrict__ group_end, int32_t G, int64_t ldq, int n_col_tiles,
-    uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row, uint8_t* __restrict__ q_colT,
-    uint8_t* __restrict__ s_colT, BatchStrides bs) {
-  // matrix blockIdx.y of a batch
-  x += blockIdx.y * bs.x;
-  if constexpr (ROW) {
-    q_row += blockIdx.y * bs.q_row;
-    s_row += blockIdx.y * bs.s_row;
-  }
-  q_colT += blockIdx.y * bs.q_colT;
-  s_colT += blockIdx.y * bs.s_colT;
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kTR * kLdsStride];
-  __shared__ int64_t rb_src[kTR / 32];   // first source row of each block of the tile
-  __shared__ int32_t rb_valid[kTR / 32]; // valid rows in that block (0: no output block)
-  const int t = threadIdx.x;
-  // Ungrouped tiles: workgroups go to the 8 XCDs round robin; within each run
-  // of 64, workgroup b takes tile b - r + 8 (r % 8) + r / 8 (r = b % 64), so
-  // an XCD runs eight consecutive tiles of a row of tiles (2 KB of each input
-  // row) rather than every eighth (measured 3-5% faster).  Grouped tiles keep
-  // the plain order, which measured 35% faster for them.
-  int bt = blockIdx.x;
-  if constexpr (!GROUPED) {
-    const int full = (int)(gridDim.x / 64 * 64);
-    if (bt < full) {
-      const int r = bt & 63;
-      bt = bt - r + (r & 7) * 8 + (r >> 3);
-    }
-  }
-  const int rt = bt / n_col_tiles;
-  const int ct = bt - rt * n_col_tiles;
-  const int64_t p0 = (int64_t)rt * kTR;  // first padded position of the tile
-  const int64_t c0 = (int64_t)ct * kTC;
-
-  if constexpr (GROUPED) {
-    // block starts only (the tile's few groups re-read their spans from
-    // group_end), keeping LDS small enough for four workgroups per CU;
-    // the scan's scratch is the tile buffer, not yet in use
-    __shared__ int32_t bstart[kMaxGroups + 1];
-    build_block_starts<kThreads>(group_end, G, R, 32, nullptr, nullptr, bstart,
-                                 reinterpret_cast<int64_t*>(tile));
-    if (t < kTR / 32) {
-      const int64_t pb = p0 / 32 + t;
-      int64_t src = 0;
-      int32_t valid = 0;
-      if (pb < bstart[G] && (pb + 1) * 32 <= ldq) {
-        const int g = find_block_group(bstart, G, (int32_t)pb);
-        int32_t gstart, gsize;
-        group_span(group_end, g, R, gstart, gsize);
-        // (bstart is non-decreasing and bstart[g] <= pb < bstart[g] + ceil32(gsize) / 32)
-        const int64_t off = (pb - bstart[g]) * 32;
-        src = (int64_t)gstart + off;
-        valid = (int32_t)min<int64_t>(32, gsize - off);
-        if (valid <= 0) valid = -1;  // cannot happen for consistent tables
-      }
-      rb_src[t] = src;
-      rb_valid[t] = valid;
-    }
-  } else {
-    if (t < kTR / 32) {
-      const int64_t r0 = p0 + 32 * t;
-      rb_src[t] = r0;
-      rb_valid[t] = r0 < R ? (int32_t)min<int64_t>(32, R - r0) : 0;
-    }
-  }
-  __syncthreads();
-  if (rb_valid[0] <= 0) return;  // tile lies past the last block (uniform)
-
-  const int64_t Cp = (C + 31) / 32 * 32;
-  // ---- phase 1: load (+ row copy), stage in LDS.  All eight loads of a
-  // thread are issued before any arithmetic, so they are in flight together.
-  const int c16 = t & 15;
-  const int64_t col1 = c0 + c16 * 8;
-  uint32_t w[8][4];
-  if (VEC && c0 + kTC <= C) {
-    // no column tail in this tile: unconditional 16-byte loads (rows past the
-    // valid range read the tile's first row, always valid, and are zeroed),
-    // so the eight loads issue back to back with no wait between them
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const int lr = (t >> 4) + 16 * i;  // tile row
-      const int rb = lr >> 5;
-      const bool row_ok = (lr & 31) < rb_valid[rb];
-      const int64_t src = row_ok ? rb_src[rb] + (lr & 31) : rb_src[0];
-      const uint4 v = *reinterpret_cast<const uint4*>(x + src * ldx + col1);
-      w[i][0] = row_ok ? v.x : 0u;
-      w[i][1] = row_ok ? v.y : 0u;
-      w[i][2] = row_ok ? v.z : 0u;
-      w[i][3] = row_ok ? v.w : 0u;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const int lr = (t >> 4) + 16 * i;
-      const int rb = lr >> 5;
-      const bool row_ok = (lr & 31) < rb_valid[rb];
-      const int64_t src = rb_src[rb] + (lr & 31);
-      w[i][0] = w[i][1] = w[i][2] = w[i][3] = 0u;
-      if (row_ok) load_chunk<VEC>(x + src * ldx, col1, C, w[i]);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const int lr = (t >> 4) + 16 * i;
-    if constexpr (ROW) {
-      const int rb = lr >> 5;
-      const bool row_ok = (lr & 31) < rb_valid[rb];
-      const int64_t src = rb_src[rb] + (lr & 31);
-      uint32_t m = hmax_u16x2(pkmax_u16(absmax_bf16x2(w[i][0], w[i][1]), absmax_bf16x2(w[i][2], w[i][3])));
-      m = quad_max_u32(m);
-      const uint32_t byte = mxfp8_scale_byte(m);
-      const float sc = e8m0_as_scale(byte);
-      uint2 codes;
-      codes.x = e4m3_encode4(w[i][0], w[i][1], sc);
-      codes.y = e4m3_encode4(w[i][2], w[i][3], sc);
-      if (row_ok && col1 < Cp) {
-        *reinterpret_cast<uint2*>(q_row + src * Cp + col1) = codes;
-        if ((c16 & 3) == 0) s_row[scale_offset(src, col1 / 32, Cp / 32)] = (uint8_t)byte;
-      }
-    }
-    *reinterpret_cast<uint4*>(tile + lr * kLdsStride + c16 * 16) = make_uint4(w[i][0], w[i][1], w[i][2], w[i][3]);
-  }
-  __syncthreads();
-
-  // ---- phase 2: column copy
+// Phase 2 of a tile, once it is staged in LDS (and a barrier has published
+// it): the column copy.  Each thread takes a column pair and one block of 32
+// rows; the codes go back through LDS as a [column][row] code tile, so that
+// eight lanes store one column's 128 codes together.  Every thread reaches the
+// two barriers inside; it returns after the code stores, whose LDS reads must
+// precede any new write to the tile.
+__device__ __forceinline__ void column_phase(uint8_t* tile, const int32_t* rb_valid, int t, int64_t c0,
+                                             int64_t p0, int64_t C, int64_t ldq, uint8_t* __restrict__ q_colT,
+                                             uint8_t* __restrict__ s_colT) {
   const int pr = t & 63;  // column pair
   const int rb = t >> 6;  // block of 32 tile rows
   const int64_t col = c0 + 2 * pr;
@@ -362,6 +244,232 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
   }
 }
 
+template <bool ROW, bool VEC>
+__global__ __launch_bounds__(kThreads) void quant_tile_kernel(
+    const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx, int64_t ldq, int n_col_tiles,
+    uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row, uint8_t* __restrict__ q_colT,
+    uint8_t* __restrict__ s_colT, BatchStrides bs) {
+  // matrix blockIdx.y of a batch
+  x += blockIdx.y * bs.x;
+  if constexpr (ROW) {
+    q_row += blockIdx.y * bs.q_row;
+    s_row += blockIdx.y * bs.s_row;
+  }
+  q_colT += blockIdx.y * bs.q_colT;
+  s_colT += blockIdx.y * bs.s_colT;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kTR * kLdsStride];
+  __shared__ int64_t rb_src[kTR / 32];   // first source row of each block of the tile
+  __shared__ int32_t rb_valid[kTR / 32]; // valid rows in that block (0: no output block)
+  const int t = threadIdx.x;
+  // Workgroups go to the 8 XCDs round robin; within each run of 64,
+  // workgroup b takes tile b - r + 8 (r % 8) + r / 8 (r = b % 64), so an XCD
+  // runs eight consecutive tiles of a row of tiles (2 KB of each input row)
+  // rather than every eighth (measured 3-5% faster).
+  int bt = blockIdx.x;
+  {
+    const int full = (int)(gridDim.x / 64 * 64);
+    if (bt < full) {
+      const int r = bt & 63;
+      bt = bt - r + (r & 7) * 8 + (r >> 3);
+    }
+  }
+  const int rt = bt / n_col_tiles;
+  const int ct = bt - rt * n_col_tiles;
+  const int64_t p0 = (int64_t)rt * kTR;  // first padded position of the tile
+  const int64_t c0 = (int64_t)ct * kTC;
+
+  if (t < kTR / 32) {
+    const int64_t r0 = p0 + 32 * t;
+    rb_src[t] = r0;
+    rb_valid[t] = r0 < R ? (int32_t)min<int64_t>(32, R - r0) : 0;
+  }
+  __syncthreads();
+  if (rb_valid[0] <= 0) return;  // tile lies past the last block (uniform)
+
+  const int64_t Cp = (C + 31) / 32 * 32;
+  // ---- phase 1: load (+ row copy), stage in LDS.  All eight loads of a
+  // thread are issued before any arithmetic, so they are in flight together.
+  const int c16 = t & 15;
+  const int64_t col1 = c0 + c16 * 8;
+  uint32_t w[8][4];
+  if (VEC && c0 + kTC <= C) {
+    // no column tail in this tile: unconditional 16-byte loads (rows past the
+    // valid range read the tile's first row, always valid, and are zeroed),
+    // so the eight loads issue back to back with no wait between them
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int lr = (t >> 4) + 16 * i;  // tile row
+      const int rb = lr >> 5;
+      const bool row_ok = (lr & 31) < rb_valid[rb];
+      const int64_t src = row_ok ? rb_src[rb] + (lr & 31) : rb_src[0];
+      const uint4 v = *reinterpret_cast<const uint4*>(x + src * ldx + col1);
+      w[i][0] = row_ok ? v.x : 0u;
+      w[i][1] = row_ok ? v.y : 0u;
+      w[i][2] = row_ok ? v.z : 0u;
+      w[i][3] = row_ok ? v.w : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int lr = (t >> 4) + 16 * i;
+      const int rb = lr >> 5;
+      const bool row_ok = (lr & 31) < rb_valid[rb];
+      const int64_t src = rb_src[rb] + (lr & 31);
+      w[i][0] = w[i][1] = w[i][2] = w[i][3] = 0u;
+      if (row_ok) load_chunk<VEC>(x + src * ldx, col1, C, w[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int lr = (t >> 4) + 16 * i;
+    if constexpr (ROW) {
+      const int rb = lr >> 5;
+      const bool row_ok = (lr & 31) < rb_valid[rb];
+      const int64_t src = rb_src[rb] + (lr & 31);
+      uint32_t m = hmax_u16x2(pkmax_u16(absmax_bf16x2(w[i][0], w[i][1]), absmax_bf16x2(w[i][2], w[i][3])));
+      m = quad_max_u32(m);
+      const uint32_t byte = mxfp8_scale_byte(m);
+      const float sc = e8m0_as_scale(byte);
+      uint2 codes;
+      codes.x = e4m3_encode4(w[i][0], w[i][1], sc);
+      codes.y = e4m3_encode4(w[i][2], w[i][3], sc);
+      if (row_ok && col1 < Cp) {
+        *reinterpret_cast<uint2*>(q_row + src * Cp + col1) = codes;
+        if ((c16 & 3) == 0) s_row[scale_offset(src, col1 / 32, Cp / 32)] = (uint8_t)byte;
+      }
+    }
+    *reinterpret_cast<uint4*>(tile + lr * kLdsStride + c16 * 16) = make_uint4(w[i][0], w[i][1], w[i][2], w[i][3]);
+  }
+  __syncthreads();
+
+  column_phase(tile, rb_valid, t, c0, p0, C, ldq, q_colT, s_colT);
+}
+
+
+// The grouped token-axis copy (rows = routed tokens in expert order, output
+// padded per group to whole 32-row blocks): tiles of 128 padded positions.  A
+// workgroup builds the group table once and walks kGrpWalk column tiles of
+// one row tile, the next tile's loads in flight while the current one is
+// quantised.  Measured on 131072 x 7168 against one tile per workgroup: the
+// token-axis copy 0.593 -> 0.569 ms, with the row copy (x 4096) 0.446 ->
+// 0.441 ms; two or eight tiles per workgroup, or re-reading the source rows
+// from LDS per tile (126 instead of 156 VGPRs, four workgroups per CU instead
+// of three), no better.  Consecutive
+// workgroups take consecutive column groups of a row tile: dealing them to
+// the XCDs like the ungrouped tiles measured 35% slower here.
+constexpr int kGrpWalk = 4;
+
+template <bool ROW, bool VEC>
+__global__ __launch_bounds__(kThreads) void quant_tile_grouped_kernel(
+    const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx, const int32_t* __restrict__ group_end,
+    int32_t G, int64_t ldq, int n_col_tiles, int n_col_groups, uint8_t* __restrict__ q_row,
+    uint8_t* __restrict__ s_row, uint8_t* __restrict__ q_colT, uint8_t* __restrict__ s_colT) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kTR * kLdsStride];
+  __shared__ int64_t rb_src[kTR / 32];   // first source row of each block of the tile
+  __shared__ int32_t rb_valid[kTR / 32]; // valid rows in that block (0: no output block)
+  const int t = threadIdx.x;
+  const int rt = blockIdx.x / n_col_groups;
+  const int ct_begin = (blockIdx.x - rt * n_col_groups) * kGrpWalk;
+  const int ct_end = min(ct_begin + kGrpWalk, n_col_tiles);
+  const int64_t p0 = (int64_t)rt * kTR;  // first padded position of the tile
+
+  // block starts only (the tile's few groups re-read their spans from
+  // group_end), keeping LDS small enough for four workgroups per CU;
+  // the scan's scratch is the tile buffer, not yet in use
+  __shared__ int32_t bstart[kMaxGroups + 1];
+  build_block_starts<kThreads>(group_end, G, R, 32, nullptr, nullptr, bstart,
+                               reinterpret_cast<int64_t*>(tile));
+  if (t < kTR / 32) {
+    const int64_t pb = p0 / 32 + t;
+    int64_t src = 0;
+    int32_t valid = 0;
+    if (pb < bstart[G] && (pb + 1) * 32 <= ldq) {
+      const int g = find_block_group(bstart, G, (int32_t)pb);
+      int32_t gstart, gsize;
+      group_span(group_end, g, R, gstart, gsize);
+      // (bstart is non-decreasing and bstart[g] <= pb < bstart[g] + ceil32(gsize) / 32)
+      const int64_t off = (pb - bstart[g]) * 32;
+      src = (int64_t)gstart + off;
+      valid = (int32_t)min<int64_t>(32, gsize - off);
+      if (valid <= 0) valid = -1;  // cannot happen for consistent tables
+    }
+    rb_src[t] = src;
+    rb_valid[t] = valid;
+  }
+  __syncthreads();
+  if (rb_valid[0] <= 0) return;  // tile lies past the last block (uniform)
+
+  const int64_t Cp = (C + 31) / 32 * 32;
+  // source rows of this thread's eight chunks (rows (t / 16) + 16 i of the
+  // tile), the same for every column tile; rows past a block's valid range
+  // read the tile's first row, always valid, and are zeroed where used
+  const int c16 = t & 15;
+  int64_t srow[8];
+  uint32_t row_ok = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int lr = (t >> 4) + 16 * i;
+    const int rb = lr >> 5;
+    const bool ok = (lr & 31) < rb_valid[rb];
+    row_ok |= (uint32_t)ok << i;
+    srow[i] = ok ? rb_src[rb] + (lr & 31) : rb_src[0];
+  }
+  // All eight loads of a thread are issued back to back, before any use, so
+  // they are in flight together; the loaded words are used only after the
+  // next barrier, so the loads of the next column tile stay in flight while
+  // the current one is quantised from LDS.
+  auto load_tile = [&](int64_t c0, uint32_t (&w)[8][4]) {
+    const int64_t col1 = c0 + c16 * 8;
+    if (VEC && c0 + kTC <= C) {  // no column tail in this tile
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const uint4 v = *reinterpret_cast<const uint4*>(x + srow[i] * ldx + col1);
+        w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        w[i][0] = w[i][1] = w[i][2] = w[i][3] = 0u;
+        if (row_ok >> i & 1u) load_chunk<VEC>(x + srow[i] * ldx, col1, C, w[i]);
+      }
+    }
+  };
+  uint32_t w[8][4];
+  load_tile((int64_t)ct_begin * kTC, w);
+#pragma unroll 1
+  for (int ct = ct_begin; ct < ct_end; ct++) {
+    const int64_t c0 = (int64_t)ct * kTC;
+    const int64_t col1 = c0 + c16 * 8;
+    // ---- phase 1: (row copy,) stage the tile in LDS
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int lr = (t >> 4) + 16 * i;
+      const bool ok = row_ok >> i & 1u;
+      const uint32_t u0 = ok ? w[i][0] : 0u, u1 = ok ? w[i][1] : 0u;
+      const uint32_t u2 = ok ? w[i][2] : 0u, u3 = ok ? w[i][3] : 0u;
+      if constexpr (ROW) {
+        uint32_t m = hmax_u16x2(pkmax_u16(absmax_bf16x2(u0, u1), absmax_bf16x2(u2, u3)));
+        m = quad_max_u32(m);
+        const uint32_t byte = mxfp8_scale_byte(m);
+        const float sc = e8m0_as_scale(byte);
+        uint2 codes;
+        codes.x = e4m3_encode4(u0, u1, sc);
+        codes.y = e4m3_encode4(u2, u3, sc);
+        if (ok && col1 < Cp) {
+          *reinterpret_cast<uint2*>(q_row + srow[i] * Cp + col1) = codes;
+          if ((c16 & 3) == 0) s_row[scale_offset(srow[i], col1 / 32, Cp / 32)] = (uint8_t)byte;
+        }
+      }
+      *reinterpret_cast<uint4*>(tile + lr * kLdsStride + c16 * 16) = make_uint4(u0, u1, u2, u3);
+    }
+    __syncthreads();
+    if (ct + 1 < ct_end) load_tile(c0 + kTC, w);
+
+    column_phase(tile, rb_valid, t, c0, p0, C, ldq, q_colT, s_colT);
+    if (ct + 1 < ct_end) __syncthreads();  // the code tile is read before the next tile is staged (uniform)
+  }
+}
+
 }  // namespace
 
 hipError_t launch_quant_row(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q,
@@ -394,15 +502,25 @@ hipError_t launch_quant_tile(const uint16_t* x, int64_t R, int64_t C, int64_t ld
   const int64_t padded = grouped ? (R + 31 * (int64_t)G) : R;
   const int64_t n_row_tiles = (padded + kTR - 1) / kTR;
   const int n_col_tiles = (int)((C + kTC - 1) / kTC);
+  if (grouped) {
+    const int n_col_groups = (n_col_tiles + kGrpWalk - 1) / kGrpWalk;
+    const int64_t grid = n_row_tiles * n_col_groups;
+    if (grid > 0x7FFFFFFF || batch != 1) return hipErrorInvalidValue;
+#define MXQ_TILE_LAUNCH(ROWv, VECv)                                                             \
+  quant_tile_grouped_kernel<ROWv, VECv><<<(unsigned)grid, kThreads, 0, st>>>(                   \
+      x, R, C, ldx, group_end, G, ldq, n_col_tiles, n_col_groups, q_row, s_row, q_colT, s_colT)
+    if (row) { if (vec) MXQ_TILE_LAUNCH(true, true); else MXQ_TILE_LAUNCH(true, false); }
+    else { if (vec) MXQ_TILE_LAUNCH(false, true); else MXQ_TILE_LAUNCH(false, false); }
+#undef MXQ_TILE_LAUNCH
+    return hipGetLastError();
+  }
   const int64_t grid = n_row_tiles * n_col_tiles;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-#define MXQ_TILE_LAUNCH(ROWv, GRPv, VECv)                                                     \
-  quant_tile_kernel<ROWv, GRPv, VECv><<<dim3((unsigned)grid, (unsigned)batch), kThreads, 0, st>>>( \
-      x, R, C, ldx, group_end, G, ldq, n_col_tiles, q_row, s_row, q_colT, s_colT, bs)
-  if (row && grouped) { if (vec) MXQ_TILE_LAUNCH(true, true, true); else MXQ_TILE_LAUNCH(true, true, false); }
-  else if (row) { if (vec) MXQ_TILE_LAUNCH(true, false, true); else MXQ_TILE_LAUNCH(true, false, false); }
-  else if (grouped) { if (vec) MXQ_TILE_LAUNCH(false, true, true); else MXQ_TILE_LAUNCH(false, true, false); }
-  else { if (vec) MXQ_TILE_LAUNCH(false, false, true); else MXQ_TILE_LAUNCH(false, false, false); }
+#define MXQ_TILE_LAUNCH(ROWv, VECv)                                                                  \
+  quant_tile_kernel<ROWv, VECv><<<dim3((unsigned)grid, (unsigned)batch), kThreads, 0, st>>>(         \
+      x, R, C, ldx, ldq, n_col_tiles, q_row, s_row, q_colT, s_colT, bs)
+  if (row) { if (vec) MXQ_TILE_LAUNCH(true, true); else MXQ_TILE_LAUNCH(true, false); }
+  else { if (vec) MXQ_TILE_LAUNCH(false, true); else MXQ_TILE_LAUNCH(false, false); }
 #undef MXQ_TILE_LAUNCH
   return hipGetLastError();
 }

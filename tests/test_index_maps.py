@@ -85,21 +85,24 @@ def test_fp4_operand_rows_cover_every_piece_once(rows, L):
 
 
 FP4_GROUP_COL_TILES = 4   # column tiles of one row tile walked by a workgroup of the MXFP4 grouped quantiser
+FP8_GROUP_COL_TILES = 4   # the same for the MXFP8 grouped token-axis copy (quant_mxfp8.hip)
 
 
-@pytest.mark.parametrize("C", [1, 31, 32, 33, 96, 128, 129, 200, 4096, 7168])
+@pytest.mark.parametrize("C", [1, 31, 32, 33, 96, 128, 129, 200, 511, 513, 4096, 7168])
 @pytest.mark.parametrize("n_row_tiles", [1, 3, 516])
-def test_fp4_grouped_column_walk_covers_every_tile_once(C, n_row_tiles):
-    """MXFP4 grouped token-axis quantiser (qdq_mxfp4.hip): workgroup b takes
-    row tile b / n_col_groups and column tiles [4 (b % n_col_groups), + 4)
-    cut at n_col_tiles; the launcher sizes the grid n_row_tiles x n_col_groups."""
-    n_col_tiles = (C + 31) // 32
-    n_col_groups = (n_col_tiles + FP4_GROUP_COL_TILES - 1) // FP4_GROUP_COL_TILES
+@pytest.mark.parametrize("col_tile, walk", [(32, FP4_GROUP_COL_TILES), (128, FP8_GROUP_COL_TILES)])
+def test_grouped_column_walk_covers_every_tile_once(C, n_row_tiles, col_tile, walk):
+    """Grouped token-axis quantisers (MXFP4: 32-column tiles, qdq_mxfp4.hip;
+    MXFP8: 128-column tiles, quant_mxfp8.hip): workgroup b takes row tile
+    b / n_col_groups and column tiles [walk (b % n_col_groups), + walk) cut at
+    n_col_tiles; the launcher sizes the grid n_row_tiles x n_col_groups."""
+    n_col_tiles = (C + col_tile - 1) // col_tile
+    n_col_groups = (n_col_tiles + walk - 1) // walk
     seen = []
     for b in range(n_row_tiles * n_col_groups):
         rt = b // n_col_groups
-        ct_begin = (b - rt * n_col_groups) * FP4_GROUP_COL_TILES
-        ct_end = min(ct_begin + FP4_GROUP_COL_TILES, n_col_tiles)
+        ct_begin = (b - rt * n_col_groups) * walk
+        ct_end = min(ct_begin + walk, n_col_tiles)
         assert 0 <= rt < n_row_tiles and ct_begin < ct_end
         seen += [(rt, ct) for ct in range(ct_begin, ct_end)]
     assert seen == [(r, c) for r in range(n_row_tiles) for c in range(n_col_tiles)]
@@ -112,3 +115,6 @@ def test_replica_constants_match_the_kernel_source():
     src = (Path(__file__).resolve().parents[1] / "moe_grouped_gemm_mxq_amd" / "csrc" / "qdq_mxfp4.hip").read_text()
     assert int(re.search(r"constexpr int kOpUnits = (\d+);", src).group(1)) == FP4_UNITS
     assert int(re.search(r"constexpr int kGrpColTiles = (\d+);", src).group(1)) == FP4_GROUP_COL_TILES
+    src8 = (Path(__file__).resolve().parents[1] / "moe_grouped_gemm_mxq_amd" / "csrc" / "quant_mxfp8.hip").read_text()
+    assert int(re.search(r"constexpr int kGrpWalk = (\d+);", src8).group(1)) == FP8_GROUP_COL_TILES
+    assert re.search(r"constexpr int kTR = 128, kTC = (\d+),", src8).group(1) == "128"
