@@ -290,7 +290,9 @@ GROUPS = [[70], [0, 1, 31, 32, 33, 0], [0, 0, 5], [64, 0], [17, 40, 1, 0, 96],
 
 
 @pytest.mark.parametrize("sizes", GROUPS)
-@pytest.mark.parametrize("C", [40, 129])
+# one or two column tiles; six (a second column group of two, the last with a
+# 40-column tail); nine with odd rows (the unaligned load path, three groups)
+@pytest.mark.parametrize("C", [40, 129, 680, 1031])
 @pytest.mark.parametrize("axis", [2, 3])
 def test_grouped_quantize_bitexact(sizes, C, axis):
     m = mxq()
