@@ -26,7 +26,11 @@
  *    group sizes back to the host and keeps no per-call state; it only caches
  *    the per-device architecture check and a thread-local error message.
  *  - Work is enqueued on the caller's stream `st` (0 = the null stream).
- *    Outputs must not alias inputs.  Tensor pointers must be 16-byte aligned.
+ *    Outputs must not alias inputs.  Code arrays (quantiser outputs, GEMM
+ *    operands) must be 16-byte aligned; each entry point states what it
+ *    requires of its other pointers (bf16 inputs 2 bytes, fp32 data and
+ *    packed scale arrays that are written as dwords 4 bytes) and rejects a
+ *    pointer that breaks it with MXQ_ERR_INVALID_ARGUMENT.
  *  - A quantised MXFP8 operand is `codes[rows][Kp]` (one E4M3 byte per
  *    element, the reduction axis K contiguous, Kp = ceil32(K), padding codes
  *    0x00) plus its scales: one E8M0 byte (value 2^(byte-127)) per row and
@@ -140,7 +144,9 @@ mxq_status mxq_operand_sizes(int64_t rows, int64_t K, int fmt, int64_t* code_byt
  *   axis_mask & MXQ_AXIS_COLT: q_colT [C][Rp], s_colT (C rows, Rp/32 blocks,
  *                              operand layout), Rp = ceil32(R)
  * Pointers for an axis not requested may be NULL.  Both axes together read
- * x once (dual-axis quantisation).  R, C >= 1; ldx >= C.
+ * x once (dual-axis quantisation).  R, C >= 1; ldx >= C.  x 2-byte aligned
+ * (16-byte alignment with ldx % 8 == 0 takes the vector load path), q_row
+ * and q_colT 16-byte, s_row 4-byte aligned; s_colT any alignment.
  */
 mxq_status mxq_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int axis_mask,
                         uint8_t* q_row, uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT,
@@ -152,8 +158,9 @@ mxq_status mxq_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, in
  * per-expert weights [G][K][N] of the MoE layer (torchtitan-npu guide,
  * "MoE 专家层低精度"; MindSpeed PR 3852, "主要改动").  The outputs of
  * matrix b are exactly what mxq_quantize writes for it, back to back:
- * q_row + b*R*Cp, s_row + b*ceil32(R)*(Cp/32), q_colT + b*C*Rp,
- * s_colT + b*ceil32(C)*(Rp/32).  1 <= batch <= 65535;
+ * q_row + b*R*Cp, s_row + b*ceil128(R)*(Cp/32), q_colT + b*C*Rp,
+ * s_colT + b*ceil128(C)*(Rp/32) (each scale array the full operand scale
+ * layout of its matrix).  1 <= batch <= 65535;
  * x_stride >= (R-1)*ldx + C when batch > 1.
  */
 mxq_status mxq_quantize_batched(const uint16_t* x, int64_t batch, int64_t R, int64_t C, int64_t ldx,
