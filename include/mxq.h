@@ -25,7 +25,9 @@
  *    never allocates or frees device memory, never synchronises, never copies
  *    group sizes back to the host and keeps no per-call state; it only caches
  *    the per-device architecture check and a thread-local error message.
- *  - Work is enqueued on the caller's stream `st` (0 = the null stream).
+ *  - Work is enqueued on the caller's stream `st` (0 = the null stream) as
+ *    kernel launches only (no memset, copy or synchronisation), so a
+ *    sequence of calls can be recorded into a HIP graph and replayed.
  *    Outputs must not alias inputs.  Code arrays (quantiser outputs, GEMM
  *    operands) must be 16-byte aligned; each entry point states what it
  *    requires of its other pointers (bf16 inputs 2 bytes, fp32 data and
