@@ -81,7 +81,7 @@ extern "C" {
 typedef enum {
     MXQ_OK = 0,
     MXQ_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misaligned pointer, bad enum */
-    MXQ_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement */
+    MXQ_ERR_UNSUPPORTED = 2,      /* valid request the library does not implement */
     MXQ_ERR_DEVICE = 3,           /* no HIP device, or the current device is not gfx950 */
     MXQ_ERR_LAUNCH = 4,           /* the HIP runtime rejected a kernel launch */
     MXQ_STATUS_MAX_ENUM = 0x7FFFFFFF
